@@ -1,0 +1,101 @@
+"""Pins of the oracle's observation scores (logits, softmax, max aggregation)."""
+import math
+
+import numpy as np
+import torch
+
+from oracle import segment_probabilities, segment_scores, layer_scores, visible_mask, rope, to_storage
+
+
+def _brute(k, kpos, q, qpos, causal):
+    """Dense masked attention through torch.softmax in float64."""
+    logits = torch.from_numpy(q) @ torch.from_numpy(k).T / math.sqrt(k.shape[1])
+    if causal:
+        mask = torch.from_numpy(kpos)[None, :] <= torch.from_numpy(qpos)[:, None]
+        logits = logits.masked_fill(~mask, float("-inf"))
+    return torch.softmax(logits, dim=1).numpy()
+
+
+def test_probabilities_match_dense_softmax():
+    rng = np.random.default_rng(0)
+    for causal in (True, False):
+        k = rng.standard_normal((37, 16)) * 2
+        kpos = np.arange(37)
+        q = rng.standard_normal((9, 16)) * 2
+        qpos = np.array([30, 31, 32, 33, 34, 35, 36, 37, 37])
+        p = segment_probabilities(k, kpos, q, qpos, causal)
+        assert np.allclose(p, _brute(k, kpos, q, qpos, causal), rtol=1e-12, atol=1e-300)
+        s = segment_scores(k, kpos, q, qpos, causal)
+        assert np.allclose(s, _brute(k, kpos, q, qpos, causal).max(axis=0), rtol=1e-12)
+
+
+def test_rows_sum_to_one_and_mask_is_causal():
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((50, 8))
+    kpos = np.arange(50)
+    qpos = np.array([10, 25, 49, 60])
+    p = segment_probabilities(k, kpos, rng.standard_normal((4, 8)), qpos)
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=1e-13)
+    assert np.all(p[0, 11:] == 0) and np.all(p[0, :11] > 0)
+    assert np.all(p[3] > 0)
+
+
+def test_identical_keys_and_zero_query_give_uniform_rows():
+    k = np.tile(np.random.default_rng(2).standard_normal(16), (20, 1))
+    p = segment_probabilities(k, np.arange(20), np.random.default_rng(3).standard_normal((3, 16)),
+                              np.array([4, 19, 19]))
+    assert np.allclose(p[0, :5], 1 / 5) and np.allclose(p[1], 1 / 20)
+    k2 = np.random.default_rng(4).standard_normal((20, 16))
+    p2 = segment_probabilities(k2, np.arange(20), np.zeros((1, 16)), np.array([19]))
+    assert np.allclose(p2, 1 / 20, rtol=1e-14)
+
+
+def test_large_logits_do_not_overflow():
+    k = np.array([[1.0, 0.0], [0.0, 1.0]]) * 100.0
+    q = np.array([[100.0, 0.0]])
+    p = segment_probabilities(k, np.arange(2), q, np.array([5]))
+    # logits 100*100/sqrt2 and 0: second probability is exp(-7071.07) -> 0
+    assert p[0, 0] == 1.0 and p[0, 1] == 0.0
+
+
+def test_max_aggregation_properties():
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((64, 16))
+    q = rng.standard_normal((12, 16))
+    qpos = rng.integers(40, 70, 12)
+    p = segment_probabilities(k, np.arange(64), q, qpos)
+    s = segment_scores(k, np.arange(64), q, qpos)
+    assert np.all(s[None, :] >= p)                             # aggregate >= every query's score
+    perm = rng.permutation(12)
+    assert np.array_equal(segment_scores(k, np.arange(64), q[perm], qpos[perm]), s)
+    one = segment_scores(k, np.arange(64), q[:1], qpos[:1])    # one query: exactly its row
+    assert np.allclose(one, p[0], rtol=1e-13, atol=0)
+
+
+def test_layer_scores_gqa_mapping_and_rotation():
+    """Segment (b, g) is scored by query heads g*G .. g*G+G-1 only, rotated to q_pos."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, d, n, no = 2, 4, 2, 16, 30, 3
+    theta = 1e4
+    k = to_storage(rng.standard_normal((B * Hkv * n, d)), "bf16")
+    kpos = np.tile(np.arange(n), B * Hkv)
+    seg_off = np.arange(B * Hkv) * n
+    seg_len = np.full(B * Hkv, n)
+    q = to_storage(rng.standard_normal((B, Hq, no, d)), "bf16")
+    qpos = np.array([[28, 29, 30], [27, 29, 30]])
+    out = layer_scores(k, kpos, seg_off, seg_len, q, qpos, np.array([no, 2]), Hkv, theta, "bf16")
+    for b in range(B):
+        nob = no if b == 0 else 2
+        for g in range(Hkv):
+            o = (b * Hkv + g) * n
+            per_head = []
+            for h in (2 * g, 2 * g + 1):
+                qr = to_storage(rope(q[b, h, :nob], qpos[b, :nob], theta), "bf16")
+                per_head.append(segment_probabilities(k[o:o + n], kpos[o:o + n], qr, qpos[b, :nob]))
+            want = np.concatenate(per_head).max(axis=0)
+            assert np.array_equal(out[o:o + n], want)
+
+
+def test_visible_mask_shapes():
+    m = visible_mask(np.arange(5), np.array([2, 4]))
+    assert m.tolist() == [[True, True, True, False, False], [True] * 5]
