@@ -1,0 +1,313 @@
+// C ABI of the eviction-step library: argument checks, workspace carving and
+// launches.  Every check runs on the host before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+#include "kvevict.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kve_status fail(kve_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+kve_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVE_OK;
+  return fail(KVE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_bytes(int32_t dtype) { return dtype == KVE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap (empty ranges never do).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+kve_status check_cache(const kve_cache* c, const char* name, bool need_v) {
+  if (!c) return fail(KVE_EINVAL, "%s: null cache", name);
+  if (c->dtype != KVE_BF16 && c->dtype != KVE_F32) return fail(KVE_EINVAL, "%s: bad dtype %d", name, c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(KVE_ESHAPE, "%s: head_dim %d not 64/128", name, c->head_dim);
+  if (c->n_kv_heads < 1 || c->n_seg < 0 || c->n_seg % c->n_kv_heads != 0 || c->n_seg > 65535)
+    return fail(KVE_ESHAPE, "%s: n_seg %d / n_kv_heads %d", name, c->n_seg, c->n_kv_heads);
+  if (c->max_seg_len < 0 || c->n_rows < 0) return fail(KVE_EINVAL, "%s: negative size", name);
+  if (c->n_seg > 0 && (!c->k || !c->pos || !c->seg_off || !c->seg_len || (need_v && !c->v)))
+    return fail(KVE_EINVAL, "%s: null pointer", name);
+  if (!aligned16(c->k) || (need_v && !aligned16(c->v))) return fail(KVE_EINVAL, "%s: k/v not 16-byte aligned", name);
+  return KVE_OK;
+}
+
+size_t rows_bytes(const kve_cache* c) { return size_t(c->n_rows) * c->head_dim * elem_bytes(c->dtype); }
+
+int score_impl() {
+  const char* e = std::getenv("KVE_SCORE_IMPL");
+  return (e && std::strcmp(e, "valu") == 0) ? 1 : 0;
+}
+
+size_t valu_lds(int rows, int D, int dtype) {
+  return size_t(rows) * D * elem_bytes(dtype) + size_t(rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
+}
+
+kve_status check_obs(const kve_cache* c, const kve_obs* o, int32_t* rows) {
+  if (!o) return fail(KVE_EINVAL, "null obs");
+  if (o->n_q_heads < c->n_kv_heads || o->n_q_heads % c->n_kv_heads != 0)
+    return fail(KVE_ESHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", o->n_q_heads, c->n_kv_heads);
+  if (o->max_obs < 1) return fail(KVE_ESHAPE, "max_obs %d", o->max_obs);
+  const int64_t r = int64_t(o->n_q_heads / c->n_kv_heads) * o->max_obs;
+  if (r > kve::kMaxObsRows) return fail(KVE_ESHAPE, "group*max_obs = %lld > %d", (long long)r, kve::kMaxObsRows);
+  if (!(o->rope_theta > 0.0)) return fail(KVE_EINVAL, "rope_theta must be > 0");
+  if (o->causal != 0 && o->causal != 1) return fail(KVE_EINVAL, "causal must be 0 or 1");
+  if (c->n_seg > 0 && (!o->q || !o->q_pos)) return fail(KVE_EINVAL, "null query pointers");
+  if (!aligned16(o->q)) return fail(KVE_EINVAL, "queries not 16-byte aligned");
+  *rows = int32_t(r);
+  return KVE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kve_last_error(void) { return g_err.c_str(); }
+
+int32_t kve_abi_version(void) { return KVE_ABI_VERSION; }
+
+size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o) {
+  int32_t rows = 0;
+  if (check_cache(c, "cache", false) != KVE_OK || check_obs(c, o, &rows) != KVE_OK) return 0;
+  return kve::score_workspace_bytes(c->n_seg / c->n_kv_heads, o->n_q_heads, o->max_obs, c->head_dim, c->dtype,
+                                    c->n_seg, c->max_seg_len, rows);
+}
+
+kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, float* head_entropy, void* ws,
+                          size_t ws_bytes, void* stream) {
+  kve_status st = check_cache(c, "cache", false);
+  if (st != KVE_OK) return st;
+  int32_t rows = 0;
+  if ((st = check_obs(c, o, &rows)) != KVE_OK) return st;
+  if (c->n_seg > 0 && !scores) return fail(KVE_EINVAL, "null scores");
+  const int impl = c->dtype == KVE_BF16 ? score_impl() : 1;
+  if (impl == 1 && valu_lds(rows, c->head_dim, c->dtype) > 65536)
+    return fail(KVE_ESHAPE, "rows*head_dim too large for the fp32 scoring path");
+  const int batch = c->n_seg / c->n_kv_heads;
+  const size_t need = kve::score_workspace_bytes(batch, o->n_q_heads, o->max_obs, c->head_dim, c->dtype, c->n_seg,
+                                                 c->max_seg_len, rows);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
+  const size_t sb = size_t(c->n_rows) * sizeof(float);
+  const size_t qb = size_t(batch) * o->n_q_heads * o->max_obs * c->head_dim * elem_bytes(c->dtype);
+  if (overlap(scores, sb, c->k, rows_bytes(c)) || overlap(scores, sb, o->q, qb) ||
+      overlap(scores, sb, c->pos, size_t(c->n_rows) * 4) || overlap(ws, need, c->k, rows_bytes(c)) ||
+      overlap(ws, need, scores, sb) || overlap(ws, need, o->q, qb) ||
+      overlap(head_entropy, size_t(c->n_seg) * 4, scores, sb))
+    return fail(KVE_EALIAS, "an output of kv_evict_score overlaps an input");
+  if (c->n_seg == 0) return KVE_OK;
+  kve::ScoreArgs a{};
+  a.k = c->k;
+  a.pos = c->pos;
+  a.seg_off = c->seg_off;
+  a.seg_len = c->seg_len;
+  a.n_rows = c->n_rows;
+  a.n_seg = c->n_seg;
+  a.n_kv = c->n_kv_heads;
+  a.max_seg_len = c->max_seg_len;
+  a.head_dim = c->head_dim;
+  a.dtype = c->dtype;
+  a.q = o->q;
+  a.q_pos = o->q_pos;
+  a.n_obs = o->n_obs;
+  a.n_q = o->n_q_heads;
+  a.max_obs = o->max_obs;
+  a.group = o->n_q_heads / c->n_kv_heads;
+  a.rows = rows;
+  a.causal = o->causal;
+  a.theta = o->rope_theta;
+  a.scores = scores;
+  a.entropy = head_entropy;
+  a.impl = impl;
+  return device_status(kve::launch_score(a, ws, static_cast<hipStream_t>(stream)), "kv_evict_score");
+}
+
+kve_status kv_evict_budgets(const float* weights, const int32_t* layer_total, const int32_t* cap, int32_t batch,
+                            int32_t n_heads, int32_t min_per_head, int32_t* budget_out, void* stream) {
+  if (batch < 0 || min_per_head < 0) return fail(KVE_EINVAL, "negative batch or floor");
+  if (n_heads < 1 || n_heads > 64) return fail(KVE_ESHAPE, "n_heads %d not in [1, 64]", n_heads);
+  if (batch > 0 && (!weights || !layer_total || !cap || !budget_out)) return fail(KVE_EINVAL, "null pointer");
+  const size_t nb = size_t(batch) * n_heads * 4;
+  if (overlap(budget_out, nb, weights, nb) || overlap(budget_out, nb, cap, nb) ||
+      overlap(budget_out, nb, layer_total, size_t(batch) * 4))
+    return fail(KVE_EALIAS, "budget_out overlaps an input");
+  return device_status(kve::launch_budgets(weights, layer_total, cap, batch, n_heads, min_per_head, budget_out,
+                                           static_cast<hipStream_t>(stream)),
+                       "kv_evict_budgets");
+}
+
+kve_status kv_evict_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total, int32_t min_per_layer,
+                                 int32_t* out, void* stream) {
+  if (!out) return fail(KVE_EINVAL, "null out");
+  if (n_layers < 1 || n_layers > 64) return fail(KVE_ESHAPE, "n_layers %d not in [1, 64]", n_layers);
+  if (!(sigma > 0.0) || min_per_layer < 0) return fail(KVE_EINVAL, "sigma must be > 0, floor >= 0");
+  if (int64_t(total) < int64_t(n_layers) * min_per_layer)
+    return fail(KVE_ESHAPE, "total %d below n_layers * floor", total);
+  return device_status(
+      kve::launch_wave_budgets(n_layers, center, sigma, total, min_per_layer, out, static_cast<hipStream_t>(stream)),
+      "kv_evict_wave_budgets");
+}
+
+size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx) {
+  if (!out || have_kept_idx || out->n_rows < 0) return 0;
+  return size_t(out->n_rows) * sizeof(int32_t);
+}
+
+kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, const int64_t* score_off,
+                                   int64_t n_scores, const int32_t* budget, int32_t uniform_budget, int32_t n_prefix,
+                                   int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  kve_status st = check_cache(in, "in", true);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(out, "out", true)) != KVE_OK) return st;
+  if (in->dtype != out->dtype || in->head_dim != out->head_dim || in->n_seg != out->n_seg ||
+      in->n_kv_heads != out->n_kv_heads)
+    return fail(KVE_ESHAPE, "in/out cache shapes differ");
+  if (n_prefix < 0 || n_recent < 0 || n_scores < 0) return fail(KVE_EINVAL, "negative prefix/recent/n_scores");
+  if (in->n_seg > 0 && !scores) return fail(KVE_EINVAL, "null scores");
+  if (!budget) {
+    if (uniform_budget < n_prefix + n_recent)
+      return fail(KVE_EBUDGET, "budget %d below prefix %d + recent %d", uniform_budget, n_prefix, n_recent);
+    const int32_t most = uniform_budget < in->max_seg_len ? uniform_budget : in->max_seg_len;
+    if (most > out->max_seg_len)
+      return fail(KVE_EBUDGET, "budget %d exceeds the output capacity %d", most, out->max_seg_len);
+  }
+  const size_t need = kept_idx ? 0 : size_t(out->n_rows) * sizeof(int32_t);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  int32_t* kept = kept_idx ? kept_idx : static_cast<int32_t*>(ws);
+  const size_t ib = rows_bytes(in), ob = rows_bytes(out);
+  const size_t ipb = size_t(in->n_rows) * 4, opb = size_t(out->n_rows) * 4;
+  const size_t kb = size_t(out->n_rows) * 4;
+  const size_t sb = size_t(n_scores) * 4;
+  const void* ins[] = {in->k, in->v, in->pos, scores, in->seg_off, in->seg_len, budget, score_off};
+  const size_t insz[] = {ib, ib, ipb, sb, size_t(in->n_seg) * 8, size_t(in->n_seg) * 4,
+                         budget ? size_t(in->n_seg) * 4 : 0, score_off ? size_t(in->n_seg) * 8 : 0};
+  const void* outs[] = {out->k, out->v, out->pos, out->seg_len, kept};
+  const size_t outsz[] = {ob, ob, opb, size_t(out->n_seg) * 4, kb};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
+  if (in->n_seg == 0) return KVE_OK;
+  kve::SelectArgs a{};
+  a.k_in = in->k;
+  a.v_in = in->v;
+  a.pos_in = in->pos;
+  a.in_off = in->seg_off;
+  a.in_len = in->seg_len;
+  a.in_rows = in->n_rows;
+  a.in_max = in->max_seg_len;
+  a.scores = scores;
+  a.score_off = score_off;
+  a.n_scores = n_scores;
+  a.budget = budget;
+  a.uniform_budget = uniform_budget;
+  a.n_prefix = n_prefix;
+  a.n_recent = n_recent;
+  a.k_out = out->k;
+  a.v_out = out->v;
+  a.pos_out = out->pos;
+  a.out_off = out->seg_off;
+  a.out_len = out->seg_len;
+  a.out_rows = out->n_rows;
+  a.out_cap = out->max_seg_len;
+  a.kept = kept;
+  a.n_seg = in->n_seg;
+  a.head_dim = in->head_dim;
+  a.elem_bytes = int32_t(elem_bytes(in->dtype));
+  return device_status(kve::launch_select_compact(a, static_cast<hipStream_t>(stream)), "kv_evict_select_compact");
+}
+
+kve_status beacon_fps_update(const void* q_in, void* q_out, const int32_t* count_in, int32_t* count_out, int32_t n_buf,
+                             int32_t cap, int32_t k_keep, int32_t head_dim, int32_t dtype, int32_t* picks,
+                             void* stream) {
+  if (dtype != KVE_BF16 && dtype != KVE_F32) return fail(KVE_EINVAL, "bad dtype %d", dtype);
+  if (n_buf < 0) return fail(KVE_EINVAL, "negative n_buf");
+  if (head_dim != 64 && head_dim != 128) return fail(KVE_ESHAPE, "head_dim %d", head_dim);
+  if (cap < 1 || cap > 64 || k_keep < 1 || k_keep > cap)
+    return fail(KVE_ESHAPE, "cap %d / k_keep %d (need 1 <= k_keep <= cap <= 64)", cap, k_keep);
+  if (size_t(4) * cap * head_dim * elem_bytes(dtype) > 65536) return fail(KVE_ESHAPE, "cap*head_dim too large");
+  if (n_buf > 0 && (!q_in || !q_out || !count_in || !count_out)) return fail(KVE_EINVAL, "null pointer");
+  if (!aligned16(q_in) || !aligned16(q_out)) return fail(KVE_EINVAL, "buffers not 16-byte aligned");
+  const size_t qb = size_t(n_buf) * cap * head_dim * elem_bytes(dtype);
+  const size_t cb = size_t(n_buf) * 4;
+  if (q_in != q_out && overlap(q_in, qb, q_out, qb)) return fail(KVE_EALIAS, "q_out partially overlaps q_in");
+  if (count_in != count_out && overlap(count_in, cb, count_out, cb))
+    return fail(KVE_EALIAS, "count_out partially overlaps count_in");
+  const size_t pb = size_t(n_buf) * k_keep * 4;
+  if (overlap(picks, pb, q_in, qb) || overlap(picks, pb, q_out, qb) || overlap(picks, pb, count_in, cb) ||
+      overlap(picks, pb, count_out, cb) || overlap(count_out, cb, q_in, qb) || overlap(count_out, cb, q_out, qb))
+    return fail(KVE_EALIAS, "picks/counts overlap the buffers");
+  return device_status(kve::launch_fps(q_in, q_out, count_in, count_out, n_buf, cap, k_keep, head_dim, dtype, picks,
+                                       static_cast<hipStream_t>(stream)),
+                       "beacon_fps_update");
+}
+
+size_t epikv_workspace_size(int32_t batch, int32_t T) {
+  if (batch < 0 || T < 0) return 0;
+  return kve::epikv_ws_bytes(batch, T);
+}
+
+kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model, int32_t window,
+                       float eps, float* g_out, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 0 || T < 0) return fail(KVE_EINVAL, "negative batch or T");
+  if (d_model != 512 && d_model != 1024 && d_model != 2048 && d_model != 4096 && d_model != 8192)
+    return fail(KVE_ESHAPE, "d_model %d", d_model);
+  if (window < 1 || window > 2048) return fail(KVE_ESHAPE, "window %d not in [1, 2048]", window);
+  if (!(eps >= 0.f)) return fail(KVE_EINVAL, "eps must be >= 0");
+  const size_t n = size_t(batch) * T;
+  if (n > 0 && (!h_a || !h_b || !scores)) return fail(KVE_EINVAL, "null pointer");
+  if (!aligned16(h_a) || !aligned16(h_b)) return fail(KVE_EINVAL, "traces not 16-byte aligned");
+  const size_t need = g_out ? 0 : kve::epikv_ws_bytes(batch, T);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  const size_t hb = n * d_model * 2;
+  const size_t gb = 2 * n * 4;
+  const float* gbuf = g_out ? g_out : static_cast<const float*>(ws);
+  if (overlap(scores, n * 4, h_a, hb) || overlap(scores, n * 4, h_b, hb) || overlap(gbuf, gb, h_a, hb) ||
+      overlap(gbuf, gb, h_b, hb) || overlap(gbuf, gb, scores, n * 4))
+    return fail(KVE_EALIAS, "an output of epikv_score overlaps an input");
+  return device_status(kve::launch_epikv(h_a, h_b, batch, T, d_model, window, eps, g_out, scores, ws,
+                                         static_cast<hipStream_t>(stream)),
+                       "epikv_score");
+}
+
+kve_status kv_rope_apply(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
+                         double rope_theta, int32_t dtype, void* stream) {
+  if (dtype != KVE_BF16 && dtype != KVE_F32) return fail(KVE_EINVAL, "bad dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(KVE_ESHAPE, "head_dim %d", head_dim);
+  if (n_rows < 0) return fail(KVE_EINVAL, "negative n_rows");
+  if (!(rope_theta > 0.0)) return fail(KVE_EINVAL, "rope_theta must be > 0");
+  if (n_rows > 0 && (!src || !dst || !pos)) return fail(KVE_EINVAL, "null pointer");
+  if (overlap(src, size_t(n_rows) * head_dim * 4, dst, size_t(n_rows) * head_dim * elem_bytes(dtype)))
+    return fail(KVE_EALIAS, "dst overlaps src");
+  return device_status(
+      kve::launch_rope_rows(src, dst, pos, n_rows, head_dim, rope_theta, dtype, static_cast<hipStream_t>(stream)),
+      "kv_rope_apply");
+}
+
+}  // extern "C"

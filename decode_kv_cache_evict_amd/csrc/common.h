@@ -1,0 +1,93 @@
+// Device helpers shared by the eviction-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvevict.h"
+
+namespace kve {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return uint16_t(b >> 16);
+}
+
+// double -> bf16 rounded once, to nearest even.  The float conversion is exact
+// enough unless it lands on a bf16 midpoint, where the double decides.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  float r = float(x);
+  uint32_t b = __float_as_uint(r);
+  if ((b & 0xFFFFu) == 0x8000u) {
+    double ax = fabs(x), ar = fabs(double(r));
+    if (ax > ar) return uint16_t((b + 0x8000u) >> 16);  // away from zero
+    if (ax < ar) return uint16_t(b >> 16);              // toward zero
+  }
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return uint16_t(b >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ uint16_t from_f64(double x) { return f64_to_bf16(x); }
+  static __device__ __forceinline__ float widen(uint16_t v) { return bf16_to_f32(v); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float from_f64(double x) { return float(x); }
+  static __device__ __forceinline__ float widen(float v) { return v; }
+};
+
+// ---------------------------------------------------------------- RoPE
+// Rotate the pair (a, b) of frequency index i (of head_dim d) to position p:
+// (a cos - b sin, b cos + a sin), angle p * theta^(-2i/d) in double.
+struct RotPair { double a, b; };
+__device__ __forceinline__ RotPair rope_pair(double a, double b, int i, int d, int p, double theta) {
+#pragma clang fp contract(off)
+  double inv = pow(theta, -2.0 * double(i) / double(d));
+  double ang = double(p) * inv;
+  double s, c;
+  sincos(ang, &s, &c);
+  RotPair r;
+  r.a = a * c - b * s;
+  r.b = b * c + a * s;
+  return r;
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Order-preserving map of fp32 values to uint32 (larger float -> larger key;
+// -0.0 and +0.0 compare equal, as IEEE values do).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+}  // namespace kve

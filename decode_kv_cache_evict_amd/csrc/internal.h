@@ -1,0 +1,72 @@
+// Launch interfaces between the C-ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kve {
+
+constexpr int kScoreChunk = 256;   // keys per score work-group
+constexpr int kMaxObsRows = 256;   // group * max_obs
+
+struct ScoreArgs {
+  // cache
+  const void* k;
+  const int32_t* pos;
+  const int64_t* seg_off;
+  const int32_t* seg_len;
+  int64_t n_rows;
+  int32_t n_seg, n_kv, max_seg_len, head_dim, dtype;
+  // observation queries
+  const void* q;          // pre-RoPE [B, Hq, max_obs, D]
+  const int32_t* q_pos;   // [B, max_obs]
+  const int32_t* n_obs;   // [B] or null
+  int32_t n_q, max_obs, group, rows, causal;
+  double theta;
+  // outputs and workspace
+  float* scores;
+  float* entropy;
+  void* qr;               // rotated queries [B, Hq, max_obs, D] (workspace)
+  float2* stats;          // [n_seg, n_chunks, rows] (m * log2e/sqrt(D), l) (workspace)
+  int32_t n_chunks;
+  int32_t impl;           // 0: MFMA (bf16), 1: plain VALU
+};
+
+size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
+                             int32_t n_seg, int32_t max_seg_len, int32_t rows);
+hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st);
+
+struct SelectArgs {
+  // input cache
+  const void* k_in; const void* v_in; const int32_t* pos_in;
+  const int64_t* in_off; const int32_t* in_len; int64_t in_rows; int32_t in_max;
+  // scores
+  const float* scores; const int64_t* score_off; int64_t n_scores;
+  // budgets
+  const int32_t* budget; int32_t uniform_budget; int32_t n_prefix, n_recent;
+  // output cache
+  void* k_out; void* v_out; int32_t* pos_out;
+  const int64_t* out_off; int32_t* out_len; int64_t out_rows; int32_t out_cap;
+  int32_t* kept;          // [out_rows]
+  int32_t n_seg, head_dim, elem_bytes;
+};
+hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st);
+
+hipError_t launch_budgets(const float* w, const int32_t* total, const int32_t* cap, int32_t batch,
+                          int32_t n_heads, int32_t min_per_head, int32_t* out, hipStream_t st);
+hipError_t launch_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total, int32_t lo,
+                               int32_t* out, hipStream_t st);
+
+hipError_t launch_fps(const void* q_in, void* q_out, const int32_t* count_in, int32_t* count_out,
+                      int32_t n_buf, int32_t cap, int32_t k_keep, int32_t head_dim, int32_t dtype,
+                      int32_t* picks, hipStream_t st);
+
+size_t epikv_ws_bytes(int32_t batch, int32_t T);
+hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model,
+                        int32_t window, float eps, float* g_out, float* scores, void* ws, hipStream_t st);
+
+hipError_t launch_rope_rows(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
+                            double theta, int32_t dtype, hipStream_t st);
+
+}  // namespace kve

@@ -1,0 +1,467 @@
+// Observation-set attention scores (BeaconKV, "打分时的 RoPE 对齐"):
+//   scores[j] = max over the group's observation rows r of softmax_r(q_r . k_j / sqrt(d))
+// computed in two passes over each segment's keys:
+//   pass 1: per (segment, 256-key chunk) work-group, partial row statistics
+//           (running max m, sum of exp2 below it) of the logits;
+//   pass 2: merge the chunk statistics into each row's log-sum-exp, recompute
+//           the logits of the chunk and take the per-key maximum of exp2(x - lse).
+// The bf16 path contracts on the matrix cores (v_mfma_f32_16x16x32_bf16) with
+// key tiles staged through LDS by coalesced 16-byte loads; a plain VALU path
+// serves fp32 caches.
+#include <climits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace kve {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kInf = __builtin_huge_valf();
+
+// Position a key is compared against by observation row r of segment s;
+// -1 marks an absent row (never sees a key).
+__device__ __forceinline__ int row_position(const ScoreArgs& a, int b, int r) {
+  if (r >= a.rows) return -1;
+  const int i = r % a.max_obs;
+  const int no = a.n_obs ? a.n_obs[b] : a.max_obs;
+  if (i >= no) return -1;
+  return a.causal ? a.q_pos[b * a.max_obs + i] : INT_MAX - 1;
+}
+
+__device__ __forceinline__ int64_t row_qr_index(const ScoreArgs& a, int b, int g, int r) {
+  const int h = g * a.group + r / a.max_obs;
+  const int i = r % a.max_obs;
+  return (int64_t(b) * a.n_q + h) * a.max_obs + i;
+}
+
+__device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& off, int& n) {
+  off = a.seg_off[s];
+  n = a.seg_len[s];
+  return n >= 0 && n <= a.max_seg_len && off >= 0 && off + n <= a.n_rows;
+}
+
+// ------------------------------------------------------------ query rotation
+// Rotate every observation row to its q_pos (double-precision angle and
+// rotation) and round to the storage dtype.  Rows past n_obs are zeroed.
+template <typename T>
+__global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
+                                  const int32_t* __restrict__ n_obs, T* __restrict__ qr,
+                                  int64_t n_pairs, int n_q, int max_obs, int D, double theta) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n_pairs) return;
+  const int half = D / 2;
+  const int i = int(idx % half);
+  const int64_t row = idx / half;                 // (b * n_q + h) * max_obs + o
+  const int o = int(row % max_obs);
+  const int b = int(row / (int64_t(max_obs) * n_q));
+  const int no = n_obs ? n_obs[b] : max_obs;
+  const T* src = q + row * D;
+  T* dst = qr + row * D;
+  if (o >= no) {
+    dst[i] = Elem<T>::from_f64(0.0);
+    dst[i + half] = Elem<T>::from_f64(0.0);
+    return;
+  }
+  RotPair r = rope_pair(double(Elem<T>::widen(src[i])), double(Elem<T>::widen(src[i + half])), i, D,
+                        q_pos[b * max_obs + o], theta);
+  dst[i] = Elem<T>::from_f64(r.a);
+  dst[i + half] = Elem<T>::from_f64(r.b);
+}
+
+// Merge a row's chunk statistics into its log-sum-exp (log2 units);
+// +inf when the row saw no key.
+__device__ __forceinline__ float merge_row(const float2* st, int nch, int rows) {
+  float M = kNegBig;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[int64_t(c) * rows].x);
+  float L = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float2 v = st[int64_t(c) * rows];
+    L += v.y * exp2f(v.x - M);
+  }
+  return L > 0.f ? M + log2f(L) : kInf;
+}
+
+// ------------------------------------------------------------ VALU path
+// One thread per key; query rows broadcast from LDS.  Used for fp32 caches.
+template <typename T, int D, bool PASS2>
+__global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* qs = reinterpret_cast<T*>(smem);                                   // [rows, D]
+  float2* wst = reinterpret_cast<float2*>(smem + size_t(a.rows) * D * sizeof(T));  // [4, rows]
+  float* lse_s = reinterpret_cast<float*>(wst + 4 * a.rows);            // [rows]
+  int* rp_s = reinterpret_cast<int*>(lse_s + a.rows);                   // [rows]
+
+  const int s = blockIdx.y, ch = blockIdx.x;
+  int64_t off;
+  int n;
+  if (!segment_ok(a, s, off, n)) return;
+  const int k0 = ch * kScoreChunk;
+  if (k0 >= n) return;
+  const int b = s / a.n_kv, g = s % a.n_kv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float c = kLog2e / sqrtf(float(D));
+  const T* qr = static_cast<const T*>(a.qr);
+
+  for (int e = tid; e < a.rows * D; e += blockDim.x) {
+    const int r = e / D, d = e % D;
+    qs[e] = qr[row_qr_index(a, b, g, r) * D + d];
+  }
+  for (int r = tid; r < a.rows; r += blockDim.x) {
+    rp_s[r] = row_position(a, b, r);
+    if (PASS2) {
+      const int nch = (n + kScoreChunk - 1) / kScoreChunk;
+      lse_s[r] = merge_row(a.stats + int64_t(s) * a.n_chunks * a.rows + r, nch, a.rows);
+    }
+  }
+  __syncthreads();
+
+  const int j = k0 + tid;
+  const bool valid = j < n;
+  float kv[D];
+  int kpos = INT_MAX;
+  const T* kp = static_cast<const T*>(a.k) + (off + (valid ? j : 0)) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) kv[d] = valid ? Elem<T>::widen(kp[d]) : 0.f;
+  if (valid) kpos = a.pos[off + j];
+
+  float best = -kInf;
+  for (int r = 0; r < a.rows; ++r) {
+    const T* qrow = qs + r * D;
+    float x = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) x = fmaf(Elem<T>::widen(qrow[d]), kv[d], x);
+    const bool vis = valid && kpos <= rp_s[r];
+    if (PASS2) {
+      const float y = vis ? fmaf(x, c, -lse_s[r]) : -kInf;
+      best = fmaxf(best, y);
+    } else {
+      const float xv = vis ? x : -kInf;
+      const float m = wave_max(fmaxf(xv, kNegBig));
+      const float l = wave_sum(vis ? exp2f(fmaf(x, c, -m * c)) : 0.f);
+      if (lane == 0) wst[w * a.rows + r] = make_float2(m, l);
+    }
+  }
+  if (PASS2) {
+    if (valid) a.scores[off + j] = exp2f(best);
+    return;
+  }
+  __syncthreads();
+  for (int r = tid; r < a.rows; r += blockDim.x) {
+    float M = kNegBig;
+    for (int q = 0; q < 4; ++q) M = fmaxf(M, wst[q * a.rows + r].x);
+    float L = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const float2 v = wst[q * a.rows + r];
+      L += v.y * exp2f((v.x - M) * c);
+    }
+    a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(M * c, L);
+  }
+}
+
+// ------------------------------------------------------------ MFMA path (bf16)
+// Work-group = 4 waves over one (segment, 256-key chunk).  Wave w owns row
+// tiles w*RT .. w*RT+RT-1 (16 rows each) and keeps their rotated queries in
+// registers as MFMA A operands.  Keys stream through a double-buffered LDS
+// tile of 64 keys; each wave reads them as B operands.  For
+// v_mfma_f32_16x16x32_bf16 lane l holds A row l%16 / B column l%16 with
+// k-slice 8*(l/16)..+7 of each 32-wide step, and result rows 4*(l/16)+i of
+// column l%16.
+template <int D, int RT, bool PASS2>
+__global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
+  constexpr int KS = D / 32;                 // MFMA k-steps
+  constexpr int BK = 64;                     // keys per LDS batch
+  constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int CPT = BK * CPR / 256;        // chunks per thread per batch
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][BK * LS];
+  __shared__ int kps[2][BK];
+  __shared__ float red[4][BK];
+  __shared__ float lse_s[kMaxObsRows];
+
+  const int s = blockIdx.y, ch = blockIdx.x;
+  int64_t off;
+  int n;
+  if (!segment_ok(a, s, off, n)) return;
+  const int k0 = ch * kScoreChunk;
+  if (k0 >= n) return;
+  const int k1 = min(n, k0 + kScoreChunk);
+  const int b = s / a.n_kv, g = s % a.n_kv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const float c = kLog2e / sqrtf(float(D));
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* qr = static_cast<const uint16_t*>(a.qr);
+
+  if (PASS2) {
+    const int nch = (n + kScoreChunk - 1) / kScoreChunk;
+    for (int r = tid; r < a.rows; r += 256)
+      lse_s[r] = merge_row(a.stats + int64_t(s) * a.n_chunks * a.rows + r, nch, a.rows);
+  }
+
+  // A operands and per-result-row state.
+  bf16x8 qa[RT][KS];
+  int rowpos[RT][4];
+  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int t = w * RT + rt;
+    const int ra = 16 * t + col;
+    const bool ok = ra < a.rows && row_position(a, b, ra) >= 0;
+    const uint16_t* src = qr + (ok ? row_qr_index(a, b, g, ra) : 0) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(src + ks * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
+      qa[rt][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rowpos[rt][i] = row_position(a, b, 16 * t + 4 * quad + i);
+      st0[rt][i] = kNegBig;
+      st1[rt][i] = 0.f;
+    }
+  }
+
+  uint4 pre[CPT];
+  int prepos = INT_MAX;
+  auto load_batch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = tid + 256 * u;
+      const int key = cidx / CPR, part = cidx % CPR;
+      const int j = kb + key;
+      pre[u] = j < k1 ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < BK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
+  };
+  auto store_batch = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = tid + 256 * u;
+      const int key = cidx / CPR, part = cidx % CPR;
+      *reinterpret_cast<uint4*>(&kt[buf][key * LS + part * 8]) = pre[u];
+    }
+    if (tid < BK) kps[buf][tid] = prepos;
+  };
+
+  load_batch(k0);
+  store_batch(0);
+  __syncthreads();
+  if (PASS2) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (w * RT + rt) + 4 * quad + i;
+        st0[rt][i] = r < a.rows ? lse_s[r] : kInf;
+      }
+  }
+
+  int buf = 0;
+  for (int kb = k0; kb < k1; kb += BK) {
+    const bool has_next = kb + BK < k1;
+    if (has_next) load_batch(kb + BK);
+
+    f32x4 acc[4][RT];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x8 bfr[KS];
+      const uint16_t* krow = &kt[buf][(q4 * 16 + col) * LS + quad * 8];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], bfr[ks], x, 0, 0, 0);
+        acc[q4][rt] = x;
+      }
+    }
+    int kpos[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[buf][q4 * 16 + col];
+
+    if (!PASS2) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) v[q4] = kpos[q4] <= rowpos[rt][i] ? acc[q4][rt][i] : -kInf;
+          const float mo = st0[rt][i];
+          const float mx = fmaxf(fmaxf(mo, fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
+          const float mc = mx * c;
+          float l = st1[rt][i] * exp2f(fmaf(mo, c, -mc));
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) l += exp2f(fmaf(v[q4], c, -mc));
+          st0[rt][i] = mx;
+          st1[rt][i] = l;
+        }
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float best = -kInf;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = kpos[q4] <= rowpos[rt][i] ? fmaf(acc[q4][rt][i], c, -st0[rt][i]) : -kInf;
+            best = fmaxf(best, y);
+          }
+        best = fmaxf(best, __shfl_xor(best, 16, kWave));
+        best = fmaxf(best, __shfl_xor(best, 32, kWave));
+        if (quad == 0) red[w][q4 * 16 + col] = best;
+      }
+    }
+    __syncthreads();
+    if (has_next) store_batch(buf ^ 1);
+    if (PASS2 && tid < BK) {
+      const int j = kb + tid;
+      if (j < k1) {
+        const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        a.scores[off + j] = exp2f(m);
+      }
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (!PASS2) {
+    // combine the 16 key columns held by each lane group, then publish
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = st0[rt][i], l = st1[rt][i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float m2 = __shfl_xor(m, o, kWave), l2 = __shfl_xor(l, o, kWave);
+          const float M = fmaxf(m, m2);
+          l = l * exp2f((m - M) * c) + l2 * exp2f((m2 - M) * c);
+          m = M;
+        }
+        const int r = 16 * (w * RT + rt) + 4 * quad + i;
+        if (col == 0 && r < a.rows)
+          a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(m * c, l);
+      }
+  }
+}
+
+// ------------------------------------------------------------ entropy
+// E = (ln S - sum(s ln s) / S) / ln n over one segment's scores, in double.
+__global__ __launch_bounds__(256) void entropy_kernel(ScoreArgs a) {
+  __shared__ double part[2][4];
+  const int s = blockIdx.x;
+  int64_t off;
+  int n;
+  if (!segment_ok(a, s, off, n)) return;
+  double S = 0.0, Q = 0.0;
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const double v = a.scores[off + j];
+    S += v;
+    if (v > 0.0) Q += v * log(v);
+  }
+  S = wave_sum_f64(S);
+  Q = wave_sum_f64(Q);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    part[0][w] = S;
+    part[1][w] = Q;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    S = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+    Q = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    double E = 0.0;
+    if (n > 1 && S > 0.0) E = (log(S) - Q / S) / log(double(n));
+    a.entropy[s] = float(E);
+  }
+}
+
+template <int D, int RT>
+hipError_t launch_mfma(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((score_mfma_kernel<D, RT, false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_mfma_kernel<D, RT, true>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_rt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  const int tiles = (a.rows + 15) / 16;
+  const int rt = (tiles + 3) / 4;
+  switch (rt) {
+    case 1: return launch_mfma<D, 1>(a, grid, st);
+    case 2: return launch_mfma<D, 2>(a, grid, st);
+    case 3: return launch_mfma<D, 3>(a, grid, st);
+    default: return launch_mfma<D, 4>(a, grid, st);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  const size_t sh = size_t(a.rows) * D * sizeof(T) + size_t(a.rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
+  hipLaunchKernelGGL((score_valu_kernel<T, D, false>), grid, dim3(256), sh, st, a);
+  hipLaunchKernelGGL((score_valu_kernel<T, D, true>), grid, dim3(256), sh, st, a);
+  return hipGetLastError();
+}
+
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
+                             int32_t n_seg, int32_t max_seg_len, int32_t rows) {
+  const size_t elem = dtype == 0 ? 2 : 4;
+  const size_t qr = align_up(size_t(batch) * n_q * max_obs * head_dim * elem);
+  const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
+  const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
+  return qr + st;
+}
+
+size_t valu_lds_bytes(int rows, int D, int dtype) {
+  return size_t(rows) * D * (dtype == 0 ? 2 : 4) + size_t(rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
+}
+
+hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
+  const int batch = a.n_seg / a.n_kv;
+  const size_t elem = a.dtype == 0 ? 2 : 4;
+  a.qr = ws;
+  a.stats = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                      align_up(size_t(batch) * a.n_q * a.max_obs * a.head_dim * elem));
+  a.n_chunks = (a.max_seg_len + kScoreChunk - 1) / kScoreChunk;
+  const int64_t n_pairs = int64_t(batch) * a.n_q * a.max_obs * (a.head_dim / 2);
+  const dim3 rg(unsigned((n_pairs + 255) / 256));
+  if (n_pairs > 0) {
+    if (a.dtype == 0)
+      hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
+                         a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_pairs, a.n_q, a.max_obs, a.head_dim,
+                         a.theta);
+    else
+      hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
+                         a.n_obs, static_cast<float*>(a.qr), n_pairs, a.n_q, a.max_obs, a.head_dim, a.theta);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
+  const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
+  if (a.dtype == 0 && a.impl == 0) {
+    e = a.head_dim == 128 ? launch_mfma_rt<128>(a, grid, st) : launch_mfma_rt<64>(a, grid, st);
+  } else if (a.dtype == 0) {
+    e = a.head_dim == 128 ? launch_valu<uint16_t, 128>(a, grid, st) : launch_valu<uint16_t, 64>(a, grid, st);
+  } else {
+    e = a.head_dim == 128 ? launch_valu<float, 128>(a, grid, st) : launch_valu<float, 64>(a, grid, st);
+  }
+  if (e != hipSuccess) return e;
+  if (a.entropy) {
+    hipLaunchKernelGGL(entropy_kernel, dim3(unsigned(a.n_seg)), dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace kve

@@ -1,0 +1,214 @@
+// Protected top-K selection and gather compaction (BeaconKV, "打分时的 RoPE 对齐":
+// the prefix and a short recent span are always kept and the rest of the
+// budget goes to the highest scores; "📊 实验": evicted entries are dropped for
+// good).
+//
+// select: one work-group per segment.  The K-th largest candidate score is found
+// by an MSB-first radix select over order-preserving 32-bit keys (four 8-bit
+// digit passes over LDS histograms); ties at the threshold go to the lower
+// slots.  Kept slots are then emitted in ascending order by a block-wide
+// ballot scan.
+// compact: a grid over (segment, 64-row tiles) that gathers kept K/V rows with
+// 16-byte loads and stores, and their positions.
+#include "common.h"
+#include "internal.h"
+
+namespace kve {
+
+namespace {
+
+constexpr int kSelBlock = 512;
+constexpr int kSelWaves = kSelBlock / kWave;
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
+
+// Exclusive block scan of a 0/1 flag; returns this thread's prefix and writes the total.
+__device__ __forceinline__ int block_flag_scan(bool f, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const int in_wave = __popcll(m & lanemask_lt(lane));
+  if (lane == 0) wtot[w] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < kSelWaves; ++q) {
+    const int t = wtot[q];
+    before += q < w ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + in_wave;
+}
+
+__global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_prefix, sh_kk;
+  __shared__ int wtot_a[kSelWaves], wtot_b[kSelWaves];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+
+  const int64_t oo = a.out_off[s];
+  const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
+  const int64_t io = a.in_off[s];
+  const int n = a.in_len[s];
+  const bool in_ok = n >= 0 && n <= a.in_max && io >= 0 && io + n <= a.in_rows;
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  const int64_t so = a.score_off ? a.score_off[s] : io;
+  const bool sc_ok = so >= 0 && so + n <= a.n_scores;
+  const int keep_n = K >= n ? n : K;
+  const bool bud_ok = K >= n || (K >= P + R && K >= 0);
+  if (!(out_ok && in_ok && sc_ok && bud_ok) || keep_n > a.out_cap) {
+    if (tid == 0) a.out_len[s] = -1;
+    return;
+  }
+  if (K >= n) {
+    for (int j = tid; j < n; j += kSelBlock) a.kept[oo + j] = j;
+    if (tid == 0) a.out_len[s] = n;
+    return;
+  }
+  const float* sc = a.scores + so;
+  const int kc = K - P - R;                 // candidates to take from [P, n-R)
+  uint32_t prefix = 0, mask = 0;
+  uint32_t kk = uint32_t(kc);
+  if (kc == 0) {
+    prefix = 0xFFFFFFFFu;                   // nothing exceeds it, nothing ties into it
+  } else {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int d = tid; d < 256; d += kSelBlock) hist[d] = 0;
+      __syncthreads();
+      for (int j = P + tid; j < n - R; j += kSelBlock) {
+        const uint32_t key = float_order_key(sc[j]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        uint32_t h[4], loc = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = hist[255 - 4 * tid - i];
+          loc += h[i];
+        }
+        uint32_t incl = loc;                // inclusive scan over lanes, high digits first
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t v = __shfl_up(incl, o, kWave);
+          if (tid >= o) incl += v;
+        }
+        const uint32_t excl = incl - loc;
+        const uint64_t hit = __ballot(incl >= kk);
+        const int first = __ffsll((unsigned long long)hit) - 1;
+        if (tid == first) {
+          uint32_t cum = excl;
+          int digit = 0;
+          uint32_t above = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (cum + h[i] >= kk) {
+              digit = 255 - 4 * tid - i;
+              above = cum;
+              break;
+            }
+            cum += h[i];
+          }
+          sh_prefix = prefix | (uint32_t(digit) << shift);
+          sh_kk = kk - above;
+        }
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      kk = sh_kk;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+  }
+  // prefix = threshold key T; kk = how many candidates equal to T are kept.
+  int base = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < n; j0 += kSelBlock) {
+    const int j = j0 + tid;
+    const bool in = j < n;
+    const bool cand = in && j >= P && j < n - R;
+    const uint32_t key = cand ? float_order_key(sc[j]) : 0u;
+    const bool eq = cand && key == prefix;
+    int eq_tot;
+    const int eq_rank = eq_seen + block_flag_scan(eq, wtot_a, eq_tot);
+    const bool keep = in && (!cand || key > prefix || (eq && uint32_t(eq_rank) < kk));
+    int keep_tot;
+    const int at = base + block_flag_scan(keep, wtot_b, keep_tot);
+    if (keep && at < K) a.kept[oo + at] = j;
+    base += keep_tot;
+    eq_seen += eq_tot;
+  }
+  if (tid == 0) a.out_len[s] = K;
+}
+
+// Gather kept rows.  RB = row bytes; CPR 16-byte chunks per row; each thread
+// moves UNR rows of K and V per tile.
+template <int CPR>
+__global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
+  constexpr int RPP = 256 / CPR;            // rows per pass
+  constexpr int UNR = 4;
+  constexpr int RPW = RPP * UNR;            // rows per work-group
+  const int s = blockIdx.y;
+  const int out_n = a.out_len[s];
+  const int r0 = blockIdx.x * RPW;
+  if (out_n <= 0 || out_n > a.out_cap || r0 >= out_n) return;
+  const int64_t io = a.in_off[s], oo = a.out_off[s];
+  const int n_in = a.in_len[s];
+  const int part = threadIdx.x % CPR;
+  const int rsub = threadIdx.x / CPR;
+  const uint4* kin = static_cast<const uint4*>(a.k_in);
+  const uint4* vin = static_cast<const uint4*>(a.v_in);
+  uint4* kout = static_cast<uint4*>(a.k_out);
+  uint4* vout = static_cast<uint4*>(a.v_out);
+  uint4 kb[UNR], vb[UNR];
+  int src[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int r = r0 + u * RPP + rsub;
+    int j = r < out_n ? a.kept[oo + r] : -1;
+    if (j >= n_in) j = -1;
+    src[u] = j;
+    if (j >= 0) {
+      kb[u] = kin[(io + j) * CPR + part];
+      vb[u] = vin[(io + j) * CPR + part];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int r = r0 + u * RPP + rsub;
+    if (src[u] >= 0) {
+      kout[(oo + r) * CPR + part] = kb[u];
+      vout[(oo + r) * CPR + part] = vb[u];
+      if (part == 0) a.pos_out[oo + r] = a.pos_in[io + src[u]];
+    }
+  }
+}
+
+template <int CPR>
+hipError_t launch_compact(const SelectArgs& a, hipStream_t st) {
+  constexpr int RPW = (256 / CPR) * 4;
+  const dim3 grid(unsigned((a.out_cap + RPW - 1) / RPW), unsigned(a.n_seg));
+  hipLaunchKernelGGL(compact_kernel<CPR>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st) {
+  if (a.n_seg == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(a.n_seg)), dim3(kSelBlock), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.out_cap == 0) return e;
+  const int cpr = a.head_dim * a.elem_bytes / 16;
+  switch (cpr) {
+    case 8: return launch_compact<8>(a, st);
+    case 16: return launch_compact<16>(a, st);
+    case 32: return launch_compact<32>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kve

@@ -1,0 +1,218 @@
+/*
+ * kvevict.h — C ABI of the decode-time KV-cache eviction step for MI355X (gfx950).
+ *
+ * The step, as the BeaconKV page describes it (sections "观察 query 集 = 最近查询 +
+ * 信标查询", "Continual FPS：有界内存的在线最远点采样", "打分时的 RoPE 对齐" and
+ * "📊 实验"): every cached key of every KV head is scored by a small observation
+ * set of queries (recent queries at their own RoPE positions, beacon queries kept
+ * pre-RoPE and rotated to the current step t), by a per-row softmax of q.k/sqrt(d)
+ * max-aggregated over the queries and the GQA group; the prefix and the recent
+ * window are always kept, the remaining budget goes to the top scores, and the
+ * cache is compacted.  Per-head budgets may follow the ReasonAlloc page ("Core
+ * Mechanism", "Key Concepts"); the EPIKV page (方法论 parts 1 and 3) supplies an
+ * attention-free alternative score.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     keeps no state and allocates no device memory; scratch comes from a
+ *     caller-provided workspace whose size the *_workspace_size calls return.
+ *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *     NULL is the null stream).  No call synchronises.
+ *   - Arguments are checked on the host BEFORE any launch; on an error status
+ *     nothing is launched and nothing is written.  Values that live in device
+ *     memory (segment offsets, lengths, budgets) are checked by the kernels,
+ *     which never read or write outside the declared buffers: a segment whose
+ *     metadata is out of range is skipped, and select/compact report it by
+ *     writing -1 as that segment's output length.
+ *   - Launch failures return KVE_EDEVICE.  No C++ exception crosses the ABI.
+ *     kve_last_error() returns a message for the last non-OK status of the
+ *     calling thread.
+ *   - Storage dtypes: KVE_BF16 (bfloat16) or KVE_F32.  head_dim is 64 or 128.
+ *
+ * Cache layout (one layer, or several layers folded into the batch)
+ *   A cache is a set of segments, one per (request b, KV head g), s = b*n_kv_heads+g.
+ *   Segment s owns rows seg_off[s] .. seg_off[s]+seg_len[s]-1 of k, v and pos; a
+ *   row of k or v is head_dim contiguous elements.  K is stored post-RoPE at the
+ *   row's original position pos[row].  Every segment must have room for
+ *   max_seg_len rows (seg_off[s] + max_seg_len <= n_rows) when the cache is an
+ *   output; as an input seg_len[s] <= max_seg_len.
+ */
+#ifndef KVEVICT_H
+#define KVEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVE_ABI_VERSION 1
+
+typedef enum {
+  KVE_OK = 0,
+  KVE_EINVAL = 1,      /* null pointer, bad enum, negative size */
+  KVE_ESHAPE = 2,      /* unsupported or inconsistent shape */
+  KVE_EALIAS = 3,      /* an output overlaps an input it must not overlap */
+  KVE_EBUDGET = 4,     /* budget below the protected prefix + recent window */
+  KVE_EWORKSPACE = 5,  /* workspace missing or too small */
+  KVE_EDEVICE = 6      /* HIP runtime / launch failure */
+} kve_status;
+
+typedef enum { KVE_BF16 = 0, KVE_F32 = 1 } kve_dtype;
+
+typedef struct kve_cache {
+  int32_t dtype;            /* kve_dtype of k and v */
+  int32_t n_seg;            /* segments = batch * n_kv_heads */
+  int32_t n_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t max_seg_len;      /* bound on every seg_len; per-segment row capacity of an output */
+  int32_t reserved;
+  int64_t n_rows;           /* rows allocated in k, v and pos */
+  void* k;                  /* [n_rows, head_dim] post-RoPE keys */
+  void* v;                  /* [n_rows, head_dim] values */
+  int32_t* pos;             /* [n_rows] original token position of each row */
+  const int64_t* seg_off;   /* [n_seg] first row of each segment */
+  int32_t* seg_len;         /* [n_seg] valid rows (written by kv_evict_select_compact on an output) */
+} kve_cache;
+
+typedef struct kve_obs {
+  const void* q;            /* [batch, n_q_heads, max_obs, head_dim] PRE-RoPE queries, cache dtype */
+  const int32_t* q_pos;     /* [batch, max_obs] position each row is rotated to:
+                               tau_i for a recent query, the current step t for a beacon */
+  const int32_t* n_obs;     /* [batch] valid rows per request (<= max_obs), or NULL = max_obs */
+  int32_t n_q_heads;        /* multiple of n_kv_heads; query head h scores KV head h / (n_q_heads/n_kv_heads) */
+  int32_t max_obs;          /* (n_q_heads/n_kv_heads) * max_obs <= 256 */
+  double rope_theta;        /* RoPE base; pairs (x_i, x_{i+d/2}), frequency theta^(-2i/d) */
+  int32_t causal;           /* 1: key j visible to row i iff pos[j] <= q_pos[i]; 0: all keys visible */
+  int32_t reserved;
+} kve_obs;
+
+/* Workspace bytes kv_evict_score needs for this cache/observation shape. */
+size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o);
+
+/*
+ * kv_evict_score — BeaconKV "打分时的 RoPE 对齐": rotate each observation query to
+ * its q_pos (angle formed in double precision, rotated value rounded to the cache
+ * dtype), take logits q.k/sqrt(d) in fp32 over every visible cached key of the
+ * segment, a per-row softmax over the segment, and
+ *   scores[row] = max over the group's query heads and observation rows of p.
+ * scores: [c->n_rows] fp32, aligned with the cache rows (rows outside every
+ * segment are not written).  head_entropy: optional [n_seg] fp32, the
+ * normalised entropy of each segment's score distribution (ReasonAlloc "Key
+ * Concepts": head utility), or NULL.
+ * Errors: EINVAL (null pointers), ESHAPE (head_dim, group, rows > 256),
+ * EWORKSPACE, EDEVICE.
+ */
+kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, float* head_entropy,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_evict_budgets — ReasonAlloc "Core Mechanism" (online head-wise
+ * reallocation): per request b, split layer_total[b] over the n_heads heads
+ * proportionally to weights[b*n_heads+g] with floor min_per_head and cap
+ * cap[b*n_heads+g] (x_g = clamp(lam*w_g, min(floor,cap_g), cap_g), sum =
+ * min(total, sum cap)), then round by largest remainder (ties to the lower
+ * head).  All-zero weights split equally.  Computed in double precision.
+ * budget_out: [batch*n_heads] int32.  A request whose total is below the sum of
+ * its floors gets -1 in every head.  Errors: EINVAL, ESHAPE (n_heads > 64), EDEVICE.
+ */
+kve_status kv_evict_budgets(const float* weights, const int32_t* layer_total, const int32_t* cap,
+                            int32_t batch, int32_t n_heads, int32_t min_per_head,
+                            int32_t* budget_out, void* stream);
+
+/*
+ * kv_evict_wave_budgets — ReasonAlloc "Core Mechanism" (offline layer-wise
+ * preallocation, the mid-peaked "Reasoning Wave"): per-layer base budgets
+ * proportional to exp(-(l-center)^2 / (2 sigma^2)), floor min_per_layer,
+ * summing exactly to total, largest-remainder rounding.  out: [n_layers] int32
+ * device.  Errors: EINVAL, ESHAPE (n_layers > 64 or total < n_layers*floor), EDEVICE.
+ */
+kve_status kv_evict_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total,
+                                 int32_t min_per_layer, int32_t* out, void* stream);
+
+/* Workspace bytes kv_evict_select_compact needs (0 when kept_idx is supplied). */
+size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx);
+
+/*
+ * kv_evict_select_compact — BeaconKV "打分时的 RoPE 对齐" and "📊 实验": per segment
+ * with n rows and budget K: if K >= n keep every row; otherwise keep slots
+ * [0, n_prefix) and [n-n_recent, n) and the K-n_prefix-n_recent other slots with
+ * the highest score (score descending, slot ascending; scores compared as fp32
+ * values, so -0.0 ties with +0.0; NaN is not supported), then gather-compact K, V and pos, in ascending slot order,
+ * into the output segment and set out->seg_len[s].
+ *   scores: fp32 [n_scores]; the score of slot j of segment s is
+ *           scores[(score_off ? score_off[s] : in->seg_off[s]) + j]
+ *           (score_off lets one per-token score serve every KV head of a request;
+ *           a segment whose scores would fall outside [0, n_scores) is rejected).
+ *   budget: [n_seg] device int32, or NULL to use uniform_budget for every segment.
+ *   kept_idx: optional [out->n_rows] int32; row out->seg_off[s]+i receives the
+ *           source slot of output row i.
+ * The output must not overlap the input (EALIAS); out->max_seg_len is each output
+ * segment's capacity.  A segment whose budget is below n_prefix+n_recent (and
+ * below n), or larger than the output capacity, or whose metadata is out of
+ * range, gets out->seg_len[s] = -1 and no rows.
+ * Errors: EINVAL, ESHAPE (dtype/head_dim/n_seg mismatch), EALIAS,
+ * EBUDGET (uniform_budget < n_prefix+n_recent, or > out->max_seg_len), EWORKSPACE, EDEVICE.
+ */
+kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, const int64_t* score_off,
+                                   int64_t n_scores, const int32_t* budget, int32_t uniform_budget,
+                                   int32_t n_prefix, int32_t n_recent, int32_t* kept_idx,
+                                   kve_cache* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * beacon_fps_update — BeaconKV "Continual FPS": for each of n_buf buffers of
+ * pre-RoPE queries ([n_buf, cap, head_dim], dtype) whose count_in equals cap, run
+ * farthest-point sampling under the cosine distance 1 - cos: first pick row 0,
+ * then repeatedly the unpicked row farthest (fp32) from the picked set, ties to
+ * the lower row, until k_keep rows are picked; write the picked rows in
+ * ascending row order to rows 0..k_keep-1 of q_out and set count_out = k_keep.
+ * Buffers with count_in != cap are copied unchanged (count_out = count_in).
+ * q_out may equal q_in and count_out may equal count_in (in place); partial
+ * overlap is EALIAS.  picks: optional [n_buf, k_keep] int32, the picks in
+ * selection order (-1 for buffers that were not full).
+ * Errors: EINVAL, ESHAPE (cap > 64, 1 <= k_keep <= cap, head_dim, and for fp32
+ * cap*head_dim <= 4096), EALIAS, EDEVICE.
+ */
+kve_status beacon_fps_update(const void* q_in, void* q_out, const int32_t* count_in, int32_t* count_out,
+                             int32_t n_buf, int32_t cap, int32_t k_keep, int32_t head_dim, int32_t dtype,
+                             int32_t* picks, void* stream);
+
+/* Workspace bytes epikv_score needs. */
+size_t epikv_workspace_size(int32_t batch, int32_t T);
+
+/*
+ * epikv_score — EPIKV page (方法论 part 1 顿悟得分 and part 3 时间趋势校正): for the
+ * two monitored layers a and b (bf16 traces [batch, T, d_model]),
+ *   g(t) = ||h(t) - h(t-1)||_2 (t >= 1), g(0) = 0,
+ *   z(t) = (g(t) - mean) / (std + eps) over the causal window
+ *          {max(1, t-window+1) .. t} (population std), z(0) = 0,
+ *   scores[b*T + t] = z_a(t) - z_b(t)   (higher keeps).
+ * g_out: optional [2, batch, T] fp32 (the two g series).  Window sums in double.
+ * d_model is 512, 1024, 2048, 4096 or 8192; the traces and scores are 16-byte aligned.
+ * Errors: EINVAL, ESHAPE (d_model, window < 1 or > 2048), EWORKSPACE, EDEVICE.
+ */
+kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model,
+                       int32_t window, float eps, float* g_out, float* scores,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_rope_apply — write keys into a cache the way a decoder layer does: rotate
+ * fp32 pre-RoPE rows src[n_rows, head_dim] to positions pos[n_rows] (half-split
+ * pairs, angle in double precision, rotation in double) and round to dtype into
+ * dst[n_rows, head_dim].  src and dst must not overlap.
+ * Errors: EINVAL, ESHAPE, EALIAS, EDEVICE.
+ */
+kve_status kv_rope_apply(const float* src, void* dst, const int32_t* pos, int64_t n_rows,
+                         int32_t head_dim, double rope_theta, int32_t dtype, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* kve_last_error(void);
+
+/* KVE_ABI_VERSION of the loaded library. */
+int32_t kve_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVEVICT_H */
