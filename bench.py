@@ -1,0 +1,304 @@
+"""Throughput of the decode-time KV-cache eviction step on one MI355X.
+
+Default workload: Qwen3-4B-shaped cache, 36 layers x batch 16 x 8 KV heads,
+head_dim 128, bf16, B_max = 4096, evicting 1/8 (to 3584) per trigger, with
+continual FPS of every query head's 32-entry beacon buffer down to 16.  Four
+consecutive trigger states are built up front (512 decoded tokens appended
+between triggers); timed steps cycle through them.  One step = one trigger
+over all 36 layers: kv_evict_score -> kv_evict_select_compact ->
+beacon_fps_update, all on one stream, inputs resident in HBM.
+
+Prints ONE JSON line.  Metric: scored KV tokens per second (a token is one
+position of one layer of one request, across its 8 KV heads).
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3-4b-36l")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    return ap.parse_args()
+
+
+class TriggerState:
+    """Inputs of one eviction trigger for all layers, folded into one segmented cache."""
+
+    def __init__(self, w, cap_rows, device):
+        import torch
+        L, B, Hkv, Hq, d = w.n_layers, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+        S = L * B * Hkv
+        self.S, self.cap = S, cap_rows
+        self.k = torch.empty(S * cap_rows, d, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty_like(self.k)
+        self.pos = torch.empty(S * cap_rows, dtype=torch.int32, device=device)
+        self.seg_off = torch.arange(S, dtype=torch.int64, device=device) * cap_rows
+        self.seg_len = torch.empty(S, dtype=torch.int32, device=device)
+        self.q = torch.empty(L * B, Hq, w.n_obs, d, dtype=torch.bfloat16, device=device)
+        self.q_pos = torch.empty(L * B, w.n_obs, dtype=torch.int32, device=device)
+        self.n_obs = torch.full((L * B,), w.n_obs, dtype=torch.int32, device=device)
+        self.buf = torch.empty(L * B * Hq, w.fps_cap, d, dtype=torch.bfloat16, device=device)
+        self.count = torch.full((L * B * Hq,), w.fps_cap, dtype=torch.int32, device=device)
+        self.t = 0
+
+    def view3(self, x):
+        return x.view(self.S, self.cap, *x.shape[1:])
+
+
+def build_states(w, device):
+    """Trigger 0 from the generator; trigger i+1 = trigger i evicted by the library + 512 appended tokens."""
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    from workloads import make_layer, make_append
+    L, B, Hkv, Hq, d, n = w.n_layers, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.len_hi
+    Rq, A = w.n_recent_q, w.append
+    per_layer = B * Hkv * n
+    states = []
+    st = TriggerState(w, n, device)
+    for l in range(L):
+        lay = make_layer(w, l, device=device)
+        rows = slice(l * per_layer, (l + 1) * per_layer)
+        kv.kv_rope_apply(lay["k_pre"], st.k[rows], lay["pos"], w.rope_theta)
+        st.v[rows] = lay["v"]
+        st.pos[rows] = lay["pos"]
+        st.seg_len[l * B * Hkv:(l + 1) * B * Hkv] = lay["seg_len"]
+        st.q[l * B:(l + 1) * B] = lay["q_obs"]
+        st.q_pos[l * B:(l + 1) * B] = lay["q_pos"]
+        st.buf[l * B * Hq:(l + 1) * B * Hq] = lay["fps_buf"]
+        del lay
+    st.t = n
+    states.append(st)
+    torch.cuda.synchronize()
+    log(f"trigger 0 built ({L} layers)")
+    keep = w.budget
+    scores = torch.empty(st.k.shape[0], dtype=torch.float32, device=device)
+    for trig in range(1, w.triggers):
+        prev = states[-1]
+        nxt = TriggerState(w, n, device)
+        run_step(prev, nxt, w, scores, fps_out=(nxt.buf, nxt.count))
+        # nxt now holds the kept rows (seg_len = keep) and the FPS'd buffers (count = 16)
+        t_new = prev.t + A
+        for l in range(L):
+            ap = make_append(w, l, trig, [prev.t] * B, device=device)
+            tmp = torch.empty(B * Hkv * A, d, dtype=torch.bfloat16, device=device)
+            kv.kv_rope_apply(ap["k_pre"].reshape(-1, d).contiguous(), tmp, ap["pos"].reshape(-1).contiguous(),
+                             w.rope_theta)
+            segs = slice(l * B * Hkv, (l + 1) * B * Hkv)
+            nxt.view3(nxt.k)[segs, keep:keep + A] = tmp.view(B * Hkv, A, d)
+            nxt.view3(nxt.v)[segs, keep:keep + A] = ap["v"].reshape(B * Hkv, A, d)
+            nxt.view3(nxt.pos)[segs, keep:keep + A] = ap["pos"].reshape(B * Hkv, A)
+            # recent observation queries: the newest Rq, at t_new - Rq .. t_new - 1
+            nxt.q[l * B:(l + 1) * B, :, :Rq] = ap["q_new"]
+            nxt.q_pos[l * B:(l + 1) * B, :Rq] = torch.arange(t_new - Rq, t_new, dtype=torch.int32, device=device)
+            nxt.q_pos[l * B:(l + 1) * B, Rq:] = t_new
+            # beacon buffer: the FPS survivors (rows 0..15) then the newest queries
+            bl = nxt.buf[l * B * Hq:(l + 1) * B * Hq]
+            bl[:, w.fps_keep:w.fps_keep + Rq] = ap["q_new"].reshape(B * Hq, Rq, d)
+        nxt.seg_len.fill_(keep + A)
+        nxt.count.fill_(w.fps_cap)
+        nxt.q[:, :, Rq:] = nxt.buf.view(L * B, Hq, w.fps_cap, d)
+        nxt.t = t_new
+        states.append(nxt)
+        torch.cuda.synchronize()
+        log(f"trigger {trig} built (t = {t_new})")
+    return states
+
+
+def make_out(w, device):
+    import torch
+    S = w.n_layers * w.batch * w.n_kv_heads
+    cap = w.budget
+    return {
+        "k": torch.empty(S * cap, w.head_dim, dtype=torch.bfloat16, device=device),
+        "v": torch.empty(S * cap, w.head_dim, dtype=torch.bfloat16, device=device),
+        "pos": torch.empty(S * cap, dtype=torch.int32, device=device),
+        "seg_off": torch.arange(S, dtype=torch.int64, device=device) * cap,
+        "seg_len": torch.empty(S, dtype=torch.int32, device=device),
+        "cap": cap,
+    }
+
+
+def run_step(st, out, w, scores, fps_out, ev=None, ws=None):
+    """One trigger over every layer: score -> select/compact -> FPS.  `out` is a
+    TriggerState (its first `budget` rows per segment receive the kept rows) or
+    a dict from make_out()."""
+    import decode_kv_cache_evict_amd as kv
+    if isinstance(out, dict):
+        ok, ov, op, oo, ol, cap = out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], out["cap"]
+    else:
+        ok, ov, op, oo, ol, cap = out.k, out.v, out.pos, out.seg_off, out.seg_len, out.cap
+    cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off, st.seg_len, w.n_kv_heads, st.cap)
+    obs = kv.make_obs(st.q, st.q_pos, st.n_obs, w.rope_theta, bool(w.causal))
+    cout = kv.make_cache(ok, ov, op, oo, ol, w.n_kv_heads, cap)
+    if ev:
+        ev[0].record()
+    kv.kv_evict_score(cache, obs, scores, ws=ws["score"] if ws else None)
+    if ev:
+        ev[1].record()
+    kv.kv_evict_select_compact(cache, scores, None, w.n_prefix, w.n_recent, cout, uniform_budget=w.budget,
+                               ws=ws["select"] if ws else None)
+    if ev:
+        ev[2].record()
+    kv.beacon_fps_update(st.buf, fps_out[0], st.count, fps_out[1], w.fps_keep)
+    if ev:
+        ev[3].record()
+
+
+def step_bytes(w):
+    """Algorithmic HBM bytes of one trigger (every input read once, every output written once)."""
+    S = w.n_layers * w.batch * w.n_kv_heads
+    n, keep, d = w.len_hi, w.budget, w.head_dim
+    row = d * 2
+    b = {
+        "score_k": S * n * row, "score_pos": S * n * 4,
+        "score_q": w.n_layers * w.batch * w.n_q_heads * w.n_obs * d * 2 + w.n_layers * w.batch * w.n_obs * 4,
+        "score_out": S * n * 4,
+        "select_scores": S * n * 4,
+        "compact_kv": 2 * 2 * S * keep * row, "compact_pos": 2 * S * keep * 4,
+        "fps": w.n_layers * w.batch * w.n_q_heads * (w.fps_cap + w.fps_keep) * d * 2,
+    }
+    b["select_compact"] = b["select_scores"] + b["compact_kv"] + b["compact_pos"]
+    b["score"] = b["score_k"] + b["score_pos"] + b["score_q"] + b["score_out"]
+    b["total"] = b["score"] + b["select_compact"] + b["fps"]
+    return b
+
+
+def cpu_baseline(w, target_s):
+    """Time the oracle (as it stands) on a bounded sample of the same workload:
+    requests of layer 0 at trigger 0, one at a time, until target_s is spent."""
+    import numpy as np
+    import torch
+    import oracle
+    from workloads import make_layer
+    from tests.oracle_side import oracle_cache_keys, np64
+    one = w.scaled(batch=1)
+    spent, tokens, reqs = 0.0, 0, 0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    while spent < target_s and reqs < w.batch * w.n_layers:
+        lay = make_layer(one.scaled(seed_base=w.seed_base + 17 * (reqs % w.batch)), reqs // w.batch)
+        k = oracle_cache_keys(lay, one)          # the cache as stored (not timed: it is an input)
+        pos, off, ln = lay["pos"].numpy(), lay["seg_off"].numpy(), lay["seg_len"].numpy()
+        q, qp, no = np64(lay["q_obs"]), lay["q_pos"].numpy(), lay["n_obs"].numpy()
+        v = np64(lay["v"])
+        buf = np64(lay["fps_buf"])
+        t0 = time.perf_counter()
+        sc = oracle.layer_scores(k, pos, off, ln, q, qp, no, one.n_kv_heads, one.rope_theta, one.dtype)
+        for s in range(one.n_kv_heads):
+            o, n = int(off[s]), int(ln[s])
+            kept = oracle.select_kept(sc[o:o + n], n, one.budget, one.n_prefix, one.n_recent)
+            oracle.compact_rows(k[o:o + n], kept)
+            oracle.compact_rows(v[o:o + n], kept)
+            oracle.compact_rows(pos[o:o + n], kept)
+        for p in range(buf.shape[0]):
+            picks = oracle.fps(buf[p], one.fps_keep)
+            oracle.compact_rows(buf[p], np.sort(picks))
+        spent += time.perf_counter() - t0
+        tokens += int(ln[0])
+        reqs += 1
+    return {"value": tokens / spent, "unit": "scored KV tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reqs} (request, layer) pairs x {w.n_kv_heads} KV heads of the same shape "
+                      f"({tokens} tokens, {spent:.1f} s, float64 numpy, {platform.processor() or platform.machine()})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the eviction step is data-parallel over requests and KV heads with no "
+              "communication; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    from workloads import get_workload
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kv.lib()
+    w = get_workload(args.workload)
+    if w.n_layers * w.batch * w.n_kv_heads > 65535 or w.budget == 0:
+        print(f"workload {w.name} is not a bench workload", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    t_setup = time.time()
+    states = build_states(w, dev)
+    out = make_out(w, dev)
+    fps_buf = torch.empty_like(states[0].buf)
+    fps_cnt = torch.empty_like(states[0].count)
+    scores = torch.empty(states[0].k.shape[0], dtype=torch.float32, device=dev)
+    c0 = kv.make_cache(states[0].k, states[0].v, states[0].pos, states[0].seg_off, states[0].seg_len,
+                       w.n_kv_heads, states[0].cap)
+    o0 = kv.make_obs(states[0].q, states[0].q_pos, states[0].n_obs, w.rope_theta)
+    ws = {"score": torch.empty(kv.kv_evict_score_workspace(c0, o0) + 256, dtype=torch.uint8, device=dev),
+          "select": torch.empty(out["k"].shape[0] * 4 + 256, dtype=torch.uint8, device=dev)}
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s; warmup {args.warmup}, timed {args.steps}")
+    for i in range(args.warmup):
+        run_step(states[i % len(states)], out, w, scores, (fps_buf, fps_cnt), ws=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(states[i % len(states)], out, w, scores, (fps_buf, fps_cnt), ev=evs[i], ws=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    part = {"score": 0.0, "select_compact": 0.0, "fps": 0.0}
+    for e in evs:
+        part["score"] += e[0].elapsed_time(e[1])
+        part["select_compact"] += e[1].elapsed_time(e[2])
+        part["fps"] += e[2].elapsed_time(e[3])
+    part = {k: v / args.steps for k, v in part.items()}
+    gpu_ms = sum(part.values())
+    tokens = w.n_layers * w.batch * w.len_hi
+    nb = step_bytes(w)
+    dom = max(part, key=part.get)
+    dom_bytes = nb[dom]
+    achieved = dom_bytes / (part[dom] * 1e-3) / 1e9
+    res = {
+        "metric": "scored KV tokens/sec (+ % HBM peak), Qwen3-4B shape, B_max=4096, batch 16",
+        "value": tokens / (ms * 1e-3),
+        "unit": "scored KV tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded clustered keys/queries; no model weights needed)",
+        "config": {"workload": f"{w.name}: {w.n_layers} layers x batch {w.batch} x {w.n_kv_heads} KV heads, "
+                               f"head_dim {w.head_dim}, {w.len_hi} -> {w.budget} per head, "
+                               f"{w.n_recent_q} recent + {w.n_beacon} beacon queries per q-head, "
+                               f"FPS {w.fps_cap}->{w.fps_keep}, {w.triggers} trigger states",
+                   "global_batch": w.batch, "seq_len": w.len_hi, "parallelism": "single GPU"},
+        "step_hbm": {"algorithmic_bytes": nb["total"], "gb_per_s": nb["total"] / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": nb["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "kernel_ms": part, "gpu_ms_per_step": gpu_ms,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dom_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
