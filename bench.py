@@ -294,6 +294,19 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dom_bytes},
     }
+    # plain device-to-device copy of 2 GiB: the achievable read+write bandwidth reference
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    res["copy_reference"] = {"what": "torch copy_ of 2 GiB, read + write bytes",
+                             "gb_per_s": 2 * src.numel() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9}
+    del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -12,7 +12,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libkvevict.so")
+LIB_PATH = os.environ.get("KVE_LIB") or os.path.join(_HERE, "_lib", "libkvevict.so")
 
 KVE_BF16, KVE_F32 = 0, 1
 STATUS = {0: "KVE_OK", 1: "KVE_EINVAL", 2: "KVE_ESHAPE", 3: "KVE_EALIAS", 4: "KVE_EBUDGET",

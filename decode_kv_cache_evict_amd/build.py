@@ -16,6 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          # packed fp32 instructions stay off in every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in arch VGPRs (no accumulator-register copies in the score loops)
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 

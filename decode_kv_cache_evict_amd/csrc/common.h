@@ -50,16 +50,18 @@ template <> struct Elem<float> {
 // Rotate the pair (a, b) of frequency index i (of head_dim d) to position p:
 // (a cos - b sin, b cos + a sin), angle p * theta^(-2i/d) in double.
 struct RotPair { double a, b; };
-__device__ __forceinline__ RotPair rope_pair(double a, double b, int i, int d, int p, double theta) {
+__device__ __forceinline__ RotPair rotate_pair(double a, double b, double c, double s) {
 #pragma clang fp contract(off)
-  double inv = pow(theta, -2.0 * double(i) / double(d));
-  double ang = double(p) * inv;
-  double s, c;
-  sincos(ang, &s, &c);
   RotPair r;
   r.a = a * c - b * s;
   r.b = b * c + a * s;
   return r;
+}
+__device__ __forceinline__ RotPair rope_pair(double a, double b, int i, int d, int p, double theta) {
+  const double ang = double(p) * pow(theta, -2.0 * double(i) / double(d));
+  double s, c;
+  sincos(ang, &s, &c);
+  return rotate_pair(a, b, c, s);
 }
 
 // ---------------------------------------------------------------- wave reductions

@@ -7,7 +7,8 @@
 
 namespace kve {
 
-constexpr int kScoreChunk = 256;   // keys per score work-group
+constexpr int kScoreChunk = 256;   // keys per work-group, VALU path (one key per thread)
+constexpr int kMfmaChunk = 1024;   // keys per work-group, MFMA path
 constexpr int kMaxObsRows = 256;   // group * max_obs
 
 struct ScoreArgs {
@@ -29,7 +30,9 @@ struct ScoreArgs {
   float* entropy;
   void* qr;               // rotated queries [B, Hq, max_obs, D] (workspace)
   float2* stats;          // [n_seg, n_chunks, rows] (m * log2e/sqrt(D), l) (workspace)
+  float* lse;             // [n_seg, rows] merged row log-sum-exp, log2 units (workspace)
   int32_t n_chunks;
+  int32_t chunk;          // keys per work-group
   int32_t impl;           // 0: MFMA (bf16), 1: plain VALU
 };
 

@@ -46,43 +46,59 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 
 // ------------------------------------------------------------ query rotation
 // Rotate every observation row to its q_pos (double-precision angle and
-// rotation) and round to the storage dtype.  Rows past n_obs are zeroed.
+// rotation) and round to the storage dtype; rows past n_obs are zeroed.  One
+// thread per (request, observation row, frequency): the angle is shared by all
+// query heads, so its sine and cosine are formed once and applied to every head.
 template <typename T>
 __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
                                   const int32_t* __restrict__ n_obs, T* __restrict__ qr,
-                                  int64_t n_pairs, int n_q, int max_obs, int D, double theta) {
+                                  int64_t n_work, int n_q, int max_obs, int D, double theta) {
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= n_pairs) return;
+  if (idx >= n_work) return;
   const int half = D / 2;
   const int i = int(idx % half);
-  const int64_t row = idx / half;                 // (b * n_q + h) * max_obs + o
-  const int o = int(row % max_obs);
-  const int b = int(row / (int64_t(max_obs) * n_q));
+  const int64_t bo = idx / half;                  // b * max_obs + o
+  const int o = int(bo % max_obs);
+  const int b = int(bo / max_obs);
   const int no = n_obs ? n_obs[b] : max_obs;
-  const T* src = q + row * D;
-  T* dst = qr + row * D;
-  if (o >= no) {
-    dst[i] = Elem<T>::from_f64(0.0);
-    dst[i + half] = Elem<T>::from_f64(0.0);
-    return;
+  const bool live = o < no;
+  double s = 0.0, c = 1.0;
+  if (live) {
+    const double ang = double(q_pos[bo]) * pow(theta, -2.0 * double(i) / double(D));
+    sincos(ang, &s, &c);
   }
-  RotPair r = rope_pair(double(Elem<T>::widen(src[i])), double(Elem<T>::widen(src[i + half])), i, D,
-                        q_pos[b * max_obs + o], theta);
-  dst[i] = Elem<T>::from_f64(r.a);
-  dst[i + half] = Elem<T>::from_f64(r.b);
+  for (int h = 0; h < n_q; ++h) {
+    const int64_t row = (int64_t(b) * n_q + h) * max_obs + o;
+    const T* src = q + row * D;
+    T* dst = qr + row * D;
+    if (!live) {
+      dst[i] = Elem<T>::from_f64(0.0);
+      dst[i + half] = Elem<T>::from_f64(0.0);
+      continue;
+    }
+    RotPair r = rotate_pair(double(Elem<T>::widen(src[i])), double(Elem<T>::widen(src[i + half])), c, s);
+    dst[i] = Elem<T>::from_f64(r.a);
+    dst[i + half] = Elem<T>::from_f64(r.b);
+  }
 }
 
-// Merge a row's chunk statistics into its log-sum-exp (log2 units);
-// +inf when the row saw no key.
-__device__ __forceinline__ float merge_row(const float2* st, int nch, int rows) {
+// Merge each row's chunk statistics into its log-sum-exp (log2 units); +inf
+// when the row saw no key.  One thread per (segment, row).
+__global__ __launch_bounds__(256) void merge_lse_kernel(ScoreArgs a) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(a.n_seg) * a.rows) return;
+  const int s = int(idx / a.rows), r = int(idx % a.rows);
+  const int n = a.seg_len[s];
+  const int nch = (n >= 0 && n <= a.max_seg_len) ? (n + a.chunk - 1) / a.chunk : 0;
+  const float2* st = a.stats + int64_t(s) * a.n_chunks * a.rows + r;
   float M = kNegBig;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[int64_t(c) * rows].x);
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[int64_t(c) * a.rows].x);
   float L = 0.f;
   for (int c = 0; c < nch; ++c) {
-    const float2 v = st[int64_t(c) * rows];
+    const float2 v = st[int64_t(c) * a.rows];
     L += v.y * exp2f(v.x - M);
   }
-  return L > 0.f ? M + log2f(L) : kInf;
+  a.lse[idx] = L > 0.f ? M + log2f(L) : kInf;
 }
 
 // ------------------------------------------------------------ VALU path
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) return;
-  const int k0 = ch * kScoreChunk;
+  const int k0 = ch * a.chunk;
   if (k0 >= n) return;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -112,10 +128,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
   }
   for (int r = tid; r < a.rows; r += blockDim.x) {
     rp_s[r] = row_position(a, b, r);
-    if (PASS2) {
-      const int nch = (n + kScoreChunk - 1) / kScoreChunk;
-      lse_s[r] = merge_row(a.stats + int64_t(s) * a.n_chunks * a.rows + r, nch, a.rows);
-    }
+    if (PASS2) lse_s[r] = a.lse[int64_t(s) * a.rows + r];
   }
   __syncthreads();
 
@@ -170,6 +183,19 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
 // v_mfma_f32_16x16x32_bf16 lane l holds A row l%16 / B column l%16 with
 // k-slice 8*(l/16)..+7 of each 32-wide step, and result rows 4*(l/16)+i of
 // column l%16.
+//
+// Pass 1 keeps, per lane and row, a reference value m and l = sum of
+// exp2(c*x - c*m) over the keys it has seen.  m is only moved when a batch's
+// sum leaves [0, 2^64] (a term overflowed or grew far above the reference):
+// the batch is then redone with m raised to the running maximum.  The first
+// batch always takes that path (m starts at -1e30), later ones almost never,
+// so the common case costs one fma, one exp and one add per logit.  The causal
+// mask is applied only to batches holding a key newer than the wave's earliest
+// query position.
+constexpr float kBig = 18446744073709551616.0f;   // 2^64
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int D, int RT, bool PASS2>
 __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   constexpr int KS = D / 32;                 // MFMA k-steps
@@ -186,9 +212,9 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) return;
-  const int k0 = ch * kScoreChunk;
+  const int k0 = ch * kMfmaChunk;
   if (k0 >= n) return;
-  const int k1 = min(n, k0 + kScoreChunk);
+  const int k1 = min(n, k0 + kMfmaChunk);
   const int b = s / a.n_kv, g = s % a.n_kv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -196,21 +222,19 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* qr = static_cast<const uint16_t*>(a.qr);
 
-  if (PASS2) {
-    const int nch = (n + kScoreChunk - 1) / kScoreChunk;
-    for (int r = tid; r < a.rows; r += 256)
-      lse_s[r] = merge_row(a.stats + int64_t(s) * a.n_chunks * a.rows + r, nch, a.rows);
-  }
+  if (PASS2)
+    for (int r = tid; r < a.rows; r += 256) lse_s[r] = a.lse[int64_t(s) * a.rows + r];
 
   // A operands and per-result-row state.
   bf16x8 qa[RT][KS];
   int rowpos[RT][4];
-  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse
+  float st0[RT][4], st1[RT][4];   // pass 1: (m, l) in raw logit units; pass 2: st0 = c*lse
+  int minpos = INT_MAX;           // earliest position among this wave's live rows
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int t = w * RT + rt;
     const int ra = 16 * t + col;
-    const bool ok = ra < a.rows && row_position(a, b, ra) >= 0;
+    const bool ok = row_position(a, b, ra) >= 0;
     const uint16_t* src = qr + (ok ? row_qr_index(a, b, g, ra) : 0) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -219,21 +243,27 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rowpos[rt][i] = row_position(a, b, 16 * t + 4 * quad + i);
+      const int rp = row_position(a, b, 16 * t + 4 * quad + i);
+      rowpos[rt][i] = rp;
+      if (rp >= 0) minpos = min(minpos, rp);
       st0[rt][i] = kNegBig;
       st1[rt][i] = 0.f;
     }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) minpos = min(minpos, __shfl_xor(minpos, o, kWave));
 
   uint4 pre[CPT];
   int prepos = INT_MAX;
   auto load_batch = [&](int kb) {
+    const bool full = kb + BK <= k1;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = tid + 256 * u;
       const int key = cidx / CPR, part = cidx % CPR;
       const int j = kb + key;
-      pre[u] = j < k1 ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8) : make_uint4(0, 0, 0, 0);
+      pre[u] = (full || j < k1) ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8)
+                                : make_uint4(0, 0, 0, 0);
     }
     if (tid < BK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
   };
@@ -256,7 +286,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * (w * RT + rt) + 4 * quad + i;
-        st0[rt][i] = r < a.rows ? lse_s[r] : kInf;
+        st0[rt][i] = (rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
       }
   }
 
@@ -284,24 +314,50 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
     int kpos[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[buf][q4 * 16 + col];
+    const bool late = kpos[0] > minpos || kpos[1] > minpos || kpos[2] > minpos || kpos[3] > minpos;
+    if (__any(late)) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kpos[q4] > rowpos[rt][i]) acc[q4][rt][i] = -kInf;
+    }
 
     if (!PASS2) {
+      float lsum[RT][4];
+      bool redo = false;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v[4];
+          const float mc = st0[rt][i] * c;
+          float l = st1[rt][i];
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) v[q4] = kpos[q4] <= rowpos[rt][i] ? acc[q4][rt][i] : -kInf;
-          const float mo = st0[rt][i];
-          const float mx = fmaxf(fmaxf(mo, fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
-          const float mc = mx * c;
-          float l = st1[rt][i] * exp2f(fmaf(mo, c, -mc));
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) l += exp2f(fmaf(v[q4], c, -mc));
-          st0[rt][i] = mx;
-          st1[rt][i] = l;
+          for (int q4 = 0; q4 < 4; ++q4) l += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+          lsum[rt][i] = l;
+          redo |= !(l <= kBig);
         }
+      if (__any(redo)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float bm = fmaxf(fmaxf(acc[0][rt][i], acc[1][rt][i]), fmaxf(acc[2][rt][i], acc[3][rt][i]));
+            const float mn = fmaxf(st0[rt][i], bm);
+            const float mc = mn * c;
+            float l = st1[rt][i] * fast_exp2((st0[rt][i] - mn) * c);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) l += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+            st0[rt][i] = mn;
+            lsum[rt][i] = l;
+          }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st1[rt][i] = lsum[rt][i];
     } else {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -309,10 +365,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float y = kpos[q4] <= rowpos[rt][i] ? fmaf(acc[q4][rt][i], c, -st0[rt][i]) : -kInf;
-            best = fmaxf(best, y);
-          }
+          for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[q4][rt][i], c, -st0[rt][i]));
         best = fmaxf(best, __shfl_xor(best, 16, kWave));
         best = fmaxf(best, __shfl_xor(best, 32, kWave));
         if (quad == 0) red[w][q4 * 16 + col] = best;
@@ -324,7 +377,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
       const int j = kb + tid;
       if (j < k1) {
         const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-        a.scores[off + j] = exp2f(m);
+        a.scores[off + j] = fast_exp2(m);
       }
     }
     __syncthreads();
@@ -383,9 +436,15 @@ __global__ __launch_bounds__(256) void entropy_kernel(ScoreArgs a) {
   }
 }
 
+void launch_merge(const ScoreArgs& a, hipStream_t st) {
+  const int64_t n = int64_t(a.n_seg) * a.rows;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a);
+}
+
 template <int D, int RT>
 hipError_t launch_mfma(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((score_mfma_kernel<D, RT, false>), grid, dim3(256), 0, st, a);
+  launch_merge(a, st);
   hipLaunchKernelGGL((score_mfma_kernel<D, RT, true>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -406,6 +465,7 @@ template <typename T, int D>
 hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const size_t sh = size_t(a.rows) * D * sizeof(T) + size_t(a.rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
   hipLaunchKernelGGL((score_valu_kernel<T, D, false>), grid, dim3(256), sh, st, a);
+  launch_merge(a, st);
   hipLaunchKernelGGL((score_valu_kernel<T, D, true>), grid, dim3(256), sh, st, a);
   return hipGetLastError();
 }
@@ -420,7 +480,8 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t qr = align_up(size_t(batch) * n_q * max_obs * head_dim * elem);
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
-  return qr + st;
+  const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
+  return qr + st + ls;
 }
 
 size_t valu_lds_bytes(int rows, int D, int dtype) {
@@ -430,26 +491,32 @@ size_t valu_lds_bytes(int rows, int D, int dtype) {
 hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const int batch = a.n_seg / a.n_kv;
   const size_t elem = a.dtype == 0 ? 2 : 4;
-  a.qr = ws;
-  a.stats = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                      align_up(size_t(batch) * a.n_q * a.max_obs * a.head_dim * elem));
-  a.n_chunks = (a.max_seg_len + kScoreChunk - 1) / kScoreChunk;
-  const int64_t n_pairs = int64_t(batch) * a.n_q * a.max_obs * (a.head_dim / 2);
-  const dim3 rg(unsigned((n_pairs + 255) / 256));
-  if (n_pairs > 0) {
+  const bool mfma = a.dtype == 0 && a.impl == 0;
+  a.chunk = mfma ? kMfmaChunk : kScoreChunk;
+  a.n_chunks = (a.max_seg_len + a.chunk - 1) / a.chunk;
+  const size_t nch256 = (size_t(a.max_seg_len) + kScoreChunk - 1) / kScoreChunk;
+  char* w = static_cast<char*>(ws);
+  a.qr = w;
+  w += align_up(size_t(batch) * a.n_q * a.max_obs * a.head_dim * elem);
+  a.stats = reinterpret_cast<float2*>(w);
+  w += align_up(size_t(a.n_seg) * (nch256 ? nch256 : 1) * a.rows * sizeof(float2));
+  a.lse = reinterpret_cast<float*>(w);
+  const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2);
+  const dim3 rg(unsigned((n_work + 255) / 256));
+  if (n_work > 0) {
     if (a.dtype == 0)
       hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
-                         a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_pairs, a.n_q, a.max_obs, a.head_dim,
+                         a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim,
                          a.theta);
     else
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
-                         a.n_obs, static_cast<float*>(a.qr), n_pairs, a.n_q, a.max_obs, a.head_dim, a.theta);
+                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, a.theta);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
-  if (a.dtype == 0 && a.impl == 0) {
+  if (mfma) {
     e = a.head_dim == 128 ? launch_mfma_rt<128>(a, grid, st) : launch_mfma_rt<64>(a, grid, st);
   } else if (a.dtype == 0) {
     e = a.head_dim == 128 ? launch_valu<uint16_t, 128>(a, grid, st) : launch_valu<uint16_t, 64>(a, grid, st);

@@ -144,52 +144,71 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
   if (tid == 0) a.out_len[s] = K;
 }
 
-// Gather kept rows.  RB = row bytes; CPR 16-byte chunks per row; each thread
-// moves UNR rows of K and V per tile.
+// Gather kept rows.  CPR 16-byte chunks per row; each thread moves UNR rows of
+// K and V per pass (all loads issued before the stores), and a work-group
+// covers PASSES passes.  Loads and stores are non-temporal: every byte is
+// touched exactly once.
+#ifndef KVE_COMPACT_UNR
+#define KVE_COMPACT_UNR 4
+#endif
+#ifndef KVE_COMPACT_PASSES
+#define KVE_COMPACT_PASSES 2
+#endif
+constexpr int kCompactUnr = KVE_COMPACT_UNR;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCompactPasses = KVE_COMPACT_PASSES;
+
 template <int CPR>
 __global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
-  constexpr int RPP = 256 / CPR;            // rows per pass
-  constexpr int UNR = 4;
-  constexpr int RPW = RPP * UNR;            // rows per work-group
+  constexpr int RPP = 256 / CPR;            // rows per sub-pass
+  constexpr int UNR = kCompactUnr;
+  constexpr int RPW = RPP * UNR * kCompactPasses;
   const int s = blockIdx.y;
   const int out_n = a.out_len[s];
-  const int r0 = blockIdx.x * RPW;
-  if (out_n <= 0 || out_n > a.out_cap || r0 >= out_n) return;
+  const int rw = blockIdx.x * RPW;
+  if (out_n <= 0 || out_n > a.out_cap || rw >= out_n) return;
   const int64_t io = a.in_off[s], oo = a.out_off[s];
   const int n_in = a.in_len[s];
   const int part = threadIdx.x % CPR;
   const int rsub = threadIdx.x / CPR;
-  const uint4* kin = static_cast<const uint4*>(a.k_in);
-  const uint4* vin = static_cast<const uint4*>(a.v_in);
-  uint4* kout = static_cast<uint4*>(a.k_out);
-  uint4* vout = static_cast<uint4*>(a.v_out);
-  uint4 kb[UNR], vb[UNR];
-  int src[UNR];
+  const u32x4* kin = static_cast<const u32x4*>(a.k_in);
+  const u32x4* vin = static_cast<const u32x4*>(a.v_in);
+  u32x4* kout = static_cast<u32x4*>(a.k_out);
+  u32x4* vout = static_cast<u32x4*>(a.v_out);
+  for (int p = 0; p < kCompactPasses; ++p) {
+    const int r0 = rw + p * RPP * UNR;
+    if (r0 >= out_n) break;
+    u32x4 kb[UNR], vb[UNR];
+    int src[UNR];
 #pragma unroll
-  for (int u = 0; u < UNR; ++u) {
-    const int r = r0 + u * RPP + rsub;
-    int j = r < out_n ? a.kept[oo + r] : -1;
-    if (j >= n_in) j = -1;
-    src[u] = j;
-    if (j >= 0) {
-      kb[u] = kin[(io + j) * CPR + part];
-      vb[u] = vin[(io + j) * CPR + part];
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * RPP + rsub;
+      int j = r < out_n ? a.kept[oo + r] : -1;
+      if (j >= n_in) j = -1;
+      src[u] = j;
     }
-  }
 #pragma unroll
-  for (int u = 0; u < UNR; ++u) {
-    const int r = r0 + u * RPP + rsub;
-    if (src[u] >= 0) {
-      kout[(oo + r) * CPR + part] = kb[u];
-      vout[(oo + r) * CPR + part] = vb[u];
-      if (part == 0) a.pos_out[oo + r] = a.pos_in[io + src[u]];
+    for (int u = 0; u < UNR; ++u) {
+      if (src[u] >= 0) {
+        kb[u] = __builtin_nontemporal_load(&kin[(io + src[u]) * CPR + part]);
+        vb[u] = __builtin_nontemporal_load(&vin[(io + src[u]) * CPR + part]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * RPP + rsub;
+      if (src[u] >= 0) {
+        __builtin_nontemporal_store(kb[u], &kout[(oo + r) * CPR + part]);
+        __builtin_nontemporal_store(vb[u], &vout[(oo + r) * CPR + part]);
+        if (part == 0) a.pos_out[oo + r] = a.pos_in[io + src[u]];
+      }
     }
   }
 }
 
 template <int CPR>
 hipError_t launch_compact(const SelectArgs& a, hipStream_t st) {
-  constexpr int RPW = (256 / CPR) * 4;
+  constexpr int RPW = (256 / CPR) * kCompactUnr * kCompactPasses;
   const dim3 grid(unsigned((a.out_cap + RPW - 1) / RPW), unsigned(a.n_seg));
   hipLaunchKernelGGL(compact_kernel<CPR>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
