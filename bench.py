@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-4b-36l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["serial", "pipelined"], default="pipelined")
+    ap.add_argument("--score-group", type=int, default=1, help="layers per scoring call (0 = all)")
+    ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
+    ap.add_argument("--graph", type=int, default=1, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     return ap.parse_args()
 
@@ -137,9 +141,9 @@ def make_out(w, device):
 
 
 def run_step(st, out, w, scores, fps_out, ev=None, ws=None):
-    """One trigger over every layer: score -> select/compact -> FPS.  `out` is a
-    TriggerState (its first `budget` rows per segment receive the kept rows) or
-    a dict from make_out()."""
+    """One trigger over every layer, all three calls batched over the 36 layers
+    (used to build the trigger chain).  `out` is a TriggerState (its first
+    `budget` rows per segment receive the kept rows) or a dict from make_out()."""
     import decode_kv_cache_evict_amd as kv
     if isinstance(out, dict):
         ok, ov, op, oo, ol, cap = out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], out["cap"]
@@ -148,18 +152,84 @@ def run_step(st, out, w, scores, fps_out, ev=None, ws=None):
     cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off, st.seg_len, w.n_kv_heads, st.cap)
     obs = kv.make_obs(st.q, st.q_pos, st.n_obs, w.rope_theta, bool(w.causal))
     cout = kv.make_cache(ok, ov, op, oo, ol, w.n_kv_heads, cap)
-    if ev:
-        ev[0].record()
     kv.kv_evict_score(cache, obs, scores, ws=ws["score"] if ws else None)
-    if ev:
-        ev[1].record()
     kv.kv_evict_select_compact(cache, scores, None, w.n_prefix, w.n_recent, cout, uniform_budget=w.budget,
                                ws=ws["select"] if ws else None)
-    if ev:
-        ev[2].record()
     kv.beacon_fps_update(st.buf, fps_out[0], st.count, fps_out[1], w.fps_keep)
-    if ev:
-        ev[3].record()
+
+
+class StepRunner:
+    """Runs one trigger as calls over groups of layers.
+
+    Scoring goes `score_group` layers per call (one layer keeps the second
+    pass's re-read of K inside the 256 MB MALL); selection + compaction goes
+    `select_group` layers per call (large grids for the one-work-group-per-
+    segment radix select).
+    serial:    everything on the current stream.
+    pipelined: select_compact(j) on a second stream as soon as the layers it
+               covers are scored, and FPS on that stream up front, so the
+               memory-bound gather overlaps the MFMA-bound scoring."""
+
+    def __init__(self, w, states, out, scores, kept, fps_out, ws_score, score_group, select_group, schedule):
+        import torch
+        import decode_kv_cache_evict_amd as kv
+        self.w, self.states, self.scores, self.kept, self.fps_out = w, states, scores, kept, fps_out
+        self.ws_score, self.schedule = ws_score, schedule
+        L, B, Hkv = w.n_layers, w.batch, w.n_kv_heads
+        select_group = max(select_group, score_group)
+        self.sgroups = [(g0, min(L, g0 + score_group)) for g0 in range(0, L, score_group)]
+        self.cgroups = [(g0, min(L, g0 + select_group)) for g0 in range(0, L, select_group)]
+        self.side = torch.cuda.Stream()
+        self.ev = [torch.cuda.Event() for _ in self.cgroups]
+        self.calls = []
+        for st in states:
+            sc, cc = [], []
+            for (l0, l1) in self.sgroups:
+                segs = slice(l0 * B * Hkv, l1 * B * Hkv)
+                cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off[segs], st.seg_len[segs], Hkv, st.cap)
+                obs = kv.make_obs(st.q[l0 * B:l1 * B], st.q_pos[l0 * B:l1 * B], st.n_obs[l0 * B:l1 * B],
+                                  w.rope_theta, bool(w.causal))
+                sc.append((l1, cache, obs))
+            for (l0, l1) in self.cgroups:
+                segs = slice(l0 * B * Hkv, l1 * B * Hkv)
+                cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off[segs], st.seg_len[segs], Hkv, st.cap)
+                cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"][segs], out["seg_len"][segs],
+                                     Hkv, out["cap"])
+                cc.append((l1, cache, cout))
+            self.calls.append((sc, cc))
+
+    def run(self, i, timing=None):
+        import torch
+        import decode_kv_cache_evict_amd as kv
+        w = self.w
+        st = self.states[i % len(self.states)]
+        sc, cc = self.calls[i % len(self.states)]
+        main = torch.cuda.current_stream()
+        side = self.side if self.schedule == "pipelined" else main
+        if side is not main:
+            side.wait_stream(main)
+        kv.beacon_fps_update(st.buf, self.fps_out[0], st.count, self.fps_out[1], w.fps_keep, stream=side)
+        ci = 0
+
+        def select(ci):
+            l1, cache, cout = cc[ci]
+            if side is not main:
+                self.ev[ci].record(main)
+                side.wait_event(self.ev[ci])
+            if timing is not None:
+                timing[ci][0].record(side)
+            kv.kv_evict_select_compact(cache, self.scores, None, w.n_prefix, w.n_recent, cout,
+                                       kept_idx=self.kept, uniform_budget=w.budget, stream=side)
+            if timing is not None:
+                timing[ci][1].record(side)
+
+        for l1, cache, obs in sc:
+            kv.kv_evict_score(cache, obs, self.scores, ws=self.ws_score, stream=main)
+            while ci < len(cc) and cc[ci][0] <= l1:
+                select(ci)
+                ci += 1
+        if side is not main:
+            main.wait_stream(side)
 
 
 def step_bytes(w):
@@ -246,35 +316,55 @@ def main():
     fps_buf = torch.empty_like(states[0].buf)
     fps_cnt = torch.empty_like(states[0].count)
     scores = torch.empty(states[0].k.shape[0], dtype=torch.float32, device=dev)
-    c0 = kv.make_cache(states[0].k, states[0].v, states[0].pos, states[0].seg_off, states[0].seg_len,
-                       w.n_kv_heads, states[0].cap)
-    o0 = kv.make_obs(states[0].q, states[0].q_pos, states[0].n_obs, w.rope_theta)
-    ws = {"score": torch.empty(kv.kv_evict_score_workspace(c0, o0) + 256, dtype=torch.uint8, device=dev),
-          "select": torch.empty(out["k"].shape[0] * 4 + 256, dtype=torch.uint8, device=dev)}
+    per_group = w.n_layers if args.score_group <= 0 else args.score_group
+    sel_group = w.n_layers if args.select_group <= 0 else args.select_group
+    c0 = kv.make_cache(states[0].k, states[0].v, states[0].pos, states[0].seg_off[:per_group * w.batch * w.n_kv_heads],
+                       states[0].seg_len[:per_group * w.batch * w.n_kv_heads], w.n_kv_heads, states[0].cap)
+    o0 = kv.make_obs(states[0].q[:per_group * w.batch], states[0].q_pos[:per_group * w.batch],
+                     states[0].n_obs[:per_group * w.batch], w.rope_theta)
+    ws_score = torch.empty(kv.kv_evict_score_workspace(c0, o0) + 256, dtype=torch.uint8, device=dev)
+    kept = torch.empty(out["k"].shape[0], dtype=torch.int32, device=dev)
+    runner = StepRunner(w, states, out, scores, kept, (fps_buf, fps_cnt), ws_score, per_group, sel_group,
+                        args.schedule)
     torch.cuda.synchronize()
-    log(f"setup {time.time() - t_setup:.1f} s; warmup {args.warmup}, timed {args.steps}")
+    log(f"setup {time.time() - t_setup:.1f} s; schedule {args.schedule}, {len(runner.sgroups)} scoring and "
+        f"{len(runner.cgroups)} select call(s), "
+        f"graph {args.graph}; warmup {args.warmup}, timed {args.steps}")
     for i in range(args.warmup):
-        run_step(states[i % len(states)], out, w, scores, (fps_buf, fps_cnt), ws=ws)
+        runner.run(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(len(states)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                runner.run(i)
+            graphs.append(gr)
+        for i in range(args.warmup):
+            graphs[i % len(states)].replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(states[i % len(states)], out, w, scores, (fps_buf, fps_cnt), ev=evs[i], ws=ws)
+        if graphs:
+            graphs[i % len(states)].replay()
+        else:
+            runner.run(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
-    part = {"score": 0.0, "select_compact": 0.0, "fps": 0.0}
-    for e in evs:
-        part["score"] += e[0].elapsed_time(e[1])
-        part["select_compact"] += e[1].elapsed_time(e[2])
-        part["fps"] += e[2].elapsed_time(e[3])
-    part = {k: v / args.steps for k, v in part.items()}
-    gpu_ms = sum(part.values())
+    # per-call durations of the dominant call (select + gather), live, same schedule, eager launches
+    timing_steps = min(args.steps, 8)
+    tev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runner.cgroups] for _ in range(timing_steps)]
+    for i in range(timing_steps):
+        runner.run(i, timing=tev[i])
+    torch.cuda.synchronize()
+    sc_ms = sum(t[0].elapsed_time(t[1]) for step in tev for t in step) / (timing_steps * len(runner.cgroups))
     tokens = w.n_layers * w.batch * w.len_hi
     nb = step_bytes(w)
-    dom = max(part, key=part.get)
-    dom_bytes = nb[dom]
-    achieved = dom_bytes / (part[dom] * 1e-3) / 1e9
+    dom_layers = runner.cgroups[0][1] - runner.cgroups[0][0]
+    dom_bytes = nb["select_compact"] * dom_layers / w.n_layers
+    achieved = dom_bytes / (sc_ms * 1e-3) / 1e9
     res = {
         "metric": "scored KV tokens/sec (+ % HBM peak), Qwen3-4B shape, B_max=4096, batch 16",
         "value": tokens / (ms * 1e-3),
@@ -290,9 +380,13 @@ def main():
                    "global_batch": w.batch, "seq_len": w.len_hi, "parallelism": "single GPU"},
         "step_hbm": {"algorithmic_bytes": nb["total"], "gb_per_s": nb["total"] / (ms * 1e-3) / 1e9,
                      "frac_of_peak": nb["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "kernel_ms": part, "gpu_ms_per_step": gpu_ms,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dom_bytes},
+        "schedule": {"kind": args.schedule, "layers_per_score_call": per_group, "layers_per_select_call": sel_group,
+                     "hip_graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "kernel": "kv_evict_select_compact (radix select + gather compaction), "
+                                               f"{dom_layers} layer(s) per launch",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": sc_ms},
     }
     # plain device-to-device copy of 2 GiB: the achievable read+write bandwidth reference
     src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)

@@ -176,10 +176,9 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------ MFMA path (bf16)
-// Work-group = 4 waves over one (segment, 256-key chunk).  Wave w owns row
-// tiles w*RT .. w*RT+RT-1 (16 rows each) and keeps their rotated queries in
-// registers as MFMA A operands.  Keys stream through a double-buffered LDS
-// tile of 64 keys; each wave reads them as B operands.  For
+// Work-groups of 4 waves.  Wave w owns row tiles w*RT .. w*RT+RT-1 (16 rows
+// each) and keeps their rotated queries in registers as MFMA A operands; keys
+// sit in LDS in 64-key batches that every wave reads as B operands.  For
 // v_mfma_f32_16x16x32_bf16 lane l holds A row l%16 / B column l%16 with
 // k-slice 8*(l/16)..+7 of each 32-wide step, and result rows 4*(l/16)+i of
 // column l%16.
@@ -193,19 +192,165 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
 // mask is applied only to batches holding a key newer than the wave's earliest
 // query position.
 constexpr float kBig = 18446744073709551616.0f;   // 2^64
+constexpr int kBK = 64;                           // keys per LDS batch
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int D, int RT>
+struct WaveRows {
+  static constexpr int KS = D / 32;
+  bf16x8 qa[RT][KS];
+  int rowpos[RT][4];
+  int minpos;
+
+  __device__ __forceinline__ void load(const ScoreArgs& a, int b, int g, int w, int col, int quad) {
+    const uint16_t* qr = static_cast<const uint16_t*>(a.qr);
+    minpos = INT_MAX;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int t = w * RT + rt;
+      const int ra = 16 * t + col;
+      const bool ok = row_position(a, b, ra) >= 0;
+      const uint16_t* src = qr + (ok ? row_qr_index(a, b, g, ra) : 0) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = ok ? *reinterpret_cast<const uint4*>(src + ks * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
+        qa[rt][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rp = row_position(a, b, 16 * t + 4 * quad + i);
+        rowpos[rt][i] = rp;
+        if (rp >= 0) minpos = min(minpos, rp);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) minpos = min(minpos, __shfl_xor(minpos, o, kWave));
+  }
+
+  // Logits of the 64 keys of one LDS batch (row stride LS): acc[q4][rt] holds
+  // rows 16*(w*RT+rt) + 4*quad + i against key q4*16 + col; masked entries -inf.
+  template <int LS>
+  __device__ __forceinline__ void logits(f32x4 (&acc)[4][RT], const uint16_t* kb, const int* kp, int col,
+                                         int quad) const {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x8 bfr[KS];
+      const uint16_t* krow = kb + (q4 * 16 + col) * LS + quad * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], bfr[ks], x, 0, 0, 0);
+        acc[q4][rt] = x;
+      }
+    }
+    int kpos[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kp[q4 * 16 + col];
+    const bool late = kpos[0] > minpos || kpos[1] > minpos || kpos[2] > minpos || kpos[3] > minpos;
+    if (__any(late)) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kpos[q4] > rowpos[rt][i]) acc[q4][rt][i] = -kInf;
+    }
+  }
+};
+
+// Pass-1 update of (m, l) with one batch of logits.
+template <int RT>
+__device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[4][RT],
+                                             float c) {
+  float lsum[RT][4];
+  bool redo = false;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mc = m[rt][i] * c;
+      float v = l[rt][i];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) v += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+      lsum[rt][i] = v;
+      redo |= !(v <= kBig);
+    }
+  if (__any(redo)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bm = fmaxf(fmaxf(acc[0][rt][i], acc[1][rt][i]), fmaxf(acc[2][rt][i], acc[3][rt][i]));
+        const float mn = fmaxf(m[rt][i], bm);
+        const float mc = mn * c;
+        float v = l[rt][i] * fast_exp2((m[rt][i] - mn) * c);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) v += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+        m[rt][i] = mn;
+        lsum[rt][i] = v;
+      }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[rt][i] = lsum[rt][i];
+}
+
+// Combine the 16 key columns of each lane group and publish one (c*m, l) per row.
+template <int RT>
+__device__ __forceinline__ void stats_publish(const ScoreArgs& a, float (&m)[RT][4], float (&l)[RT][4], int s, int ch,
+                                              int w, int col, int quad, float c) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mm = m[rt][i], ll = l[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
+        const float M = fmaxf(mm, m2);
+        ll = ll * exp2f((mm - M) * c) + l2 * exp2f((m2 - M) * c);
+        mm = M;
+      }
+      const int r = 16 * (w * RT + rt) + 4 * quad + i;
+      if (col == 0 && r < a.rows) a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(mm * c, ll);
+    }
+}
+
+// Pass-2: per key of the batch, the max over this wave's rows of c*x - lse,
+// combined over the 4 lane groups; written to red[w][key].
+template <int RT>
+__device__ __forceinline__ void key_max(const f32x4 (&acc)[4][RT], const float (&lse)[RT][4], float c,
+                                        float* redw, int col, int quad) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float best = -kInf;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[q4][rt][i], c, -lse[rt][i]));
+    best = fmaxf(best, __shfl_xor(best, 16, kWave));
+    best = fmaxf(best, __shfl_xor(best, 32, kWave));
+    if (quad == 0) redw[q4 * 16 + col] = best;
+  }
+}
+
+// Two-pass variant: pass 1 and pass 2 are separate launches over
+// (1024-key chunk, segment) work-groups; pass 2 re-reads K.
 template <int D, int RT, bool PASS2>
 __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
-  constexpr int KS = D / 32;                 // MFMA k-steps
-  constexpr int BK = 64;                     // keys per LDS batch
   constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int CPT = BK * CPR / 256;        // chunks per thread per batch
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][BK * LS];
-  __shared__ int kps[2][BK];
-  __shared__ float red[4][BK];
+  constexpr int CPT = kBK * CPR / 256;       // chunks per thread per batch
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kBK * LS];
+  __shared__ int kps[2][kBK];
+  __shared__ float red[4][kBK];
   __shared__ float lse_s[kMaxObsRows];
 
   const int s = blockIdx.y, ch = blockIdx.x;
@@ -220,43 +365,24 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   const int col = lane & 15, quad = lane >> 4;
   const float c = kLog2e / sqrtf(float(D));
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* qr = static_cast<const uint16_t*>(a.qr);
 
   if (PASS2)
     for (int r = tid; r < a.rows; r += 256) lse_s[r] = a.lse[int64_t(s) * a.rows + r];
-
-  // A operands and per-result-row state.
-  bf16x8 qa[RT][KS];
-  int rowpos[RT][4];
-  float st0[RT][4], st1[RT][4];   // pass 1: (m, l) in raw logit units; pass 2: st0 = c*lse
-  int minpos = INT_MAX;           // earliest position among this wave's live rows
+  WaveRows<D, RT> rows;
+  rows.load(a, b, g, w, col, quad);
+  float st0[RT][4], st1[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int t = w * RT + rt;
-    const int ra = 16 * t + col;
-    const bool ok = row_position(a, b, ra) >= 0;
-    const uint16_t* src = qr + (ok ? row_qr_index(a, b, g, ra) : 0) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = ok ? *reinterpret_cast<const uint4*>(src + ks * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
-      qa[rt][ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rp = row_position(a, b, 16 * t + 4 * quad + i);
-      rowpos[rt][i] = rp;
-      if (rp >= 0) minpos = min(minpos, rp);
       st0[rt][i] = kNegBig;
       st1[rt][i] = 0.f;
     }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) minpos = min(minpos, __shfl_xor(minpos, o, kWave));
 
   uint4 pre[CPT];
   int prepos = INT_MAX;
   auto load_batch = [&](int kb) {
-    const bool full = kb + BK <= k1;
+    const bool full = kb + kBK <= k1;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = tid + 256 * u;
@@ -265,7 +391,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
       pre[u] = (full || j < k1) ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8)
                                 : make_uint4(0, 0, 0, 0);
     }
-    if (tid < BK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
+    if (tid < kBK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
   };
   auto store_batch = [&](int buf) {
 #pragma unroll
@@ -274,7 +400,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
       const int key = cidx / CPR, part = cidx % CPR;
       *reinterpret_cast<uint4*>(&kt[buf][key * LS + part * 8]) = pre[u];
     }
-    if (tid < BK) kps[buf][tid] = prepos;
+    if (tid < kBK) kps[buf][tid] = prepos;
   };
 
   load_batch(k0);
@@ -286,94 +412,21 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * (w * RT + rt) + 4 * quad + i;
-        st0[rt][i] = (rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
+        st0[rt][i] = (rows.rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
       }
   }
 
   int buf = 0;
-  for (int kb = k0; kb < k1; kb += BK) {
-    const bool has_next = kb + BK < k1;
-    if (has_next) load_batch(kb + BK);
-
+  for (int kb = k0; kb < k1; kb += kBK) {
+    const bool has_next = kb + kBK < k1;
+    if (has_next) load_batch(kb + kBK);
     f32x4 acc[4][RT];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x8 bfr[KS];
-      const uint16_t* krow = &kt[buf][(q4 * 16 + col) * LS + quad * 8];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], bfr[ks], x, 0, 0, 0);
-        acc[q4][rt] = x;
-      }
-    }
-    int kpos[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[buf][q4 * 16 + col];
-    const bool late = kpos[0] > minpos || kpos[1] > minpos || kpos[2] > minpos || kpos[3] > minpos;
-    if (__any(late)) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kpos[q4] > rowpos[rt][i]) acc[q4][rt][i] = -kInf;
-    }
-
-    if (!PASS2) {
-      float lsum[RT][4];
-      bool redo = false;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float mc = st0[rt][i] * c;
-          float l = st1[rt][i];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) l += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
-          lsum[rt][i] = l;
-          redo |= !(l <= kBig);
-        }
-      if (__any(redo)) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float bm = fmaxf(fmaxf(acc[0][rt][i], acc[1][rt][i]), fmaxf(acc[2][rt][i], acc[3][rt][i]));
-            const float mn = fmaxf(st0[rt][i], bm);
-            const float mc = mn * c;
-            float l = st1[rt][i] * fast_exp2((st0[rt][i] - mn) * c);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) l += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
-            st0[rt][i] = mn;
-            lsum[rt][i] = l;
-          }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st1[rt][i] = lsum[rt][i];
-    } else {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float best = -kInf;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[q4][rt][i], c, -st0[rt][i]));
-        best = fmaxf(best, __shfl_xor(best, 16, kWave));
-        best = fmaxf(best, __shfl_xor(best, 32, kWave));
-        if (quad == 0) red[w][q4 * 16 + col] = best;
-      }
-    }
+    rows.template logits<LS>(acc, kt[buf], kps[buf], col, quad);
+    if (!PASS2) stats_update<RT>(st0, st1, acc, c);
+    else key_max<RT>(acc, st0, c, red[w], col, quad);
     __syncthreads();
     if (has_next) store_batch(buf ^ 1);
-    if (PASS2 && tid < BK) {
+    if (PASS2 && tid < kBK) {
       const int j = kb + tid;
       if (j < k1) {
         const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
@@ -383,26 +436,153 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
     __syncthreads();
     buf ^= 1;
   }
+  if (!PASS2) stats_publish<RT>(a, st0, st1, s, ch, w, col, quad, c);
+}
 
-  if (!PASS2) {
-    // combine the 16 key columns held by each lane group, then publish
+// Fused variant: one work-group per (segment, 256-key chunk), taken in ticket
+// order from an atomic counter.  The chunk's keys stay in LDS; after pass 1
+// the work-group publishes its row statistics, waits until every chunk of its
+// segment has published (a bounded spin on a per-segment counter), merges
+// the log-sum-exp and runs pass 2 on the keys still in LDS, so K is read from
+// HBM once.  Deadlock-free: a ticket is only taken by a running work-group,
+// so all chunks of a segment but those of the newest segment are held by
+// running or finished work-groups, and the newest segment's missing chunks
+// are taken as soon as any older work-group finishes.  The spin is bounded
+// (kSpinLimit polls) so a broken counter cannot hang the GPU.
+constexpr int kFusedChunk = 256;
+constexpr int kSpinLimit = 1 << 22;
+
+template <int D, int RT>
+__global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __restrict__ ctr) {
+  constexpr int LS = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = kBK * CPR / 256;
+  constexpr int NB = kFusedChunk / kBK;      // LDS batches per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t kt[NB][kBK * LS];
+  __shared__ int kps[NB][kBK];
+  __shared__ float red[4][kBK];
+  __shared__ float lse_s[kMaxObsRows];
+  __shared__ int sh_item;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  if (tid == 0) sh_item = atomicAdd(&ctr[0], 1);
+  __syncthreads();
+  const int item = sh_item;
+  const int s = item / a.n_chunks, ch = item % a.n_chunks;
+  if (s >= a.n_seg) return;
+  int64_t off;
+  int n;
+  if (!segment_ok(a, s, off, n)) return;
+  const int k0 = ch * kFusedChunk;
+  if (k0 >= n) return;
+  const int k1 = min(n, k0 + kFusedChunk);
+  const int nch = (n + kFusedChunk - 1) / kFusedChunk;
+  const int b = s / a.n_kv, g = s % a.n_kv;
+  const float c = kLog2e / sqrtf(float(D));
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+
+  WaveRows<D, RT> rows;
+  rows.load(a, b, g, w, col, quad);
+  float st0[RT][4], st1[RT][4];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float m = st0[rt][i], l = st1[rt][i];
+    for (int i = 0; i < 4; ++i) {
+      st0[rt][i] = kNegBig;
+      st1[rt][i] = 0.f;
+    }
+
+  uint4 pre[CPT];
+  int prepos = INT_MAX;
+  auto load_batch = [&](int kb) {
+    const bool full = kb + kBK <= k1;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float m2 = __shfl_xor(m, o, kWave), l2 = __shfl_xor(l, o, kWave);
-          const float M = fmaxf(m, m2);
-          l = l * exp2f((m - M) * c) + l2 * exp2f((m2 - M) * c);
-          m = M;
-        }
-        const int r = 16 * (w * RT + rt) + 4 * quad + i;
-        if (col == 0 && r < a.rows)
-          a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(m * c, l);
-      }
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = tid + 256 * u;
+      const int key = cidx / CPR, part = cidx % CPR;
+      const int j = kb + key;
+      pre[u] = (full || j < k1) ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8)
+                                : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kBK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
+  };
+  auto store_batch = [&](int bi) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = tid + 256 * u;
+      const int key = cidx / CPR, part = cidx % CPR;
+      *reinterpret_cast<uint4*>(&kt[bi][key * LS + part * 8]) = pre[u];
+    }
+    if (tid < kBK) kps[bi][tid] = prepos;
+  };
+
+  const int nb = (k1 - k0 + kBK - 1) / kBK;
+  load_batch(k0);
+  store_batch(0);
+  __syncthreads();
+  for (int bi = 0; bi < nb; ++bi) {
+    if (bi + 1 < nb) load_batch(k0 + (bi + 1) * kBK);
+    f32x4 acc[4][RT];
+    rows.template logits<LS>(acc, kt[bi], kps[bi], col, quad);
+    stats_update<RT>(st0, st1, acc, c);
+    if (bi + 1 < nb) store_batch(bi + 1);
+    __syncthreads();
   }
+  stats_publish<RT>(a, st0, st1, s, ch, w, col, quad, c);
+
+  // segment barrier: publish, then wait for every chunk of this segment
+  // (release on the increment; relaxed polling, which reads the counter at the
+  // coherence point; one acquire fence once the count is complete)
+  __syncthreads();
+  if (tid == 0) {
+    __hip_atomic_fetch_add(&ctr[1 + s], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while (__hip_atomic_load(&ctr[1 + s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
+      __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  for (int r = tid; r < a.rows; r += 256) {
+    const float2* st = a.stats + int64_t(s) * a.n_chunks * a.rows + r;
+    float M = kNegBig;
+    for (int q = 0; q < nch; ++q) M = fmaxf(M, st[int64_t(q) * a.rows].x);
+    float L = 0.f;
+    for (int q = 0; q < nch; ++q) {
+      const float2 v = st[int64_t(q) * a.rows];
+      L += v.y * exp2f(v.x - M);
+    }
+    lse_s[r] = L > 0.f ? M + log2f(L) : kInf;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * (w * RT + rt) + 4 * quad + i;
+      st0[rt][i] = (rows.rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
+    }
+  for (int bi = 0; bi < nb; ++bi) {
+    f32x4 acc[4][RT];
+    rows.template logits<LS>(acc, kt[bi], kps[bi], col, quad);
+    key_max<RT>(acc, st0, c, red[w], col, quad);
+    __syncthreads();
+    if (tid < kBK) {
+      const int j = k0 + bi * kBK + tid;
+      if (j < k1) {
+        const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        a.scores[off + j] = fast_exp2(m);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Zero the fused kernel's ticket and per-segment counters (a plain kernel, so
+// the step can be captured in a graph).
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // ------------------------------------------------------------ entropy
@@ -461,6 +641,27 @@ hipError_t launch_mfma_rt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   }
 }
 
+template <int D, int RT>
+hipError_t launch_fused_t(const ScoreArgs& a, int* ctr, hipStream_t st) {
+  const int n_ctr = 1 + a.n_seg;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctr + 255) / 256)), dim3(256), 0, st, ctr, n_ctr);
+  const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
+  hipLaunchKernelGGL((score_fused_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctr);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fused(const ScoreArgs& a, int* ctr, hipStream_t st) {
+  const int tiles = (a.rows + 15) / 16;
+  const int rt = (tiles + 3) / 4;
+  switch (rt) {
+    case 1: return launch_fused_t<D, 1>(a, ctr, st);
+    case 2: return launch_fused_t<D, 2>(a, ctr, st);
+    case 3: return launch_fused_t<D, 3>(a, ctr, st);
+    default: return launch_fused_t<D, 4>(a, ctr, st);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const size_t sh = size_t(a.rows) * D * sizeof(T) + size_t(a.rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
@@ -481,7 +682,8 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
   const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
-  return qr + st + ls;
+  const size_t ct = align_up(size_t(n_seg + 1) * sizeof(int));
+  return qr + st + ls + ct;
 }
 
 size_t valu_lds_bytes(int rows, int D, int dtype) {
@@ -491,8 +693,9 @@ size_t valu_lds_bytes(int rows, int D, int dtype) {
 hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const int batch = a.n_seg / a.n_kv;
   const size_t elem = a.dtype == 0 ? 2 : 4;
-  const bool mfma = a.dtype == 0 && a.impl == 0;
-  a.chunk = mfma ? kMfmaChunk : kScoreChunk;
+  const bool fused = a.dtype == 0 && a.impl == 0;
+  const bool mfma = a.dtype == 0 && a.impl == 2;
+  a.chunk = fused ? kFusedChunk : (mfma ? kMfmaChunk : kScoreChunk);
   a.n_chunks = (a.max_seg_len + a.chunk - 1) / a.chunk;
   const size_t nch256 = (size_t(a.max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   char* w = static_cast<char*>(ws);
@@ -501,6 +704,8 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   a.stats = reinterpret_cast<float2*>(w);
   w += align_up(size_t(a.n_seg) * (nch256 ? nch256 : 1) * a.rows * sizeof(float2));
   a.lse = reinterpret_cast<float*>(w);
+  w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
+  int* ctr = reinterpret_cast<int*>(w);
   const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2);
   const dim3 rg(unsigned((n_work + 255) / 256));
   if (n_work > 0) {
@@ -516,7 +721,9 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
-  if (mfma) {
+  if (fused) {
+    e = a.head_dim == 128 ? launch_fused<128>(a, ctr, st) : launch_fused<64>(a, ctr, st);
+  } else if (mfma) {
     e = a.head_dim == 128 ? launch_mfma_rt<128>(a, grid, st) : launch_mfma_rt<64>(a, grid, st);
   } else if (a.dtype == 0) {
     e = a.head_dim == 128 ? launch_valu<uint16_t, 128>(a, grid, st) : launch_valu<uint16_t, 64>(a, grid, st);

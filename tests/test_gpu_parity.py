@@ -55,14 +55,14 @@ def test_rope_keys_bit_exact(name):
     assert mism == 0, f"{mism} of {got.size} rotated key elements differ"
 
 
-@pytest.mark.parametrize("impl", ["mfma", "valu"])
+@pytest.mark.parametrize("impl", ["twopass", "fused", "valu"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_scores_match_oracle(name, impl, monkeypatch):
     w, L, D, k_orc, s_orc = _case(name)
-    if impl == "valu":
+    if impl != "twopass":
         if w.dtype != "bf16":
             pytest.skip("fp32 caches always use the VALU path")
-        monkeypatch.setenv("KVE_SCORE_IMPL", "valu")
+        monkeypatch.setenv("KVE_SCORE_IMPL", impl)
     scores, ent = score_layer(D, w, entropy=True)
     torch.cuda.synchronize()
     g = scores.cpu().numpy()
@@ -287,3 +287,43 @@ def test_invalid_arguments_raise_before_launch():
     with pytest.raises(kv.KveError) as ei:
         kv.kv_evict_select_compact(c, scores, None, 4, 16, cout, kept_idx=out["kept"], uniform_budget=300)
     assert ei.value.name == "KVE_EALIAS"
+
+
+def test_entropy_budgets_drive_variable_k_selection():
+    """Scores with head entropy -> per-head budgets (layer total from the wave
+    table) -> variable-K selection, all on the GPU, against the oracle."""
+    w = CASES["llama-ragged"]
+    w_, L, D, k_orc, s_orc = _case("llama-ragged")
+    n_layers, layer = 32, 9
+    table = torch.zeros(n_layers, dtype=torch.int32, device="cuda")
+    kv.kv_evict_wave_budgets(n_layers, w.wave_center, w.wave_sigma, 8 * 1024, 64 // 4, table)
+    scores, ent = score_layer(D, w, entropy=True)
+    torch.cuda.synchronize()
+    tab = table.cpu().numpy()
+    assert np.array_equal(tab, oracle.layer_wave_budgets(n_layers, w.wave_center, w.wave_sigma, 8 * 1024, 16))
+    total = torch.full((w.batch,), int(w.n_kv_heads * tab[layer]), dtype=torch.int32, device="cuda")
+    bud = torch.zeros(w.batch * w.n_kv_heads, dtype=torch.int32, device="cuda")
+    kv.kv_evict_budgets(ent, total, D["seg_len"], w.batch, w.n_kv_heads, 24, bud)
+    out = alloc_out(D, w, int(max(L["lengths"])))
+    select_compact(D, w, scores, out, budget=bud)
+    torch.cuda.synchronize()
+    g_bud = bud.cpu().numpy()
+    kept = out["kept"].cpu().numpy()
+    lens = out["seg_len"].cpu().numpy()
+    cap = out["cap"]
+    for b in range(w.batch):
+        segs = range(b * w.n_kv_heads, (b + 1) * w.n_kv_heads)
+        n = [int(L["seg_len"][s]) for s in segs]
+        E = np.array([oracle.normalized_entropy(s_orc[int(L["seg_off"][s]):int(L["seg_off"][s]) + n[i]])
+                      for i, s in enumerate(segs)])
+        want = oracle.head_budgets(E, np.array(n), int(w.n_kv_heads * tab[layer]), 24)
+        got = g_bud[b * w.n_kv_heads:(b + 1) * w.n_kv_heads]
+        assert got.sum() == want.sum() and np.all(got >= 24)
+        if not np.array_equal(got, want):
+            # only a near-tie of largest-remainder fractions may move one token between heads
+            assert np.abs(got - want).max() <= 1, (got, want)
+        for i, s in enumerate(segs):
+            assert lens[s] == got[i]
+            o = int(L["seg_off"][s])
+            ok, _, msg = kept_matches(kept[s * cap:s * cap + got[i]], s_orc[o:o + n[i]], n[i], int(got[i]), 4, 16)
+            assert ok, msg
