@@ -35,10 +35,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-4b-36l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", choices=["serial", "pipelined"], default="pipelined")
-    ap.add_argument("--score-group", type=int, default=1, help="layers per scoring call (0 = all)")
+    ap.add_argument("--schedule", choices=["serial", "pipelined"], default="serial")
+    ap.add_argument("--score-group", type=int, default=0, help="layers per scoring call (0 = all)")
     ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
-    ap.add_argument("--graph", type=int, default=1, help="replay each trigger as a captured HIP graph")
+    ap.add_argument("--graph", type=int, default=0, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     return ap.parse_args()
 

@@ -56,14 +56,14 @@ kve_status check_cache(const kve_cache* c, const char* name, bool need_v) {
 
 size_t rows_bytes(const kve_cache* c) { return size_t(c->n_rows) * c->head_dim * elem_bytes(c->dtype); }
 
-// Scoring implementation for bf16 caches: two MFMA passes (default), or for
-// cross-checks "fused" (one K read, work-groups of a segment meet at a
-// barrier between the passes) or "valu".
+// Scoring implementation for bf16 caches: two MFMA passes (default), the
+// single-read MFMA kernel ("fused") or, for cross-checks, the plain VALU
+// kernels ("valu").
 int score_impl() {
   const char* e = std::getenv("KVE_SCORE_IMPL");
   if (e && std::strcmp(e, "valu") == 0) return 1;
-  if (e && std::strcmp(e, "fused") == 0) return 0;
-  return 2;
+  if (e && std::strcmp(e, "fused") == 0) return 2;
+  return 0;
 }
 
 size_t valu_lds(int rows, int D, int dtype) {

@@ -33,7 +33,7 @@ struct ScoreArgs {
   float* lse;             // [n_seg, rows] merged row log-sum-exp, log2 units (workspace)
   int32_t n_chunks;
   int32_t chunk;          // keys per work-group
-  int32_t impl;           // 0: fused MFMA (one K read), 1: plain VALU, 2: two-pass MFMA
+  int32_t impl;           // 0: two-pass MFMA, 1: plain VALU, 2: single-read MFMA
 };
 
 size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,

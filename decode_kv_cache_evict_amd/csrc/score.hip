@@ -176,21 +176,24 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------ MFMA path (bf16)
-// Work-groups of 4 waves.  Wave w owns row tiles w*RT .. w*RT+RT-1 (16 rows
-// each) and keeps their rotated queries in registers as MFMA A operands; keys
-// sit in LDS in 64-key batches that every wave reads as B operands.  For
-// v_mfma_f32_16x16x32_bf16 lane l holds A row l%16 / B column l%16 with
-// k-slice 8*(l/16)..+7 of each 32-wide step, and result rows 4*(l/16)+i of
-// column l%16.
+// Two launches over (segment, 1024-key chunk) work-groups of 4 waves: pass 1
+// publishes per-chunk row statistics, merge_lse_kernel folds them into each
+// row's log-sum-exp, pass 2 recomputes the logits and keeps the per-key max.
+//
+// Wave w owns row tiles w*RT .. w*RT+RT-1 (16 rows each) and keeps their
+// rotated queries in registers as MFMA A operands; keys stream through a
+// double-buffered LDS tile of 64 keys (one barrier per tile) that every wave
+// reads as B operands.  For v_mfma_f32_16x16x32_bf16 lane l holds A row l%16 /
+// B column l%16 with k-slice 8*(l/16)..+7 of each 32-wide step, and result rows
+// 4*(l/16)+i of column l%16.  The epilogue works on two 16-key tiles at a time.
 //
 // Pass 1 keeps, per lane and row, a reference value m and l = sum of
-// exp2(c*x - c*m) over the keys it has seen.  m is only moved when a batch's
-// sum leaves [0, 2^64] (a term overflowed or grew far above the reference):
-// the batch is then redone with m raised to the running maximum.  The first
-// batch always takes that path (m starts at -1e30), later ones almost never,
-// so the common case costs one fma, one exp and one add per logit.  The causal
-// mask is applied only to batches holding a key newer than the wave's earliest
-// query position.
+// exp2(c*x - c*m) over the keys it has seen.  m is only moved when a sum leaves
+// [0, 2^64] (a term overflowed or grew far above the reference): the tiles are
+// then redone with m raised to the running maximum.  The first tiles always take
+// that path (m starts at -1e30), later ones almost never, so the common case
+// costs one fma, one exp and one add per logit.  The causal mask is applied only
+// to tiles holding a key newer than the wave's earliest query position.
 constexpr float kBig = 18446744073709551616.0f;   // 2^64
 constexpr int kBK = 64;                           // keys per LDS batch
 
@@ -203,23 +206,23 @@ struct WaveRows {
   int rowpos[RT][4];
   int minpos;
 
-  __device__ __forceinline__ void load(const ScoreArgs& a, int b, int g, int w, int col, int quad) {
-    const uint16_t* qr = static_cast<const uint16_t*>(a.qr);
+  // rpos/qoff: per-row position and row index into the rotated queries (-1: absent), in LDS.
+  __device__ __forceinline__ void load(const uint16_t* qr, const int* rpos, const int* qoff, int w, int col,
+                                       int quad) {
     minpos = INT_MAX;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int t = w * RT + rt;
-      const int ra = 16 * t + col;
-      const bool ok = row_position(a, b, ra) >= 0;
-      const uint16_t* src = qr + (ok ? row_qr_index(a, b, g, ra) : 0) * D;
+      const int qo = qoff[16 * t + col];
+      const uint16_t* src = qr + int64_t(qo >= 0 ? qo : 0) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = ok ? *reinterpret_cast<const uint4*>(src + ks * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
+        uint4 v = qo >= 0 ? *reinterpret_cast<const uint4*>(src + ks * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
         qa[rt][ks] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rp = row_position(a, b, 16 * t + 4 * quad + i);
+        const int rp = rpos[16 * t + 4 * quad + i];
         rowpos[rt][i] = rp;
         if (rp >= 0) minpos = min(minpos, rp);
       }
@@ -228,15 +231,14 @@ struct WaveRows {
     for (int o = 32; o > 0; o >>= 1) minpos = min(minpos, __shfl_xor(minpos, o, kWave));
   }
 
-  // Logits of the 64 keys of one LDS batch (row stride LS): acc[q4][rt] holds
-  // rows 16*(w*RT+rt) + 4*quad + i against key q4*16 + col; masked entries -inf.
+  // Logits of key tiles q0, q0+1 of one LDS batch (row stride LS): acc[j][rt] holds
+  // rows 16*(w*RT+rt) + 4*quad + i against key (q0+j)*16 + col.
   template <int LS>
-  __device__ __forceinline__ void logits(f32x4 (&acc)[4][RT], const uint16_t* kb, const int* kp, int col,
-                                         int quad) const {
+  __device__ __forceinline__ void logits2(f32x4 (&acc)[2][RT], const uint16_t* kb, int q0, int col, int quad) const {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int j = 0; j < 2; ++j) {
       bf16x8 bfr[KS];
-      const uint16_t* krow = kb + (q4 * 16 + col) * LS + quad * 8;
+      const uint16_t* krow = kb + ((q0 + j) * 16 + col) * LS + quad * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         bfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
@@ -245,28 +247,25 @@ struct WaveRows {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], bfr[ks], x, 0, 0, 0);
-        acc[q4][rt] = x;
+        acc[j][rt] = x;
       }
     }
-    int kpos[4];
+  }
+
+  __device__ __forceinline__ void mask2(f32x4 (&acc)[2][RT], const int (&kpos)[2]) const {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kp[q4 * 16 + col];
-    const bool late = kpos[0] > minpos || kpos[1] > minpos || kpos[2] > minpos || kpos[3] > minpos;
-    if (__any(late)) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kpos[q4] > rowpos[rt][i]) acc[q4][rt][i] = -kInf;
-    }
+        for (int i = 0; i < 4; ++i)
+          if (kpos[j] > rowpos[rt][i]) acc[j][rt][i] = -kInf;
   }
 };
 
-// Pass-1 update of (m, l) with one batch of logits.
+// Pass-1 update of (m, l) with two key tiles of logits.
 template <int RT>
-__device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[4][RT],
+__device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[2][RT],
                                              float c) {
   float lsum[RT][4];
   bool redo = false;
@@ -275,9 +274,7 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float mc = m[rt][i] * c;
-      float v = l[rt][i];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) v += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+      const float v = l[rt][i] + fast_exp2(fmaf(acc[0][rt][i], c, -mc)) + fast_exp2(fmaf(acc[1][rt][i], c, -mc));
       lsum[rt][i] = v;
       redo |= !(v <= kBig);
     }
@@ -286,14 +283,11 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float bm = fmaxf(fmaxf(acc[0][rt][i], acc[1][rt][i]), fmaxf(acc[2][rt][i], acc[3][rt][i]));
-        const float mn = fmaxf(m[rt][i], bm);
+        const float mn = fmaxf(m[rt][i], fmaxf(acc[0][rt][i], acc[1][rt][i]));
         const float mc = mn * c;
-        float v = l[rt][i] * fast_exp2((m[rt][i] - mn) * c);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) v += fast_exp2(fmaf(acc[q4][rt][i], c, -mc));
+        lsum[rt][i] = l[rt][i] * fast_exp2((m[rt][i] - mn) * c) + fast_exp2(fmaf(acc[0][rt][i], c, -mc)) +
+                      fast_exp2(fmaf(acc[1][rt][i], c, -mc));
         m[rt][i] = mn;
-        lsum[rt][i] = v;
       }
   }
 #pragma unroll
@@ -302,56 +296,36 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
     for (int i = 0; i < 4; ++i) l[rt][i] = lsum[rt][i];
 }
 
-// Combine the 16 key columns of each lane group and publish one (c*m, l) per row.
+// Pass-2: per key of tiles q0, q0+1, the max over this wave's rows of
+// c*x - lse, combined over the 4 lane groups; written to redw[key].
 template <int RT>
-__device__ __forceinline__ void stats_publish(const ScoreArgs& a, float (&m)[RT][4], float (&l)[RT][4], int s, int ch,
-                                              int w, int col, int quad, float c) {
+__device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float (&lse)[RT][4], float c, float* redw,
+                                         int q0, int col, int quad) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mm = m[rt][i], ll = l[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
-        const float M = fmaxf(mm, m2);
-        ll = ll * exp2f((mm - M) * c) + l2 * exp2f((m2 - M) * c);
-        mm = M;
-      }
-      const int r = 16 * (w * RT + rt) + 4 * quad + i;
-      if (col == 0 && r < a.rows) a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(mm * c, ll);
-    }
-}
-
-// Pass-2: per key of the batch, the max over this wave's rows of c*x - lse,
-// combined over the 4 lane groups; written to red[w][key].
-template <int RT>
-__device__ __forceinline__ void key_max(const f32x4 (&acc)[4][RT], const float (&lse)[RT][4], float c,
-                                        float* redw, int col, int quad) {
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
+  for (int j = 0; j < 2; ++j) {
     float best = -kInf;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[q4][rt][i], c, -lse[rt][i]));
+      for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[j][rt][i], c, -lse[rt][i]));
     best = fmaxf(best, __shfl_xor(best, 16, kWave));
     best = fmaxf(best, __shfl_xor(best, 32, kWave));
-    if (quad == 0) redw[q4 * 16 + col] = best;
+    if (quad == 0) redw[(q0 + j) * 16 + col] = best;
   }
 }
 
-// Two-pass variant: pass 1 and pass 2 are separate launches over
-// (1024-key chunk, segment) work-groups; pass 2 re-reads K.
 template <int D, int RT, bool PASS2>
-__global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_mfma_kernel(ScoreArgs a) {
   constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int CPT = kBK * CPR / 256;       // chunks per thread per batch
+  constexpr int KPU = 256 / CPR;             // keys covered by one 16-byte load per thread
+  constexpr int CPT = kBK / KPU;             // loads per thread per batch
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kBK * LS];
   __shared__ int kps[2][kBK];
-  __shared__ float red[4][kBK];
+  __shared__ float red[2][4][kBK];
   __shared__ float lse_s[kMaxObsRows];
+  __shared__ int rpos_s[kMaxObsRows];
+  __shared__ int qoff_s[kMaxObsRows];
 
   const int s = blockIdx.y, ch = blockIdx.x;
   int64_t off;
@@ -364,113 +338,170 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
   const float c = kLog2e / sqrtf(float(D));
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
 
-  if (PASS2)
-    for (int r = tid; r < a.rows; r += 256) lse_s[r] = a.lse[int64_t(s) * a.rows + r];
+  // per-row metadata, once per work-group
+  for (int r = tid; r < 16 * 4 * RT; r += 256) {
+    const int rp = row_position(a, b, r);
+    rpos_s[r] = rp;
+    qoff_s[r] = rp >= 0 ? int(row_qr_index(a, b, g, r)) : -1;
+    if (PASS2) lse_s[r] = rp >= 0 ? a.lse[int64_t(s) * a.rows + r] : kInf;
+  }
+  __syncthreads();
   WaveRows<D, RT> rows;
-  rows.load(a, b, g, w, col, quad);
-  float st0[RT][4], st1[RT][4];
+  rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
+  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse (log2 units)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st0[rt][i] = kNegBig;
+      st0[rt][i] = PASS2 ? lse_s[16 * (w * RT + rt) + 4 * quad + i] : kNegBig;
       st1[rt][i] = 0.f;
     }
 
+  // thread's share of a batch: keys key0 + u*KPU (u < CPT), 16-byte chunk `part`
+  const int key0 = tid / CPR, part = tid % CPR;
+  const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
   uint4 pre[CPT];
   int prepos = INT_MAX;
-  auto load_batch = [&](int kb) {
-    const bool full = kb + kBK <= k1;
+  auto load_batch = [&](int kb) {          // kb: batch start relative to k0
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int cidx = tid + 256 * u;
-      const int key = cidx / CPR, part = cidx % CPR;
-      const int j = kb + key;
-      pre[u] = (full || j < k1) ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8)
-                                : make_uint4(0, 0, 0, 0);
+      const bool ok = k0 + kb + key0 + u * KPU < k1;
+      pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(kb + u * KPU) * D) : make_uint4(0, 0, 0, 0);
     }
-    if (tid < kBK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
+    if (tid < kBK) prepos = (k0 + kb + tid < k1) ? a.pos[off + k0 + kb + tid] : INT_MAX;
   };
   auto store_batch = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int cidx = tid + 256 * u;
-      const int key = cidx / CPR, part = cidx % CPR;
-      *reinterpret_cast<uint4*>(&kt[buf][key * LS + part * 8]) = pre[u];
-    }
+    for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[buf][(key0 + u * KPU) * LS + part * 8]) = pre[u];
     if (tid < kBK) kps[buf][tid] = prepos;
   };
-
-  load_batch(k0);
-  store_batch(0);
-  __syncthreads();
-  if (PASS2) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * (w * RT + rt) + 4 * quad + i;
-        st0[rt][i] = (rows.rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
-      }
-  }
-
-  int buf = 0;
-  for (int kb = k0; kb < k1; kb += kBK) {
-    const bool has_next = kb + kBK < k1;
-    if (has_next) load_batch(kb + kBK);
-    f32x4 acc[4][RT];
-    rows.template logits<LS>(acc, kt[buf], kps[buf], col, quad);
-    if (!PASS2) stats_update<RT>(st0, st1, acc, c);
-    else key_max<RT>(acc, st0, c, red[w], col, quad);
-    __syncthreads();
-    if (has_next) store_batch(buf ^ 1);
-    if (PASS2 && tid < kBK) {
-      const int j = kb + tid;
-      if (j < k1) {
-        const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-        a.scores[off + j] = fast_exp2(m);
-      }
+  auto finish_keys = [&](int bi, int kb) {  // pass 2: per-key max over the 4 waves -> score
+    const int j = k0 + kb + tid;
+    if (tid < kBK && j < k1) {
+      const float m = fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid]));
+      a.scores[off + j] = fast_exp2(m);
     }
+  };
+
+  const int span = k1 - k0;
+  load_batch(0);
+  store_batch(0);
+  if (kBK < span) load_batch(kBK);
+  __syncthreads();
+  int cur = 0;
+  for (int kb = 0; kb < span; kb += kBK) {
+    int kpos[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[cur][q4 * 16 + col];
+    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
+                      kpos[3] > rows.minpos;
+    const bool any_late = __any(late);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc[2][RT];
+      rows.template logits2<LS>(acc, kt[cur], 2 * h, col, quad);
+      if (any_late) {
+        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
+        rows.mask2(acc, kp2);
+      }
+      if (!PASS2) stats_update<RT>(st0, st1, acc, c);
+      else key_max2<RT>(acc, st0, c, red[cur][w], 2 * h, col, quad);
+    }
+    if (kb + kBK < span) store_batch(cur ^ 1);
+    if (kb + 2 * kBK < span) load_batch(kb + 2 * kBK);
+    if (PASS2 && kb > 0) finish_keys(cur ^ 1, kb - kBK);
     __syncthreads();
-    buf ^= 1;
+    cur ^= 1;
   }
-  if (!PASS2) stats_publish<RT>(a, st0, st1, s, ch, w, col, quad, c);
+  if (PASS2) {
+    finish_keys(cur ^ 1, ((span - 1) / kBK) * kBK);
+    return;
+  }
+  // combine the 16 key columns held by each lane group, then publish
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mm = st0[rt][i], ll = st1[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
+        const float M = fmaxf(mm, m2);
+        ll = ll * fast_exp2((mm - M) * c) + l2 * fast_exp2((m2 - M) * c);
+        mm = M;
+      }
+      const int r = 16 * (w * RT + rt) + 4 * quad + i;
+      if (col == 0 && r < a.rows) a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(mm * c, ll);
+    }
 }
 
-// Fused variant: one work-group per (segment, 256-key chunk), taken in ticket
-// order from an atomic counter.  The chunk's keys stay in LDS; after pass 1
-// the work-group publishes its row statistics, waits until every chunk of its
-// segment has published (a bounded spin on a per-segment counter), merges
-// the log-sum-exp and runs pass 2 on the keys still in LDS, so K is read from
-// HBM once.  Deadlock-free: a ticket is only taken by a running work-group,
-// so all chunks of a segment but those of the newest segment are held by
-// running or finished work-groups, and the newest segment's missing chunks
-// are taken as soon as any older work-group finishes.  The spin is bounded
-// (kSpinLimit polls) so a broken counter cannot hang the GPU.
+// Single-read variant: one work-group per (segment, 256-key chunk).  The
+// chunk's keys stay in LDS for both passes; between the passes the work-groups
+// of a segment exchange their row statistics through coherent (agent-scope)
+// atomic stores and loads and meet at a per-segment arrival counter, so K is
+// read from HBM once.
+//
+// Work assignment: eight ticket queues, queue q holding the chunks of the
+// segments s = q (mod 8).  A work-group takes a ticket from the queue of the
+// XCD it runs on (so a segment's chunks share one L2 and its queries are
+// fetched once) and steals from the other queues when its own is empty.
+// Deadlock-free: a ticket is only taken by a running work-group, so every
+// chunk of a segment but those of the newest segment in a queue is held by a
+// running or finished work-group, and missing chunks are taken as soon as any
+// older work-group finishes.  The wait is bounded (kSpinLimit polls).
 constexpr int kFusedChunk = 256;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kQueues = 8;
+
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & (kQueues - 1);
+}
+
+__device__ __forceinline__ void store_stat(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_stat(const float2* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 
 template <int D, int RT>
-__global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __restrict__ ctr) {
+__global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __restrict__ ctl) {
   constexpr int LS = D + 8;
   constexpr int CPR = D / 8;
-  constexpr int CPT = kBK * CPR / 256;
-  constexpr int NB = kFusedChunk / kBK;      // LDS batches per chunk
+  constexpr int KPU = 256 / CPR;
+  constexpr int CPT = kBK / KPU;
+  constexpr int NB = kFusedChunk / kBK;
   __shared__ __attribute__((aligned(16))) uint16_t kt[NB][kBK * LS];
   __shared__ int kps[NB][kBK];
   __shared__ float red[4][kBK];
   __shared__ float lse_s[kMaxObsRows];
+  __shared__ int rpos_s[kMaxObsRows];
+  __shared__ int qoff_s[kMaxObsRows];
   __shared__ int sh_item;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
-  if (tid == 0) sh_item = atomicAdd(&ctr[0], 1);
+  if (tid == 0) {
+    const unsigned x = xcc_id();
+    int item = -1;
+    for (int k = 0; k < kQueues && item < 0; ++k) {
+      const int q = int((x + k) & (kQueues - 1));
+      const int nq = (q < a.n_seg ? (a.n_seg - q + kQueues - 1) / kQueues : 0) * a.n_chunks;
+      if (nq == 0 || __hip_atomic_load(&ctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nq) continue;
+      const int t = atomicAdd(&ctl[q], 1);
+      if (t < nq) item = (t / a.n_chunks * kQueues + q) * a.n_chunks + t % a.n_chunks;
+    }
+    sh_item = item;
+  }
   __syncthreads();
   const int item = sh_item;
+  if (item < 0) return;
   const int s = item / a.n_chunks, ch = item % a.n_chunks;
-  if (s >= a.n_seg) return;
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) return;
@@ -480,10 +511,15 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
   const int nch = (n + kFusedChunk - 1) / kFusedChunk;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
 
+  for (int r = tid; r < 16 * 4 * RT; r += 256) {
+    const int rp = row_position(a, b, r);
+    rpos_s[r] = rp;
+    qoff_s[r] = rp >= 0 ? int(row_qr_index(a, b, g, r)) : -1;
+  }
+  __syncthreads();
   WaveRows<D, RT> rows;
-  rows.load(a, b, g, w, col, quad);
+  rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
   float st0[RT][4], st1[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -493,93 +529,125 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
       st1[rt][i] = 0.f;
     }
 
+  const int key0 = tid / CPR, part = tid % CPR;
+  const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
   uint4 pre[CPT];
   int prepos = INT_MAX;
-  auto load_batch = [&](int kb) {
-    const bool full = kb + kBK <= k1;
+  auto load_batch = [&](int bi) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int cidx = tid + 256 * u;
-      const int key = cidx / CPR, part = cidx % CPR;
-      const int j = kb + key;
-      pre[u] = (full || j < k1) ? *reinterpret_cast<const uint4*>(K + (off + j) * D + part * 8)
-                                : make_uint4(0, 0, 0, 0);
+      const bool ok = k0 + bi * kBK + key0 + u * KPU < k1;
+      pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(bi * kBK + u * KPU) * D) : make_uint4(0, 0, 0, 0);
     }
-    if (tid < kBK) prepos = (kb + tid < k1) ? a.pos[off + kb + tid] : INT_MAX;
+    if (tid < kBK) prepos = (k0 + bi * kBK + tid < k1) ? a.pos[off + k0 + bi * kBK + tid] : INT_MAX;
   };
   auto store_batch = [&](int bi) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int cidx = tid + 256 * u;
-      const int key = cidx / CPR, part = cidx % CPR;
-      *reinterpret_cast<uint4*>(&kt[bi][key * LS + part * 8]) = pre[u];
-    }
+    for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[bi][(key0 + u * KPU) * LS + part * 8]) = pre[u];
     if (tid < kBK) kps[bi][tid] = prepos;
   };
 
   const int nb = (k1 - k0 + kBK - 1) / kBK;
-  load_batch(k0);
+  load_batch(0);
   store_batch(0);
+  if (nb > 1) load_batch(1);
   __syncthreads();
   for (int bi = 0; bi < nb; ++bi) {
-    if (bi + 1 < nb) load_batch(k0 + (bi + 1) * kBK);
-    f32x4 acc[4][RT];
-    rows.template logits<LS>(acc, kt[bi], kps[bi], col, quad);
-    stats_update<RT>(st0, st1, acc, c);
+    int kpos[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[bi][q4 * 16 + col];
+    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
+                      kpos[3] > rows.minpos;
+    const bool any_late = __any(late);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc[2][RT];
+      rows.template logits2<LS>(acc, kt[bi], 2 * h, col, quad);
+      if (any_late) {
+        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
+        rows.mask2(acc, kp2);
+      }
+      stats_update<RT>(st0, st1, acc, c);
+    }
     if (bi + 1 < nb) store_batch(bi + 1);
+    if (bi + 2 < nb) load_batch(bi + 2);
     __syncthreads();
   }
-  stats_publish<RT>(a, st0, st1, s, ch, w, col, quad, c);
-
-  // segment barrier: publish, then wait for every chunk of this segment
-  // (release on the increment; relaxed polling, which reads the counter at the
-  // coherence point; one acquire fence once the count is complete)
+  // publish this chunk's row statistics (coherent stores), then wait for the segment
+  float2* stats_seg = a.stats + int64_t(s) * a.n_chunks * a.rows;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mm = st0[rt][i], ll = st1[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
+        const float M = fmaxf(mm, m2);
+        ll = ll * fast_exp2((mm - M) * c) + l2 * fast_exp2((m2 - M) * c);
+        mm = M;
+      }
+      const int r = 16 * (w * RT + rt) + 4 * quad + i;
+      if (col == 0 && r < a.rows) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm * c, ll));
+    }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __hip_atomic_fetch_add(&ctr[1 + s], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int* arrive = ctl + kQueues + s;
+    atomicAdd(arrive, 1);
     int spins = 0;
-    while (__hip_atomic_load(&ctr[1 + s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
-      __builtin_amdgcn_s_sleep(2);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
+      __builtin_amdgcn_s_sleep(1);
   }
   __syncthreads();
-  for (int r = tid; r < a.rows; r += 256) {
-    const float2* st = a.stats + int64_t(s) * a.n_chunks * a.rows + r;
-    float M = kNegBig;
-    for (int q = 0; q < nch; ++q) M = fmaxf(M, st[int64_t(q) * a.rows].x);
-    float L = 0.f;
-    for (int q = 0; q < nch; ++q) {
-      const float2 v = st[int64_t(q) * a.rows];
-      L += v.y * exp2f(v.x - M);
+  for (int r = tid; r < 16 * 4 * RT; r += 256) {
+    float lse = kInf;
+    if (r < a.rows && rpos_s[r] >= 0) {
+      float M = kNegBig, L = 0.f;
+      for (int q = 0; q < nch; ++q) {
+        const float2 v = load_stat(&stats_seg[int64_t(q) * a.rows + r]);
+        const float Mn = fmaxf(M, v.x);
+        L = L * fast_exp2(M - Mn) + v.y * fast_exp2(v.x - Mn);
+        M = Mn;
+      }
+      lse = L > 0.f ? M + log2f(L) : kInf;
     }
-    lse_s[r] = L > 0.f ? M + log2f(L) : kInf;
+    lse_s[r] = lse;
   }
   __syncthreads();
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * (w * RT + rt) + 4 * quad + i;
-      st0[rt][i] = (rows.rowpos[rt][i] >= 0) ? lse_s[r] : kInf;
-    }
+    for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
   for (int bi = 0; bi < nb; ++bi) {
-    f32x4 acc[4][RT];
-    rows.template logits<LS>(acc, kt[bi], kps[bi], col, quad);
-    key_max<RT>(acc, st0, c, red[w], col, quad);
-    __syncthreads();
-    if (tid < kBK) {
-      const int j = k0 + bi * kBK + tid;
-      if (j < k1) {
-        const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-        a.scores[off + j] = fast_exp2(m);
+    int kpos[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[bi][q4 * 16 + col];
+    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
+                      kpos[3] > rows.minpos;
+    const bool any_late = __any(late);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc[2][RT];
+      rows.template logits2<LS>(acc, kt[bi], 2 * h, col, quad);
+      if (any_late) {
+        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
+        rows.mask2(acc, kp2);
       }
+      key_max2<RT>(acc, st0, c, red[w], 2 * h, col, quad);
+    }
+    __syncthreads();
+    const int j = k0 + bi * kBK + tid;
+    if (tid < kBK && j < k1) {
+      const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+      a.scores[off + j] = fast_exp2(m);
     }
     __syncthreads();
   }
 }
 
-// Zero the fused kernel's ticket and per-segment counters (a plain kernel, so
-// the step can be captured in a graph).
+// Zero a small int array (queue tickets and arrival counters) with a kernel, so
+// a captured graph holds no memset node.
 __global__ void zero_ints_kernel(int* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -642,23 +710,22 @@ hipError_t launch_mfma_rt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <int D, int RT>
-hipError_t launch_fused_t(const ScoreArgs& a, int* ctr, hipStream_t st) {
-  const int n_ctr = 1 + a.n_seg;
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctr + 255) / 256)), dim3(256), 0, st, ctr, n_ctr);
+hipError_t launch_fused_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
+  const int n_ctl = kQueues + a.n_seg;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
-  hipLaunchKernelGGL((score_fused_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctr);
+  hipLaunchKernelGGL((score_fused_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_fused(const ScoreArgs& a, int* ctr, hipStream_t st) {
-  const int tiles = (a.rows + 15) / 16;
-  const int rt = (tiles + 3) / 4;
+hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
+  const int rt = ((a.rows + 15) / 16 + 3) / 4;
   switch (rt) {
-    case 1: return launch_fused_t<D, 1>(a, ctr, st);
-    case 2: return launch_fused_t<D, 2>(a, ctr, st);
-    case 3: return launch_fused_t<D, 3>(a, ctr, st);
-    default: return launch_fused_t<D, 4>(a, ctr, st);
+    case 1: return launch_fused_t<D, 1>(a, ctl, st);
+    case 2: return launch_fused_t<D, 2>(a, ctl, st);
+    case 3: return launch_fused_t<D, 3>(a, ctl, st);
+    default: return launch_fused_t<D, 4>(a, ctl, st);
   }
 }
 
@@ -682,7 +749,7 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
   const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
-  const size_t ct = align_up(size_t(n_seg + 1) * sizeof(int));
+  const size_t ct = align_up(size_t(n_seg + kQueues) * sizeof(int));
   return qr + st + ls + ct;
 }
 
@@ -693,8 +760,8 @@ size_t valu_lds_bytes(int rows, int D, int dtype) {
 hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const int batch = a.n_seg / a.n_kv;
   const size_t elem = a.dtype == 0 ? 2 : 4;
-  const bool fused = a.dtype == 0 && a.impl == 0;
-  const bool mfma = a.dtype == 0 && a.impl == 2;
+  const bool mfma = a.dtype == 0 && a.impl == 0;
+  const bool fused = a.dtype == 0 && a.impl == 2;
   a.chunk = fused ? kFusedChunk : (mfma ? kMfmaChunk : kScoreChunk);
   a.n_chunks = (a.max_seg_len + a.chunk - 1) / a.chunk;
   const size_t nch256 = (size_t(a.max_seg_len) + kScoreChunk - 1) / kScoreChunk;
@@ -705,7 +772,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   w += align_up(size_t(a.n_seg) * (nch256 ? nch256 : 1) * a.rows * sizeof(float2));
   a.lse = reinterpret_cast<float*>(w);
   w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
-  int* ctr = reinterpret_cast<int*>(w);
+  int* ctl = reinterpret_cast<int*>(w);
   const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2);
   const dim3 rg(unsigned((n_work + 255) / 256));
   if (n_work > 0) {
@@ -722,7 +789,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
   if (fused) {
-    e = a.head_dim == 128 ? launch_fused<128>(a, ctr, st) : launch_fused<64>(a, ctr, st);
+    e = a.head_dim == 128 ? launch_fused<128>(a, ctl, st) : launch_fused<64>(a, ctl, st);
   } else if (mfma) {
     e = a.head_dim == 128 ? launch_mfma_rt<128>(a, grid, st) : launch_mfma_rt<64>(a, grid, st);
   } else if (a.dtype == 0) {

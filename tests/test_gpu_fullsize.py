@@ -1,0 +1,145 @@
+"""Full-size parity on sampled outputs, in the launch configuration the benchmark
+times (all layers of a trigger folded into one segment table: one score call,
+one select/compact call, one FPS call).  The oracle recomputes the sampled
+segments one by one from the generator's inputs."""
+import numpy as np
+import pytest
+import torch
+
+import decode_kv_cache_evict_amd as kv
+import oracle
+from tests.oracle_side import np64
+from tests.parity import assert_scores_close, kept_matches
+from workloads import get_workload, make_layer, make_traces
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.lib()
+
+
+def _oracle_segment(w, layer, b, g):
+    """Oracle scores of segment (b, g) of `layer`, from regenerated inputs."""
+    L = make_layer(w, layer, device="cuda")
+    n = L["lengths"][b]
+    s = b * w.n_kv_heads + g
+    o = int(L["seg_off"][s])
+    kpre = np64(L["k_pre"][o:o + n])
+    pos = L["pos"][o:o + n].cpu().numpy()
+    k = oracle.to_storage(oracle.rope(kpre, pos, w.rope_theta), w.dtype)
+    q = np64(L["q_obs"][b])
+    qp = L["q_pos"][b].cpu().numpy()
+    rows = [oracle.to_storage(oracle.rope(q[h], qp, w.rope_theta), w.dtype)
+            for h in range(g * w.group, (g + 1) * w.group)]
+    sc = oracle.segment_scores(k, pos, np.concatenate(rows), np.tile(qp, w.group), bool(w.causal))
+    return sc, np64(L["fps_buf"][b * w.n_q_heads:(b + 1) * w.n_q_heads]), n
+
+
+def test_qwen3_4b_36_layers_trigger_sampled():
+    import bench
+    w = get_workload("qwen3-4b-36l").scaled(triggers=1)
+    st = bench.build_states(w, "cuda")[0]
+    out = bench.make_out(w, "cuda")
+    scores = torch.empty(st.k.shape[0], dtype=torch.float32, device="cuda")
+    kept = torch.empty(out["k"].shape[0], dtype=torch.int32, device="cuda")
+    fbuf = torch.empty_like(st.buf)
+    fcnt = torch.empty_like(st.count)
+    picks = torch.empty(st.buf.shape[0], w.fps_keep, dtype=torch.int32, device="cuda")
+    cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off, st.seg_len, w.n_kv_heads, st.cap)
+    obs = kv.make_obs(st.q, st.q_pos, st.n_obs, w.rope_theta)
+    cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, out["cap"])
+    kv.kv_evict_score(cache, obs, scores)
+    kv.kv_evict_select_compact(cache, scores, None, w.n_prefix, w.n_recent, cout, kept_idx=kept,
+                               uniform_budget=w.budget)
+    kv.beacon_fps_update(st.buf, fbuf, st.count, fcnt, w.fps_keep, picks)
+    torch.cuda.synchronize()
+    assert torch.all(out["seg_len"] == w.budget)
+    assert torch.all(fcnt == w.fps_keep)
+    rng = np.random.default_rng(7)
+    n = w.len_hi
+    cap = out["cap"]
+    for layer in (0, 17, 35):
+        for b, g in {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}:
+            s_orc, bufs, _ = _oracle_segment(w, layer, b, g)
+            seg = (layer * w.batch + b) * w.n_kv_heads + g
+            got = scores[seg * n:(seg + 1) * n].cpu().numpy()
+            assert_scores_close(got, s_orc, what=f"layer {layer} request {b} head {g}")
+            ks = kept[seg * cap:(seg + 1) * cap].cpu().numpy()
+            ok, _, msg = kept_matches(ks, s_orc, n, w.budget, w.n_prefix, w.n_recent)
+            assert ok, msg
+            src = st.k[seg * n:(seg + 1) * n].view(torch.int16).cpu().numpy()
+            dst = out["k"][seg * cap:(seg + 1) * cap].view(torch.int16).cpu().numpy()
+            assert np.array_equal(dst, src[ks])
+            vs = st.v[seg * n:(seg + 1) * n].view(torch.int16).cpu().numpy()
+            vd = out["v"][seg * cap:(seg + 1) * cap].view(torch.int16).cpu().numpy()
+            assert np.array_equal(vd, vs[ks])
+            for h in range(g * w.group, (g + 1) * w.group):
+                p = (layer * w.batch + b) * w.n_q_heads + h
+                P = picks[p].cpu().numpy()
+                assert oracle.fps_acceptable(bufs[h], P, 2e-3)[0]
+                assert torch.equal(fbuf[p, :w.fps_keep], st.buf[p, np.sort(P).tolist()])
+
+
+def test_long_65k_attention_and_hidden_state_scores_sampled():
+    w = get_workload("long-65k")
+    L = make_layer(w, 0, device="cuda")
+    n = w.len_hi
+    k = torch.empty(L["k_pre"].shape, dtype=torch.bfloat16, device="cuda")
+    kv.kv_rope_apply(L["k_pre"], k, L["pos"], w.rope_theta)
+    cache = kv.make_cache(k, L["v"], L["pos"], L["seg_off"], L["seg_len"], w.n_kv_heads, n)
+    obs = kv.make_obs(L["q_obs"], L["q_pos"], L["n_obs"], w.rope_theta)
+    scores = torch.empty(k.shape[0], dtype=torch.float32, device="cuda")
+    kv.kv_evict_score(cache, obs, scores)
+    # attention-free score on the same cache
+    h = make_traces(w, device="cuda")
+    epi = torch.empty(w.batch, n, dtype=torch.float32, device="cuda")
+    gser = torch.empty(2, w.batch, n, dtype=torch.float32, device="cuda")
+    kv.epikv_score(h[0], h[1], w.epikv_window, w.epikv_eps, epi, g_out=gser)
+    S = w.batch * w.n_kv_heads
+    mk = lambda: {"k": torch.empty(S * w.budget, w.head_dim, dtype=torch.bfloat16, device="cuda"),  # noqa: E731
+                  "v": torch.empty(S * w.budget, w.head_dim, dtype=torch.bfloat16, device="cuda"),
+                  "pos": torch.empty(S * w.budget, dtype=torch.int32, device="cuda"),
+                  "seg_off": torch.arange(S, dtype=torch.int64, device="cuda") * w.budget,
+                  "seg_len": torch.empty(S, dtype=torch.int32, device="cuda"),
+                  "kept": torch.empty(S * w.budget, dtype=torch.int32, device="cuda")}
+    outs = {"attn": mk(), "epikv": mk()}
+    score_off = (torch.arange(S, device="cuda") // w.n_kv_heads * n).to(torch.int64)
+    for name, sc, so in (("attn", scores, None), ("epikv", epi.view(-1), score_off)):
+        o = outs[name]
+        co = kv.make_cache(o["k"], o["v"], o["pos"], o["seg_off"], o["seg_len"], w.n_kv_heads, w.budget)
+        kv.kv_evict_select_compact(cache, sc, None, w.n_prefix, w.n_recent, co, kept_idx=o["kept"],
+                                   score_off=so, uniform_budget=w.budget)
+    torch.cuda.synchronize()
+    # attention scores and kept sets of two sampled segments
+    for b, g in ((0, 3), (3, 6)):
+        seg = b * w.n_kv_heads + g
+        o = seg * n
+        kpre = np64(L["k_pre"][o:o + n])
+        pos = np.arange(n)
+        kk = oracle.to_storage(oracle.rope(kpre, pos, w.rope_theta), w.dtype)
+        q = np64(L["q_obs"][b])
+        qp = L["q_pos"][b].cpu().numpy()
+        rows = [oracle.to_storage(oracle.rope(q[hh], qp, w.rope_theta), w.dtype)
+                for hh in range(g * w.group, (g + 1) * w.group)]
+        s_orc = oracle.segment_scores(kk, pos, np.concatenate(rows), np.tile(qp, w.group))
+        assert_scores_close(scores[o:o + n].cpu().numpy(), s_orc, what=f"65k segment {seg}")
+        ks = outs["attn"]["kept"][seg * w.budget:(seg + 1) * w.budget].cpu().numpy()
+        ok, _, msg = kept_matches(ks, s_orc, n, w.budget, w.n_prefix, w.n_recent)
+        assert ok, msg
+    # hidden-state score: full series for one request, sampled windows checked exactly
+    b = 2
+    hn = h[:, b].float().cpu().numpy().astype(np.float64)
+    s_orc = oracle.epikv_score(hn[0], hn[1], w.epikv_window, w.epikv_eps)
+    got = epi[b].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - s_orc) <= 2e-3 * np.maximum(1.0, np.abs(s_orc)))
+    ga = oracle.epikv_g(hn[0])
+    assert_scores_close(gser[0, b].cpu().numpy(), ga, rtol=1e-5, floor=1e-6, what="g")
+    for g in (0, 5):
+        seg = b * w.n_kv_heads + g
+        ks = outs["epikv"]["kept"][seg * w.budget:(seg + 1) * w.budget].cpu().numpy()
+        ok, _, msg = kept_matches(ks, s_orc, n, w.budget, w.n_prefix, w.n_recent, floor=2e-3)
+        assert ok, msg

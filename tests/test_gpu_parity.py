@@ -55,11 +55,11 @@ def test_rope_keys_bit_exact(name):
     assert mism == 0, f"{mism} of {got.size} rotated key elements differ"
 
 
-@pytest.mark.parametrize("impl", ["twopass", "fused", "valu"])
+@pytest.mark.parametrize("impl", ["mfma", "fused", "valu"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_scores_match_oracle(name, impl, monkeypatch):
     w, L, D, k_orc, s_orc = _case(name)
-    if impl != "twopass":
+    if impl != "mfma":
         if w.dtype != "bf16":
             pytest.skip("fp32 caches always use the VALU path")
         monkeypatch.setenv("KVE_SCORE_IMPL", impl)
