@@ -232,6 +232,28 @@ class StepRunner:
             main.wait_stream(side)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_compact_qwen3-4b-36l_hbm_traffic.txt")
+DOMINANT_SOURCE = os.path.join(ROOT, "decode_kv_cache_evict_amd", "csrc", "select.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant call, from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (scaled by a plain copy's counts), or None if
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv_pairs = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv_pairs[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(DOMINANT_SOURCE, "rb").read()).hexdigest()
+    if kv_pairs.get("source_sha256") != sha or "traffic_bytes_per_launch" not in kv_pairs:
+        return None
+    return float(kv_pairs["traffic_bytes_per_launch"])
+
+
 def step_bytes(w):
     """Algorithmic HBM bytes of one trigger (every input read once, every output written once)."""
     S = w.n_layers * w.batch * w.n_kv_heads
@@ -385,7 +407,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "kv_evict_select_compact (radix select + gather compaction), "
                                                f"{dom_layers} layer(s) per launch",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dom_bytes,
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic() if dom_layers == w.n_layers else None,
+                     "bytes_per_launch": dom_bytes,
                      "avg_launch_ms": sc_ms},
     }
     # plain device-to-device copy of 2 GiB: the achievable read+write bandwidth reference

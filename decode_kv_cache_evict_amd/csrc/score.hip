@@ -199,6 +199,23 @@ constexpr int kBK = 64;                           // keys per LDS batch
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block -> (segment, chunk) so that the chunks of one segment land on the same
+// XCD (work-groups are handed to the 8 XCDs round-robin by linear block id):
+// they then share that XCD's L2 for the segment's rotated queries.
+__device__ __forceinline__ void xcd_item(const ScoreArgs& a, int& s, int& ch) {
+  const int L = blockIdx.x;
+  const int full = (a.n_seg / 8) * 8;                // segments covered by the XCD-striped part
+  if (L < full * a.n_chunks) {
+    const int x = L % 8, slot = L / 8;
+    s = (slot / a.n_chunks) * 8 + x;
+    ch = slot % a.n_chunks;
+  } else {
+    const int r = L - full * a.n_chunks;
+    s = full + r / a.n_chunks;
+    ch = r % a.n_chunks;
+  }
+}
+
 template <int D, int RT>
 struct WaveRows {
   static constexpr int KS = D / 32;
@@ -327,7 +344,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   __shared__ int rpos_s[kMaxObsRows];
   __shared__ int qoff_s[kMaxObsRows];
 
-  const int s = blockIdx.y, ch = blockIdx.x;
+  int s, ch;
+  xcd_item(a, s, ch);
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) return;
@@ -690,10 +708,11 @@ void launch_merge(const ScoreArgs& a, hipStream_t st) {
 }
 
 template <int D, int RT>
-hipError_t launch_mfma(const ScoreArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_mfma_kernel<D, RT, false>), grid, dim3(256), 0, st, a);
+hipError_t launch_mfma(const ScoreArgs& a, dim3, hipStream_t st) {
+  const dim3 grid1(unsigned(int64_t(a.n_seg) * a.n_chunks));
+  hipLaunchKernelGGL((score_mfma_kernel<D, RT, false>), grid1, dim3(256), 0, st, a);
   launch_merge(a, st);
-  hipLaunchKernelGGL((score_mfma_kernel<D, RT, true>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_mfma_kernel<D, RT, true>), grid1, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
