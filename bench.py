@@ -5,8 +5,10 @@ head_dim 128, bf16, B_max = 4096, evicting 1/8 (to 3584) per trigger, with
 continual FPS of every query head's 32-entry beacon buffer down to 16.  Four
 consecutive trigger states are built up front (512 decoded tokens appended
 between triggers); timed steps cycle through them.  One step = one trigger
-over all 36 layers: kv_evict_score -> kv_evict_select_compact ->
-beacon_fps_update, all on one stream, inputs resident in HBM.
+over all 36 layers: kv_evict_score_select_compact (scoring, protected top-K
+and gather compaction in one kernel) and beacon_fps_update, on one stream,
+inputs resident in HBM.  --call split times the two-call form
+(kv_evict_score, then kv_evict_select_compact) instead.
 
 Prints ONE JSON line.  Metric: scored KV tokens per second (a token is one
 position of one layer of one request, across its 8 KV heads).
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
     ap.add_argument("--graph", type=int, default=0, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    ap.add_argument("--call", choices=["split", "fused"], default="fused",
+                    help="split: kv_evict_score then kv_evict_select_compact; "
+                         "fused: kv_evict_score_select_compact (one kernel per call)")
     return ap.parse_args()
 
 
@@ -170,11 +175,14 @@ class StepRunner:
                covers are scored, and FPS on that stream up front, so the
                memory-bound gather overlaps the MFMA-bound scoring."""
 
-    def __init__(self, w, states, out, scores, kept, fps_out, ws_score, score_group, select_group, schedule):
+    def __init__(self, w, states, out, scores, kept, fps_out, ws_score, score_group, select_group, schedule,
+                 call="split"):
         import torch
         import decode_kv_cache_evict_amd as kv
         self.w, self.states, self.scores, self.kept, self.fps_out = w, states, scores, kept, fps_out
-        self.ws_score, self.schedule = ws_score, schedule
+        self.ws_score, self.schedule, self.call = ws_score, schedule, call
+        if call == "fused":
+            select_group = score_group
         L, B, Hkv = w.n_layers, w.batch, w.n_kv_heads
         select_group = max(select_group, score_group)
         self.sgroups = [(g0, min(L, g0 + score_group)) for g0 in range(0, L, score_group)]
@@ -209,6 +217,19 @@ class StepRunner:
         if side is not main:
             side.wait_stream(main)
         kv.beacon_fps_update(st.buf, self.fps_out[0], st.count, self.fps_out[1], w.fps_keep, stream=side)
+        if self.call == "fused":
+            # one call per layer group: score, select and gather in one kernel;
+            # the output cache (K, V, pos, lengths) is the result, no index list
+            for ci, ((l1, cache, obs), (_, _, cout)) in enumerate(zip(sc, cc)):
+                if timing is not None:
+                    timing[ci][0].record(main)
+                kv.kv_evict_score_select_compact(cache, obs, self.scores, None, w.n_prefix, w.n_recent, cout,
+                                                 uniform_budget=w.budget, ws=self.ws_score, stream=main)
+                if timing is not None:
+                    timing[ci][1].record(main)
+            if side is not main:
+                main.wait_stream(side)
+            return
         ci = 0
 
         def select(ci):
@@ -232,15 +253,28 @@ class StepRunner:
             main.wait_stream(side)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_compact_qwen3-4b-36l_hbm_traffic.txt")
-DOMINANT_SOURCE = os.path.join(ROOT, "decode_kv_cache_evict_amd", "csrc", "select.hip")
+CSRC = os.path.join(ROOT, "decode_kv_cache_evict_amd", "csrc")
+TRAFFIC = {
+    "split": (os.path.join(ROOT, "profiles", "select_compact_qwen3-4b-36l_hbm_traffic.txt"),
+              [os.path.join(CSRC, "select.hip"), os.path.join(CSRC, "select_common.h")]),
+    "fused": (os.path.join(ROOT, "profiles", "score_select_compact_qwen3-4b-36l_hbm_traffic.txt"),
+              [os.path.join(CSRC, "score.hip"), os.path.join(CSRC, "select_common.h")]),
+}
 
 
-def measured_traffic():
+def source_sha(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(call="split"):
     """HBM bytes per launch of the dominant call, from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary (scaled by a plain copy's counts), or None if
-    the kernel source changed since the counters were taken."""
-    import hashlib
+    the kernel sources changed since the counters were taken."""
+    TRAFFIC_FILE, sources = TRAFFIC[call]
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv_pairs = {}
@@ -248,8 +282,7 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv_pairs[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(DOMINANT_SOURCE, "rb").read()).hexdigest()
-    if kv_pairs.get("source_sha256") != sha or "traffic_bytes_per_launch" not in kv_pairs:
+    if kv_pairs.get("source_sha256") != source_sha(sources) or "traffic_bytes_per_launch" not in kv_pairs:
         return None
     return float(kv_pairs["traffic_bytes_per_launch"])
 
@@ -268,8 +301,14 @@ def step_bytes(w):
         "fps": w.n_layers * w.batch * w.n_q_heads * (w.fps_cap + w.fps_keep) * d * 2,
     }
     b["select_compact"] = b["select_scores"] + b["compact_kv"] + b["compact_pos"]
+    # one-kernel trigger: K, pos and queries read once, kept V rows read, the
+    # scores and the output cache (K, V, pos) written
+    b["fused_step"] = (b["score_k"] + b["score_pos"] + b["score_q"] + b["score_out"]
+                       + 3 * S * keep * row + S * keep * 4)
     b["score"] = b["score_k"] + b["score_pos"] + b["score_q"] + b["score_out"]
-    b["total"] = b["score"] + b["select_compact"] + b["fps"]
+    # the step's algorithmic bytes: the one-kernel form's (the split form adds
+    # a write and re-read of the scores and a second read of the kept K rows)
+    b["total"] = b["fused_step"] + b["fps"]
     return b
 
 
@@ -344,10 +383,16 @@ def main():
                        states[0].seg_len[:per_group * w.batch * w.n_kv_heads], w.n_kv_heads, states[0].cap)
     o0 = kv.make_obs(states[0].q[:per_group * w.batch], states[0].q_pos[:per_group * w.batch],
                      states[0].n_obs[:per_group * w.batch], w.rope_theta)
-    ws_score = torch.empty(kv.kv_evict_score_workspace(c0, o0) + 256, dtype=torch.uint8, device=dev)
+    if args.call == "fused":
+        cout0 = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"][:per_group * w.batch * w.n_kv_heads],
+                              out["seg_len"][:per_group * w.batch * w.n_kv_heads], w.n_kv_heads, out["cap"])
+        nws = kv.kv_evict_score_select_compact_workspace(c0, o0, cout0, False)
+    else:
+        nws = kv.kv_evict_score_workspace(c0, o0)
+    ws_score = torch.empty(nws + 256, dtype=torch.uint8, device=dev)
     kept = torch.empty(out["k"].shape[0], dtype=torch.int32, device=dev)
     runner = StepRunner(w, states, out, scores, kept, (fps_buf, fps_cnt), ws_score, per_group, sel_group,
-                        args.schedule)
+                        args.schedule, args.call)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f} s; schedule {args.schedule}, {len(runner.sgroups)} scoring and "
         f"{len(runner.cgroups)} select call(s), "
@@ -385,7 +430,8 @@ def main():
     tokens = w.n_layers * w.batch * w.len_hi
     nb = step_bytes(w)
     dom_layers = runner.cgroups[0][1] - runner.cgroups[0][0]
-    dom_bytes = nb["select_compact"] * dom_layers / w.n_layers
+    dom_key = "fused_step" if args.call == "fused" else "select_compact"
+    dom_bytes = nb[dom_key] * dom_layers / w.n_layers
     achieved = dom_bytes / (sc_ms * 1e-3) / 1e9
     res = {
         "metric": "scored KV tokens/sec (+ % HBM peak), Qwen3-4B shape, B_max=4096, batch 16",
@@ -402,13 +448,17 @@ def main():
                    "global_batch": w.batch, "seq_len": w.len_hi, "parallelism": "single GPU"},
         "step_hbm": {"algorithmic_bytes": nb["total"], "gb_per_s": nb["total"] / (ms * 1e-3) / 1e9,
                      "frac_of_peak": nb["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "schedule": {"kind": args.schedule, "layers_per_score_call": per_group, "layers_per_select_call": sel_group,
+        "schedule": {"kind": args.schedule, "call": args.call, "layers_per_score_call": per_group,
+                     "layers_per_select_call": runner.cgroups[0][1] - runner.cgroups[0][0],
                      "hip_graph": bool(args.graph)},
-        "roofline": {"bound": "hbm", "kernel": "kv_evict_select_compact (radix select + gather compaction), "
-                                               f"{dom_layers} layer(s) per launch",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("kv_evict_score_select_compact (score, radix select and gather in one kernel)"
+                                if args.call == "fused" else
+                                "kv_evict_select_compact (radix select + gather compaction)")
+                     + f", {dom_layers} layer(s) per launch",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": measured_traffic() if dom_layers == w.n_layers else None,
+                     "traffic": measured_traffic(args.call) if dom_layers == w.n_layers else None,
                      "bytes_per_launch": dom_bytes,
                      "avg_launch_ms": sc_ms},
     }

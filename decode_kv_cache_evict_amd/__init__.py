@@ -1,12 +1,12 @@
 """MI355X-native decode-time KV-cache eviction step.
 
 The work runs in libkvevict.so (hand-written HIP for gfx950); this package is
-its Python face: ``_abi`` marshals torch tensors into the C entry points and
-``step`` sequences them for one eviction trigger.
+its Python face: ``_abi`` marshals torch tensors into the C entry points.
 """
 from ._abi import (  # noqa: F401
     KveError, KveCache, KveObs, lib, make_cache, make_obs,
     kv_evict_score_workspace, kv_evict_score, kv_evict_budgets, kv_evict_wave_budgets,
-    kv_evict_select_workspace, kv_evict_select_compact, beacon_fps_update,
+    kv_evict_select_workspace, kv_evict_select_compact, kv_evict_score_select_compact_workspace,
+    kv_evict_score_select_compact, beacon_fps_update,
     epikv_workspace_size, epikv_score, kv_rope_apply, kve_abi_version, EXPORTS, LIB_PATH,
 )

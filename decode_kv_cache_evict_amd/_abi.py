@@ -18,7 +18,8 @@ KVE_BF16, KVE_F32 = 0, 1
 STATUS = {0: "KVE_OK", 1: "KVE_EINVAL", 2: "KVE_ESHAPE", 3: "KVE_EALIAS", 4: "KVE_EBUDGET",
           5: "KVE_EWORKSPACE", 6: "KVE_EDEVICE"}
 EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv_evict_wave_budgets",
-           "kv_evict_select_workspace", "kv_evict_select_compact", "beacon_fps_update",
+           "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_score_select_compact_workspace",
+           "kv_evict_score_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "kv_rope_apply", "kve_last_error", "kve_abi_version"]
 
 
@@ -62,6 +63,8 @@ def lib():
             "kv_evict_wave_budgets": (I32, [I32, D, D, I32, I32, P, P]),
             "kv_evict_select_workspace": (SZ, [CP, I32]),
             "kv_evict_select_compact": (I32, [CP, P, P, I64, P, I32, I32, I32, P, CP, P, SZ, P]),
+            "kv_evict_score_select_compact_workspace": (SZ, [CP, OP, CP, I32]),
+            "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
             "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, P, P, P, SZ, P]),
@@ -179,6 +182,23 @@ def kv_evict_select_compact(cache_in, scores, budget, n_prefix, n_recent, cache_
                                          int(scores.numel()), _ptr(budget), int(uniform_budget), int(n_prefix),
                                          int(n_recent), _ptr(kept_idx), ctypes.byref(cache_out), wp, wn,
                                          _stream(stream)))
+
+
+def kv_evict_score_select_compact_workspace(cache_in, obs, cache_out, have_kept_idx):
+    return int(lib().kv_evict_score_select_compact_workspace(ctypes.byref(cache_in), ctypes.byref(obs),
+                                                             ctypes.byref(cache_out), int(bool(have_kept_idx))))
+
+
+def kv_evict_score_select_compact(cache_in, obs, scores, budget, n_prefix, n_recent, cache_out, kept_idx=None,
+                                  uniform_budget=0, ws=None, stream=None):
+    """One trigger: score, protected top-K and gather in a single call (scores fp32 [n_rows] is written)."""
+    if ws is None:
+        ws = _ws(kv_evict_score_select_compact_workspace(cache_in, obs, cache_out, kept_idx is not None),
+                 scores.device)
+    wp, wn = _aligned(ws)
+    _check(lib().kv_evict_score_select_compact(ctypes.byref(cache_in), ctypes.byref(obs), _ptr(scores), _ptr(budget),
+                                               int(uniform_budget), int(n_prefix), int(n_recent), _ptr(kept_idx),
+                                               ctypes.byref(cache_out), wp, wn, _stream(stream)))
 
 
 def beacon_fps_update(q_in, q_out, count_in, count_out, k_keep, picks=None, stream=None):

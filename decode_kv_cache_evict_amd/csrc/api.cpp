@@ -85,6 +85,38 @@ kve_status check_obs(const kve_cache* c, const kve_obs* o, int32_t* rows) {
   return KVE_OK;
 }
 
+kve::ScoreArgs score_args(const kve_cache* c, const kve_obs* o, int32_t rows, float* scores) {
+  kve::ScoreArgs a{};
+  a.k = c->k;
+  a.pos = c->pos;
+  a.seg_off = c->seg_off;
+  a.seg_len = c->seg_len;
+  a.n_rows = c->n_rows;
+  a.n_seg = c->n_seg;
+  a.n_kv = c->n_kv_heads;
+  a.max_seg_len = c->max_seg_len;
+  a.head_dim = c->head_dim;
+  a.dtype = c->dtype;
+  a.q = o->q;
+  a.q_pos = o->q_pos;
+  a.n_obs = o->n_obs;
+  a.n_q = o->n_q_heads;
+  a.max_obs = o->max_obs;
+  a.group = o->n_q_heads / c->n_kv_heads;
+  a.rows = rows;
+  a.causal = o->causal;
+  a.theta = o->rope_theta;
+  a.scores = scores;
+  return a;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+size_t step_score_ws(const kve_cache* in, const kve_obs* o, int32_t rows) {
+  return round256(kve::score_workspace_bytes(in->n_seg / in->n_kv_heads, o->n_q_heads, o->max_obs, in->head_dim,
+                                             in->dtype, in->n_seg, in->max_seg_len, rows));
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,27 +156,7 @@ kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, f
       overlap(head_entropy, size_t(c->n_seg) * 4, scores, sb))
     return fail(KVE_EALIAS, "an output of kv_evict_score overlaps an input");
   if (c->n_seg == 0) return KVE_OK;
-  kve::ScoreArgs a{};
-  a.k = c->k;
-  a.pos = c->pos;
-  a.seg_off = c->seg_off;
-  a.seg_len = c->seg_len;
-  a.n_rows = c->n_rows;
-  a.n_seg = c->n_seg;
-  a.n_kv = c->n_kv_heads;
-  a.max_seg_len = c->max_seg_len;
-  a.head_dim = c->head_dim;
-  a.dtype = c->dtype;
-  a.q = o->q;
-  a.q_pos = o->q_pos;
-  a.n_obs = o->n_obs;
-  a.n_q = o->n_q_heads;
-  a.max_obs = o->max_obs;
-  a.group = o->n_q_heads / c->n_kv_heads;
-  a.rows = rows;
-  a.causal = o->causal;
-  a.theta = o->rope_theta;
-  a.scores = scores;
+  kve::ScoreArgs a = score_args(c, o, rows, scores);
   a.entropy = head_entropy;
   a.impl = impl;
   return device_status(kve::launch_score(a, ws, static_cast<hipStream_t>(stream)), "kv_evict_score");
@@ -246,6 +258,86 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   a.head_dim = in->head_dim;
   a.elem_bytes = int32_t(elem_bytes(in->dtype));
   return device_status(kve::launch_select_compact(a, static_cast<hipStream_t>(stream)), "kv_evict_select_compact");
+}
+
+size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
+                                               int32_t have_kept_idx) {
+  int32_t rows = 0;
+  if (check_cache(in, "in", true) != KVE_OK || check_obs(in, o, &rows) != KVE_OK || !out || out->n_rows < 0)
+    return 0;
+  return step_score_ws(in, o, rows) + (have_kept_idx ? 0 : size_t(out->n_rows) * sizeof(int32_t));
+}
+
+kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, float* scores,
+                                         const int32_t* budget, int32_t uniform_budget, int32_t n_prefix,
+                                         int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  // every check of both halves runs before anything is launched
+  kve_status st = check_cache(in, "in", true);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(out, "out", true)) != KVE_OK) return st;
+  int32_t rows = 0;
+  if ((st = check_obs(in, o, &rows)) != KVE_OK) return st;
+  if (in->dtype != out->dtype || in->head_dim != out->head_dim || in->n_seg != out->n_seg ||
+      in->n_kv_heads != out->n_kv_heads)
+    return fail(KVE_ESHAPE, "in/out cache shapes differ");
+  if (n_prefix < 0 || n_recent < 0) return fail(KVE_EINVAL, "negative prefix/recent");
+  if (in->n_seg > 0 && !scores) return fail(KVE_EINVAL, "null scores");
+  const bool fused = in->dtype == KVE_BF16 && score_impl() == 0 && in->max_seg_len > 0 &&
+                     in->max_seg_len <= kve::step_max_seg(in->head_dim);
+  const int impl = in->dtype == KVE_BF16 ? score_impl() : 1;
+  if (!fused && impl == 1 && valu_lds(rows, in->head_dim, in->dtype) > 65536)
+    return fail(KVE_ESHAPE, "rows*head_dim too large for the fp32 scoring path");
+  if (!budget) {
+    if (uniform_budget < n_prefix + n_recent)
+      return fail(KVE_EBUDGET, "budget %d below prefix %d + recent %d", uniform_budget, n_prefix, n_recent);
+    const int32_t most = uniform_budget < in->max_seg_len ? uniform_budget : in->max_seg_len;
+    if (most > out->max_seg_len)
+      return fail(KVE_EBUDGET, "budget %d exceeds the output capacity %d", most, out->max_seg_len);
+  }
+  const size_t sw = step_score_ws(in, o, rows);
+  const size_t need = sw + (kept_idx ? 0 : size_t(out->n_rows) * sizeof(int32_t));
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
+  int32_t* kept = kept_idx ? kept_idx : reinterpret_cast<int32_t*>(static_cast<char*>(ws) + sw);
+  const int32_t batch = in->n_seg / in->n_kv_heads;
+  const size_t ns = size_t(in->n_seg);
+  const void* ins[] = {in->k, in->v, in->pos, in->seg_off, in->seg_len, o->q, o->q_pos, o->n_obs, budget,
+                       out->seg_off};
+  const size_t insz[] = {rows_bytes(in), rows_bytes(in), size_t(in->n_rows) * 4, ns * 8, ns * 4,
+                         size_t(batch) * o->n_q_heads * o->max_obs * in->head_dim * elem_bytes(in->dtype),
+                         size_t(batch) * o->max_obs * 4, size_t(batch) * 4, budget ? ns * 4 : 0, ns * 8};
+  const void* outs[] = {scores, out->k, out->v, out->pos, out->seg_len, kept, ws};
+  const size_t outsz[] = {size_t(in->n_rows) * 4, rows_bytes(out), rows_bytes(out), size_t(out->n_rows) * 4,
+                          ns * 4, size_t(out->n_rows) * 4, sw};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
+  if (in->n_seg == 0) return KVE_OK;
+  if (!fused) {
+    if ((st = kv_evict_score(in, o, scores, nullptr, ws, sw, stream)) != KVE_OK) return st;
+    return kv_evict_select_compact(in, scores, nullptr, in->n_rows, budget, uniform_budget, n_prefix, n_recent, kept,
+                                   out, nullptr, 0, stream);
+  }
+  kve::ScoreArgs a = score_args(in, o, rows, scores);
+  a.v = in->v;
+  a.k_out = out->k;
+  a.v_out = out->v;
+  a.pos_out = out->pos;
+  a.out_off = out->seg_off;
+  a.out_len = out->seg_len;
+  a.out_rows = out->n_rows;
+  a.out_cap = out->max_seg_len;
+  a.kept = kept_idx;   // the fused kernel needs no index list of its own
+  a.budget = budget;
+  a.uniform_budget = uniform_budget;
+  a.n_prefix = n_prefix;
+  a.n_recent = n_recent;
+  return device_status(kve::launch_score_select_compact(a, ws, static_cast<hipStream_t>(stream)),
+                       "kv_evict_score_select_compact");
 }
 
 kve_status beacon_fps_update(const void* q_in, void* q_out, const int32_t* count_in, int32_t* count_out, int32_t n_buf,

@@ -34,7 +34,19 @@ struct ScoreArgs {
   int32_t n_chunks;
   int32_t chunk;          // keys per work-group
   int32_t impl;           // 0: two-pass MFMA, 1: plain VALU, 2: single-read MFMA
+  // fused score -> select -> compact (kv_evict_score_select_compact) only
+  const void* v;
+  void* k_out; void* v_out; int32_t* pos_out;
+  const int64_t* out_off; int32_t* out_len; int64_t out_rows; int32_t out_cap;
+  int32_t* kept;          // optional, aligned with output rows
+  const int32_t* budget;  // [n_seg] or null
+  int32_t uniform_budget, n_prefix, n_recent;
 };
+
+// Largest segment the fused step can select on chip: its order keys reuse the
+// two 64-key tiles of padded bf16 rows (64 * (D + 8) 32-bit words).
+constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 8); }
+hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
 
 size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
                              int32_t n_seg, int32_t max_seg_len, int32_t rows);

@@ -9,9 +9,11 @@
 // key tiles staged through LDS by coalesced 16-byte loads; a plain VALU path
 // serves fp32 caches.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 namespace kve {
 
@@ -220,7 +222,6 @@ template <int D, int RT>
 struct WaveRows {
   static constexpr int KS = D / 32;
   bf16x8 qa[RT][KS];
-  int rowpos[RT][4];
   int minpos;
 
   // rpos/qoff: per-row position and row index into the rotated queries (-1: absent), in LDS.
@@ -240,7 +241,6 @@ struct WaveRows {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rp = rpos[16 * t + 4 * quad + i];
-        rowpos[rt][i] = rp;
         if (rp >= 0) minpos = min(minpos, rp);
       }
     }
@@ -269,14 +269,18 @@ struct WaveRows {
     }
   }
 
-  __device__ __forceinline__ void mask2(f32x4 (&acc)[2][RT], const int (&kpos)[2]) const {
+  // Causal mask for the rare tiles holding keys newer than some row (row positions from LDS).
+  __device__ __forceinline__ void mask2(f32x4 (&acc)[2][RT], const int (&kpos)[2], const int* rpos, int w,
+                                        int quad) const {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int i = 0; i < 4; ++i) {
+        const int rp = rpos[16 * (w * RT + rt) + 4 * quad + i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kpos[j] > rowpos[rt][i]) acc[j][rt][i] = -kInf;
+        for (int j = 0; j < 2; ++j)
+          if (kpos[j] > rp) acc[j][rt][i] = -kInf;
+      }
   }
 };
 
@@ -331,146 +335,23 @@ __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float 
   }
 }
 
-template <int D, int RT, bool PASS2>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_mfma_kernel(ScoreArgs a) {
-  constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
-  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int KPU = 256 / CPR;             // keys covered by one 16-byte load per thread
-  constexpr int CPT = kBK / KPU;             // loads per thread per batch
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kBK * LS];
-  __shared__ int kps[2][kBK];
-  __shared__ float red[2][4][kBK];
-  __shared__ float lse_s[kMaxObsRows];
-  __shared__ int rpos_s[kMaxObsRows];
-  __shared__ int qoff_s[kMaxObsRows];
-
-  int s, ch;
-  xcd_item(a, s, ch);
-  int64_t off;
-  int n;
-  if (!segment_ok(a, s, off, n)) return;
-  const int k0 = ch * kMfmaChunk;
-  if (k0 >= n) return;
-  const int k1 = min(n, k0 + kMfmaChunk);
-  const int b = s / a.n_kv, g = s % a.n_kv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, quad = lane >> 4;
-  const float c = kLog2e / sqrtf(float(D));
-
-  // per-row metadata, once per work-group
-  for (int r = tid; r < 16 * 4 * RT; r += 256) {
-    const int rp = row_position(a, b, r);
-    rpos_s[r] = rp;
-    qoff_s[r] = rp >= 0 ? int(row_qr_index(a, b, g, r)) : -1;
-    if (PASS2) lse_s[r] = rp >= 0 ? a.lse[int64_t(s) * a.rows + r] : kInf;
-  }
-  __syncthreads();
-  WaveRows<D, RT> rows;
-  rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
-  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse (log2 units)
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st0[rt][i] = PASS2 ? lse_s[16 * (w * RT + rt) + 4 * quad + i] : kNegBig;
-      st1[rt][i] = 0.f;
-    }
-
-  // thread's share of a batch: keys key0 + u*KPU (u < CPT), 16-byte chunk `part`
-  const int key0 = tid / CPR, part = tid % CPR;
-  const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
-  uint4 pre[CPT];
-  int prepos = INT_MAX;
-  auto load_batch = [&](int kb) {          // kb: batch start relative to k0
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const bool ok = k0 + kb + key0 + u * KPU < k1;
-      pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(kb + u * KPU) * D) : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < kBK) prepos = (k0 + kb + tid < k1) ? a.pos[off + k0 + kb + tid] : INT_MAX;
-  };
-  auto store_batch = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[buf][(key0 + u * KPU) * LS + part * 8]) = pre[u];
-    if (tid < kBK) kps[buf][tid] = prepos;
-  };
-  auto finish_keys = [&](int bi, int kb) {  // pass 2: per-key max over the 4 waves -> score
-    const int j = k0 + kb + tid;
-    if (tid < kBK && j < k1) {
-      const float m = fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid]));
-      a.scores[off + j] = fast_exp2(m);
-    }
-  };
-
-  const int span = k1 - k0;
-  load_batch(0);
-  store_batch(0);
-  if (kBK < span) load_batch(kBK);
-  __syncthreads();
-  int cur = 0;
-  for (int kb = 0; kb < span; kb += kBK) {
-    int kpos[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[cur][q4 * 16 + col];
-    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
-                      kpos[3] > rows.minpos;
-    const bool any_late = __any(late);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 acc[2][RT];
-      rows.template logits2<LS>(acc, kt[cur], 2 * h, col, quad);
-      if (any_late) {
-        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
-        rows.mask2(acc, kp2);
-      }
-      if (!PASS2) stats_update<RT>(st0, st1, acc, c);
-      else key_max2<RT>(acc, st0, c, red[cur][w], 2 * h, col, quad);
-    }
-    if (kb + kBK < span) store_batch(cur ^ 1);
-    if (kb + 2 * kBK < span) load_batch(kb + 2 * kBK);
-    if (PASS2 && kb > 0) finish_keys(cur ^ 1, kb - kBK);
-    __syncthreads();
-    cur ^= 1;
-  }
-  if (PASS2) {
-    finish_keys(cur ^ 1, ((span - 1) / kBK) * kBK);
-    return;
-  }
-  // combine the 16 key columns held by each lane group, then publish
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mm = st0[rt][i], ll = st1[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
-        const float M = fmaxf(mm, m2);
-        ll = ll * fast_exp2((mm - M) * c) + l2 * fast_exp2((m2 - M) * c);
-        mm = M;
-      }
-      const int r = 16 * (w * RT + rt) + 4 * quad + i;
-      if (col == 0 && r < a.rows) a.stats[(int64_t(s) * a.n_chunks + ch) * a.rows + r] = make_float2(mm * c, ll);
-    }
-}
-
-// Single-read variant: one work-group per (segment, 256-key chunk).  The
-// chunk's keys stay in LDS for both passes; between the passes the work-groups
-// of a segment exchange their row statistics through coherent (agent-scope)
-// atomic stores and loads and meet at a per-segment arrival counter, so K is
-// read from HBM once.
+// Single-read variant (MODE 2): the chunk's two passes run in one work-group.
+// Between them the work-groups of a segment exchange their row statistics
+// through coherent (agent-scope) atomic stores and loads and meet at a
+// per-segment arrival counter; pass 2 then re-reads the chunk it has just read,
+// which the memory-side cache still holds, so K crosses HBM once.
 //
-// Work assignment: eight ticket queues, queue q holding the chunks of the
-// segments s = q (mod 8).  A work-group takes a ticket from the queue of the
-// XCD it runs on (so a segment's chunks share one L2 and its queries are
-// fetched once) and steals from the other queues when its own is empty.
-// Deadlock-free: a ticket is only taken by a running work-group, so every
-// chunk of a segment but those of the newest segment in a queue is held by a
-// running or finished work-group, and missing chunks are taken as soon as any
-// older work-group finishes.  The wait is bounded (kSpinLimit polls).
-constexpr int kFusedChunk = 256;
+// Work assignment in that mode: eight ticket queues, queue q holding the chunks
+// of the segments s = q (mod 8).  A work-group takes a ticket from the queue of
+// the XCD it runs on (a segment's chunks then share one L2) and steals from the
+// other queues when its own is empty.  Deadlock-free: a ticket is only taken by
+// a running work-group, so every chunk of a segment but those of the newest
+// segment in a queue is held by a running or finished work-group, and missing
+// chunks are taken as soon as any older work-group finishes.  The wait is
+// bounded (kSpinLimit polls).
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kQueues = 8;
+constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3;
 
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
@@ -487,16 +368,133 @@ __device__ __forceinline__ float2 load_stat(const float2* p) {
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-template <int D, int RT>
-__global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __restrict__ ctl) {
-  constexpr int LS = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int KPU = 256 / CPR;
-  constexpr int CPT = kBK / KPU;
-  constexpr int NB = kFusedChunk / kBK;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[NB][kBK * LS];
-  __shared__ int kps[NB][kBK];
-  __shared__ float red[4][kBK];
+// Ticket from the XCD-local queue, else from any other; -1 when all are empty.
+__device__ __forceinline__ int take_ticket(const ScoreArgs& a, int* ctl) {
+  const unsigned x = xcc_id();
+  for (int k = 0; k < kQueues; ++k) {
+    const int q = int((x + k) & (kQueues - 1));
+    const int nq = (q < a.n_seg ? (a.n_seg - q + kQueues - 1) / kQueues : 0) * a.n_chunks;
+    if (nq == 0 || __hip_atomic_load(&ctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nq) continue;
+    const int t = atomicAdd(&ctl[q], 1);
+    if (t < nq) return (t / a.n_chunks * kQueues + q) * a.n_chunks + t % a.n_chunks;
+  }
+  return -1;
+}
+
+// One-kernel trigger (kv_evict_score_select_compact): each work-group scores
+// its chunk with the single-read scheme above, stores the chunk's scores with
+// coherent stores and meets the segment's other work-groups at a second arrival
+// counter.  Every work-group of the segment then finds the same protected top-K
+// threshold (radix select over the segment's scores, copied to LDS) and gathers
+// its own chunk's kept rows to their places in the output segment.
+// keys: LDS scratch of step_max_seg(D) words.
+template <int D>
+__device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
+                                                    uint32_t* keys, int tid) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;             // rows per pass
+  constexpr int UNR = 4;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int wtot[4];
+  __shared__ int mine[kMfmaChunk];           // this chunk's kept slots, ascending
+  const int64_t oo = a.out_off[s];
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
+  const bool bud_ok = K >= n || (K >= P + R && K >= 0);
+  const int keep_n = K >= n ? n : K;
+  const bool first = k0 == 0;
+  if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D)) {
+    if (first && tid == 0) a.out_len[s] = -1;
+    return;
+  }
+  int base = 0, cnt = 0;                     // output row of this chunk's first kept slot; kept count
+  if (K >= n) {
+    for (int j = k0 + tid; j < k1; j += 256) mine[j - k0] = j;
+    base = k0;
+    cnt = k1 - k0;
+  } else {
+    for (int j = tid; j < n; j += 256)
+      keys[j] = float_order_key(
+          __hip_atomic_load(&a.scores[off + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    uint32_t T, kk;
+    radix_threshold<256>([&](int j) { return keys[j]; }, P, n, R, K - P - R, hist, sh, T, kk);
+    // kept slots and threshold ties before this chunk
+    int eq_b = 0, gt_b = 0;
+    for (int j = P + tid; j < min(k0, n - R); j += 256) {
+      eq_b += keys[j] == T;
+      gt_b += keys[j] > T;
+    }
+    eq_b = block_sum<256>(eq_b, wtot);
+    gt_b = block_sum<256>(gt_b, wtot);
+    const int prot_b = min(k0, P) + max(0, k0 - (n - R));
+    base = prot_b + gt_b + min(eq_b, int(kk));
+    int eq_seen = eq_b;
+    for (int j0 = k0; j0 < k1; j0 += 256) {
+      const int j = j0 + tid;
+      const bool in = j < k1;
+      const bool cand = in && j >= P && j < n - R;
+      const uint32_t key = cand ? keys[j] : 0u;
+      const bool eq = cand && key == T;
+      int eq_tot;
+      const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
+      const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
+      int keep_tot;
+      const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
+      if (keep) mine[at] = j;
+      cnt += keep_tot;
+      eq_seen += eq_tot;
+    }
+  }
+  if (first && tid == 0) a.out_len[s] = keep_n;
+  __syncthreads();
+  // gather: 16-byte chunks, UNR rows per thread in flight
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* kin = static_cast<const u32x4*>(a.k);
+  const u32x4* vin = static_cast<const u32x4*>(a.v);
+  u32x4* kout = static_cast<u32x4*>(a.k_out);
+  u32x4* vout = static_cast<u32x4*>(a.v_out);
+  const int part = tid % CPR, rsub = tid / CPR;
+  for (int r0 = 0; r0 < cnt; r0 += RPP * UNR) {
+    u32x4 kb[UNR], vb[UNR];
+    int src[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * RPP + rsub;
+      src[u] = r < cnt ? mine[r] : -1;
+      if (src[u] >= 0) {
+        kb[u] = kin[(off + src[u]) * CPR + part];
+        vb[u] = __builtin_nontemporal_load(&vin[(off + src[u]) * CPR + part]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * RPP + rsub;
+      if (src[u] >= 0) {
+        const int64_t dst = oo + base + r;
+        __builtin_nontemporal_store(kb[u], &kout[dst * CPR + part]);
+        __builtin_nontemporal_store(vb[u], &vout[dst * CPR + part]);
+        if (part == 0) {
+          a.pos_out[dst] = a.pos[off + src[u]];
+          if (a.kept) a.kept[dst] = src[u];
+        }
+      }
+    }
+  }
+}
+
+template <int D, int RT, int MODE>
+__device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
+  constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int KPU = 256 / CPR;             // keys covered by one 16-byte load per thread
+  constexpr int CPT = kBK / KPU;             // loads per thread per batch
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kBK * LS];
+  static_assert(sizeof(kt) == 4 * step_max_seg(D), "selection keys reuse the key tiles");
+  __shared__ int kps[2][kBK];
+  __shared__ float red[2][4][kBK];
   __shared__ float lse_s[kMaxObsRows];
   __shared__ int rpos_s[kMaxObsRows];
   __shared__ int qoff_s[kMaxObsRows];
@@ -504,94 +502,123 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
-  if (tid == 0) {
-    const unsigned x = xcc_id();
-    int item = -1;
-    for (int k = 0; k < kQueues && item < 0; ++k) {
-      const int q = int((x + k) & (kQueues - 1));
-      const int nq = (q < a.n_seg ? (a.n_seg - q + kQueues - 1) / kQueues : 0) * a.n_chunks;
-      if (nq == 0 || __hip_atomic_load(&ctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nq) continue;
-      const int t = atomicAdd(&ctl[q], 1);
-      if (t < nq) item = (t / a.n_chunks * kQueues + q) * a.n_chunks + t % a.n_chunks;
-    }
-    sh_item = item;
+  int s, ch;
+  if (MODE >= kModeFused) {
+    if (tid == 0) sh_item = take_ticket(a, ctl);
+    __syncthreads();
+    const int item = sh_item;
+    if (item < 0) return;
+    s = item / a.n_chunks;
+    ch = item % a.n_chunks;
+  } else {
+    xcd_item(a, s, ch);
   }
-  __syncthreads();
-  const int item = sh_item;
-  if (item < 0) return;
-  const int s = item / a.n_chunks, ch = item % a.n_chunks;
   int64_t off;
   int n;
-  if (!segment_ok(a, s, off, n)) return;
-  const int k0 = ch * kFusedChunk;
-  if (k0 >= n) return;
-  const int k1 = min(n, k0 + kFusedChunk);
-  const int nch = (n + kFusedChunk - 1) / kFusedChunk;
+  if (!segment_ok(a, s, off, n)) {
+    if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
+    return;
+  }
+  const int k0 = ch * kMfmaChunk;
+  if (k0 >= n) {
+    if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
+    return;
+  }
+  const int k1 = min(n, k0 + kMfmaChunk);
+  const int nch = (n + kMfmaChunk - 1) / kMfmaChunk;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
 
+  // per-row metadata, once per work-group
   for (int r = tid; r < 16 * 4 * RT; r += 256) {
     const int rp = row_position(a, b, r);
     rpos_s[r] = rp;
     qoff_s[r] = rp >= 0 ? int(row_qr_index(a, b, g, r)) : -1;
+    if (MODE == kModePass2) lse_s[r] = rp >= 0 ? a.lse[int64_t(s) * a.rows + r] : kInf;
   }
   __syncthreads();
   WaveRows<D, RT> rows;
   rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
-  float st0[RT][4], st1[RT][4];
+  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse (log2 units)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st0[rt][i] = kNegBig;
+      st0[rt][i] = MODE == kModePass2 ? lse_s[16 * (w * RT + rt) + 4 * quad + i] : kNegBig;
       st1[rt][i] = 0.f;
     }
 
+  // thread's share of a batch: keys key0 + u*KPU (u < CPT), 16-byte chunk `part`
   const int key0 = tid / CPR, part = tid % CPR;
   const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
-  uint4 pre[CPT];
-  int prepos = INT_MAX;
-  auto load_batch = [&](int bi) {
+  const int span = k1 - k0;
+
+  // One sweep over the chunk: pass 1 updates (st0, st1); pass 2 writes scores.
+  auto sweep = [&](auto pass2_tag) {
+    constexpr bool P2 = decltype(pass2_tag)::value;
+    uint4 pre[CPT];
+    int prepos = INT_MAX;
+    auto load_batch = [&](int kb) {        // kb: batch start relative to k0
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const bool ok = k0 + bi * kBK + key0 + u * KPU < k1;
-      pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(bi * kBK + u * KPU) * D) : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < CPT; ++u) {
+        const bool ok = k0 + kb + key0 + u * KPU < k1;
+        pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(kb + u * KPU) * D) : make_uint4(0, 0, 0, 0);
+      }
+      if (tid < kBK) prepos = (k0 + kb + tid < k1) ? a.pos[off + k0 + kb + tid] : INT_MAX;
+    };
+    auto store_batch = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[buf][(key0 + u * KPU) * LS + part * 8]) = pre[u];
+      if (tid < kBK) kps[buf][tid] = prepos;
+    };
+    auto finish_keys = [&](int bi, int kb) {  // per-key max over the 4 waves -> score
+      const int j = k0 + kb + tid;
+      if (tid < kBK && j < k1) {
+        const float m = fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid]));
+        if (MODE == kModeStep)   // read back by the segment's other work-groups: coherent store
+          __hip_atomic_store(&a.scores[off + j], fast_exp2(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          a.scores[off + j] = fast_exp2(m);
+      }
+    };
+    load_batch(0);
+    store_batch(0);
+    if (kBK < span) load_batch(kBK);
+    __syncthreads();
+    int cur = 0;
+    for (int kb = 0; kb < span; kb += kBK) {
+      int kpos[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[cur][q4 * 16 + col];
+      const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
+                        kpos[3] > rows.minpos;
+      const bool any_late = __any(late);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc[2][RT];
+        rows.template logits2<LS>(acc, kt[cur], 2 * h, col, quad);
+        if (any_late) {
+          const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
+          rows.mask2(acc, kp2, rpos_s, w, quad);
+        }
+        if (!P2) stats_update<RT>(st0, st1, acc, c);
+        else key_max2<RT>(acc, st0, c, red[cur][w], 2 * h, col, quad);
+      }
+      if (kb + kBK < span) store_batch(cur ^ 1);
+      if (kb + 2 * kBK < span) load_batch(kb + 2 * kBK);
+      if (P2 && kb > 0) finish_keys(cur ^ 1, kb - kBK);
+      __syncthreads();
+      cur ^= 1;
     }
-    if (tid < kBK) prepos = (k0 + bi * kBK + tid < k1) ? a.pos[off + k0 + bi * kBK + tid] : INT_MAX;
-  };
-  auto store_batch = [&](int bi) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[bi][(key0 + u * KPU) * LS + part * 8]) = pre[u];
-    if (tid < kBK) kps[bi][tid] = prepos;
+    if (P2) finish_keys(cur ^ 1, ((span - 1) / kBK) * kBK);
   };
 
-  const int nb = (k1 - k0 + kBK - 1) / kBK;
-  load_batch(0);
-  store_batch(0);
-  if (nb > 1) load_batch(1);
-  __syncthreads();
-  for (int bi = 0; bi < nb; ++bi) {
-    int kpos[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[bi][q4 * 16 + col];
-    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
-                      kpos[3] > rows.minpos;
-    const bool any_late = __any(late);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 acc[2][RT];
-      rows.template logits2<LS>(acc, kt[bi], 2 * h, col, quad);
-      if (any_late) {
-        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
-        rows.mask2(acc, kp2);
-      }
-      stats_update<RT>(st0, st1, acc, c);
-    }
-    if (bi + 1 < nb) store_batch(bi + 1);
-    if (bi + 2 < nb) load_batch(bi + 2);
-    __syncthreads();
+  if (MODE == kModePass2) {
+    sweep(std::integral_constant<bool, true>{});
+    return;
   }
-  // publish this chunk's row statistics (coherent stores), then wait for the segment
+  sweep(std::integral_constant<bool, false>{});
+  // combine the 16 key columns held by each lane group, then publish
   float2* stats_seg = a.stats + int64_t(s) * a.n_chunks * a.rows;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -606,8 +633,14 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
         mm = M;
       }
       const int r = 16 * (w * RT + rt) + 4 * quad + i;
-      if (col == 0 && r < a.rows) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm * c, ll));
+      if (col == 0 && r < a.rows) {
+        if (MODE >= kModeFused) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm * c, ll));
+        else stats_seg[int64_t(ch) * a.rows + r] = make_float2(mm * c, ll);
+      }
     }
+  if (MODE < kModeFused) return;
+
+  // segment barrier: the stores above are acknowledged before the arrival count
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -622,10 +655,17 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
     float lse = kInf;
     if (r < a.rows && rpos_s[r] >= 0) {
       float M = kNegBig, L = 0.f;
-      for (int q = 0; q < nch; ++q) {
-        const float2 v = load_stat(&stats_seg[int64_t(q) * a.rows + r]);
-        const float Mn = fmaxf(M, v.x);
-        L = L * fast_exp2(M - Mn) + v.y * fast_exp2(v.x - Mn);
+      for (int q0 = 0; q0 < nch; q0 += 8) {          // 8 independent loads in flight per pass
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = q0 + u < nch ? load_stat(&stats_seg[int64_t(q0 + u) * a.rows + r]) : make_float2(kNegBig, 0.f);
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, v[u].x);
+        L *= fast_exp2(M - Mn);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) L += v[u].y * fast_exp2(v[u].x - Mn);
         M = Mn;
       }
       lse = L > 0.f ? M + log2f(L) : kInf;
@@ -637,31 +677,43 @@ __global__ __launch_bounds__(256) void score_fused_kernel(ScoreArgs a, int* __re
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
-  for (int bi = 0; bi < nb; ++bi) {
-    int kpos[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[bi][q4 * 16 + col];
-    const bool late = kpos[0] > rows.minpos || kpos[1] > rows.minpos || kpos[2] > rows.minpos ||
-                      kpos[3] > rows.minpos;
-    const bool any_late = __any(late);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 acc[2][RT];
-      rows.template logits2<LS>(acc, kt[bi], 2 * h, col, quad);
-      if (any_late) {
-        const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
-        rows.mask2(acc, kp2);
-      }
-      key_max2<RT>(acc, st0, c, red[w], 2 * h, col, quad);
-    }
-    __syncthreads();
-    const int j = k0 + bi * kBK + tid;
-    if (tid < kBK && j < k1) {
-      const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-      a.scores[off + j] = fast_exp2(m);
-    }
-    __syncthreads();
+  sweep(std::integral_constant<bool, true>{});
+  if (MODE != kModeStep) return;
+
+  // second segment barrier: every chunk's scores are stored
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    int* arrive = ctl + kQueues + a.n_seg + s;
+    atomicAdd(arrive, 1);
+    int spins = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
+      __builtin_amdgcn_s_sleep(1);
   }
+  __syncthreads();
+  step_select_compact<D>(a, s, off, n, k0, k1, reinterpret_cast<uint32_t*>(&kt[0][0]), tid);
+}
+
+// Pass 1 and the single-read kernel carry the row statistics in registers; all
+// three fit 3 waves per SIMD.
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_pass1_kernel(ScoreArgs a) {
+  score_mfma_body<D, RT, kModePass1>(a, nullptr);
+}
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_pass2_kernel(ScoreArgs a) {
+  score_mfma_body<D, RT, kModePass2>(a, nullptr);
+}
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_fused_kernel(ScoreArgs a,
+                                                                                                    int* ctl) {
+  score_mfma_body<D, RT, kModeFused>(a, ctl);
+}
+
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_step_kernel(ScoreArgs a,
+                                                                                                   int* ctl) {
+  score_mfma_body<D, RT, kModeStep>(a, ctl);
 }
 
 // Zero a small int array (queue tickets and arrival counters) with a kernel, so
@@ -710,9 +762,9 @@ void launch_merge(const ScoreArgs& a, hipStream_t st) {
 template <int D, int RT>
 hipError_t launch_mfma(const ScoreArgs& a, dim3, hipStream_t st) {
   const dim3 grid1(unsigned(int64_t(a.n_seg) * a.n_chunks));
-  hipLaunchKernelGGL((score_mfma_kernel<D, RT, false>), grid1, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_pass1_kernel<D, RT>), grid1, dim3(256), 0, st, a);
   launch_merge(a, st);
-  hipLaunchKernelGGL((score_mfma_kernel<D, RT, true>), grid1, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_pass2_kernel<D, RT>), grid1, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -748,6 +800,15 @@ hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
   }
 }
 
+template <int D, int RT>
+hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
+  const int n_ctl = kQueues + 2 * a.n_seg;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
+  const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
+  hipLaunchKernelGGL((score_step_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const size_t sh = size_t(a.rows) * D * sizeof(T) + size_t(a.rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
@@ -768,7 +829,7 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
   const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
-  const size_t ct = align_up(size_t(n_seg + kQueues) * sizeof(int));
+  const size_t ct = align_up(size_t(2 * n_seg + kQueues) * sizeof(int));
   return qr + st + ls + ct;
 }
 
@@ -776,14 +837,15 @@ size_t valu_lds_bytes(int rows, int D, int dtype) {
   return size_t(rows) * D * (dtype == 0 ? 2 : 4) + size_t(rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
 }
 
-hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
+namespace {
+
+// Carve the workspace and rotate the observation queries; returns the control
+// counters' address.
+int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   const int batch = a.n_seg / a.n_kv;
   const size_t elem = a.dtype == 0 ? 2 : 4;
-  const bool mfma = a.dtype == 0 && a.impl == 0;
-  const bool fused = a.dtype == 0 && a.impl == 2;
-  a.chunk = fused ? kFusedChunk : (mfma ? kMfmaChunk : kScoreChunk);
-  a.n_chunks = (a.max_seg_len + a.chunk - 1) / a.chunk;
   const size_t nch256 = (size_t(a.max_seg_len) + kScoreChunk - 1) / kScoreChunk;
+  a.n_chunks = (a.max_seg_len + a.chunk - 1) / a.chunk;
   char* w = static_cast<char*>(ws);
   a.qr = w;
   w += align_up(size_t(batch) * a.n_q * a.max_obs * a.head_dim * elem);
@@ -803,7 +865,29 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
                          a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, a.theta);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  return ctl;
+}
+
+template <int D>
+hipError_t launch_step(const ScoreArgs& a, int* ctl, hipStream_t st) {
+  const int rt = ((a.rows + 15) / 16 + 3) / 4;
+  switch (rt) {
+    case 1: return launch_step_t<D, 1>(a, ctl, st);
+    case 2: return launch_step_t<D, 2>(a, ctl, st);
+    case 3: return launch_step_t<D, 3>(a, ctl, st);
+    default: return launch_step_t<D, 4>(a, ctl, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
+  const bool mfma = a.dtype == 0 && a.impl == 0;
+  const bool fused = a.dtype == 0 && a.impl == 2;
+  a.chunk = (fused || mfma) ? kMfmaChunk : kScoreChunk;
+  hipError_t e;
+  int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
@@ -822,6 +906,15 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
+  a.chunk = kMfmaChunk;
+  hipError_t e;
+  int* ctl = prepare(a, ws, st, e);
+  if (e != hipSuccess) return e;
+  if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
+  return a.head_dim == 128 ? launch_step<128>(a, ctl, st) : launch_step<64>(a, ctl, st);
 }
 
 }  // namespace kve

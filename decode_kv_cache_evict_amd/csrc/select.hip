@@ -12,6 +12,7 @@
 // 16-byte loads and stores, and their positions.
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 namespace kve {
 
@@ -20,30 +21,9 @@ namespace {
 constexpr int kSelBlock = 512;
 constexpr int kSelWaves = kSelBlock / kWave;
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
-
-// Exclusive block scan of a 0/1 flag; returns this thread's prefix and writes the total.
-__device__ __forceinline__ int block_flag_scan(bool f, int* wtot, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint64_t m = __ballot(f);
-  const int in_wave = __popcll(m & lanemask_lt(lane));
-  if (lane == 0) wtot[w] = __popcll(m);
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int q = 0; q < kSelWaves; ++q) {
-    const int t = wtot[q];
-    before += q < w ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + in_wave;
-}
-
 __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_kk;
+  __shared__ uint32_t sh[2];
   __shared__ int wtot_a[kSelWaves], wtot_b[kSelWaves];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -69,74 +49,21 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
     return;
   }
   const float* sc = a.scores + so;
-  const int kc = K - P - R;                 // candidates to take from [P, n-R)
-  uint32_t prefix = 0, mask = 0;
-  uint32_t kk = uint32_t(kc);
-  if (kc == 0) {
-    prefix = 0xFFFFFFFFu;                   // nothing exceeds it, nothing ties into it
-  } else {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int d = tid; d < 256; d += kSelBlock) hist[d] = 0;
-      __syncthreads();
-      for (int j = P + tid; j < n - R; j += kSelBlock) {
-        const uint32_t key = float_order_key(sc[j]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns digits 255-4l .. 252-4l (descending)
-        uint32_t h[4], loc = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[i] = hist[255 - 4 * tid - i];
-          loc += h[i];
-        }
-        uint32_t incl = loc;                // inclusive scan over lanes, high digits first
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t v = __shfl_up(incl, o, kWave);
-          if (tid >= o) incl += v;
-        }
-        const uint32_t excl = incl - loc;
-        const uint64_t hit = __ballot(incl >= kk);
-        const int first = __ffsll((unsigned long long)hit) - 1;
-        if (tid == first) {
-          uint32_t cum = excl;
-          int digit = 0;
-          uint32_t above = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (cum + h[i] >= kk) {
-              digit = 255 - 4 * tid - i;
-              above = cum;
-              break;
-            }
-            cum += h[i];
-          }
-          sh_prefix = prefix | (uint32_t(digit) << shift);
-          sh_kk = kk - above;
-        }
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      kk = sh_kk;
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-  }
-  // prefix = threshold key T; kk = how many candidates equal to T are kept.
+  uint32_t T, kk;
+  radix_threshold<kSelBlock>([&](int j) { return float_order_key(sc[j]); }, P, n, R, K - P - R, hist, sh, T, kk);
+  // kept = protected, keys above T, and the first kk candidates equal to T
   int base = 0, eq_seen = 0;
   for (int j0 = 0; j0 < n; j0 += kSelBlock) {
     const int j = j0 + tid;
     const bool in = j < n;
     const bool cand = in && j >= P && j < n - R;
     const uint32_t key = cand ? float_order_key(sc[j]) : 0u;
-    const bool eq = cand && key == prefix;
+    const bool eq = cand && key == T;
     int eq_tot;
-    const int eq_rank = eq_seen + block_flag_scan(eq, wtot_a, eq_tot);
-    const bool keep = in && (!cand || key > prefix || (eq && uint32_t(eq_rank) < kk));
+    const int eq_rank = eq_seen + block_flag_scan<kSelBlock>(eq, wtot_a, eq_tot);
+    const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
     int keep_tot;
-    const int at = base + block_flag_scan(keep, wtot_b, keep_tot);
+    const int at = base + block_flag_scan<kSelBlock>(keep, wtot_b, keep_tot);
     if (keep && at < K) a.kept[oo + at] = j;
     base += keep_tot;
     eq_seen += eq_tot;

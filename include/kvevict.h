@@ -160,6 +160,34 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
                                    int32_t n_prefix, int32_t n_recent, int32_t* kept_idx,
                                    kve_cache* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes kv_evict_score_select_compact needs. */
+size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
+                                               int32_t have_kept_idx);
+
+/*
+ * kv_evict_score_select_compact — one eviction trigger of BeaconKV ("打分时的
+ * RoPE 对齐" for the score, "📊 实验" for dropping the evicted rows): the
+ * result of kv_evict_score(in, o, scores, NULL) followed by
+ * kv_evict_select_compact(in, scores, NULL, in->n_rows, budget, ...), with the
+ * same meaning of every argument.  For bf16 caches whose max_seg_len fits the
+ * on-chip selection (8704 rows at head_dim 128, 4608 at 64) it runs as one
+ * kernel: each segment's work-groups score their chunk, wait for the segment's
+ * other chunks, select, and gather their own chunk's kept rows while those are
+ * still in cache; otherwise it makes the two calls.  scores ([in->n_rows] fp32)
+ * is written as by kv_evict_score.  Budgets must be known before the call
+ * (uniform, or a device array from an earlier step); the per-head entropy that
+ * ReasonAlloc's reallocation needs comes from kv_evict_score.  Ties between
+ * near-equal scores may resolve differently from the two-call form, since the
+ * softmax normaliser is summed in another order (scores agree to fp32 rounding).
+ * Errors: the union of kv_evict_score's and kv_evict_select_compact's; scores,
+ * the output cache, kept_idx and the workspace must not overlap any input or
+ * each other (EALIAS).
+ */
+kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, float* scores,
+                                         const int32_t* budget, int32_t uniform_budget, int32_t n_prefix,
+                                         int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
+                                         size_t ws_bytes, void* stream);
+
 /*
  * beacon_fps_update — BeaconKV "Continual FPS": for each of n_buf buffers of
  * pre-RoPE queries ([n_buf, cap, head_dim], dtype) whose count_in equals cap, run

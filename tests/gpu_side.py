@@ -54,3 +54,12 @@ def select_compact(D, w, scores, out, budget=None, uniform=0, score_off=None):
     cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, out["cap"])
     kv.kv_evict_select_compact(cin, scores, budget, w.n_prefix, w.n_recent, cout, kept_idx=out["kept"],
                                score_off=score_off, uniform_budget=uniform)
+
+
+def score_select_compact(D, w, out, budget=None, uniform=0, with_kept=True):
+    """One fused trigger (kv_evict_score_select_compact); returns the scores it wrote."""
+    scores = torch.zeros(D["k"].shape[0], dtype=torch.float32, device=D["k"].device)
+    cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, out["cap"])
+    kv.kv_evict_score_select_compact(cache_of(D, w), obs_of(D, w), scores, budget, w.n_prefix, w.n_recent, cout,
+                                     kept_idx=out["kept"] if with_kept else None, uniform_budget=uniform)
+    return scores
