@@ -415,12 +415,49 @@ __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, i
     base = k0;
     cnt = k1 - k0;
   } else {
-    for (int j = tid; j < n; j += 256)
-      keys[j] = float_order_key(
-          __hip_atomic_load(&a.scores[off + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    // the segment's scores into LDS, eight loads in flight per thread (clamped
+    // addresses, so no load waits on a branch), with the candidates' min and max
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int j0 = 0; j0 < n; j0 += 8 * 256) {
+      float raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        raw[u] = __hip_atomic_load(&a.scores[off + min(j0 + u * 256 + tid, n - 1)], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * 256 + tid;
+        if (j < n) {
+          const uint32_t key = float_order_key(raw[u]);
+          keys[j] = key;
+          if (j >= P && j < n - R) {
+            kmin = min(kmin, key);
+            kmax = max(kmax, key);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+      kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+    }
+    if ((tid & 63) == 0) {
+      hist[tid >> 6] = kmin;
+      hist[4 + (tid >> 6)] = kmax;
+    }
     __syncthreads();
+    kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
+    kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+    __syncthreads();
+    // every candidate shares the leading bits of its min and max: the radix digits start below them
+    const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
     uint32_t T, kk;
-    radix_threshold<256>([&](int j) { return keys[j]; }, P, n, R, K - P - R, hist, sh, T, kk);
+    radix_threshold_v<256>(
+        [&](const auto& f) {
+          for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
+        },
+        K - P - R, hist, sh, T, kk, kmin, known);
     // kept slots and threshold ties before this chunk
     int eq_b = 0, gt_b = 0;
     for (int j = P + tid; j < min(k0, n - R); j += 256) {

@@ -44,30 +44,36 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
   return t;
 }
 
-// Threshold of a protected top-K over one segment: among the candidate slots
-// j in [P, n-R) find the kc-th largest order key T (MSB-first radix select,
-// four 8-bit digits, LDS histograms) and kk, the number of candidates equal to
-// T that are kept (the lowest slots).  key_at(j) returns slot j's order key.
-// kc == 0 gives T = 0xFFFFFFFF, kk = 0 (nothing beyond the protected slots).
-// hist: 256 uints of LDS; sh: 2 uints of LDS.
-template <int BLOCK, typename KeyAt>
-__device__ __forceinline__ void radix_threshold(const KeyAt& key_at, int P, int n, int R, int kc, uint32_t* hist,
-                                                uint32_t* sh, uint32_t& T, uint32_t& kk_out) {
+// Threshold of a top-kc selection: find the kc-th largest order key T among the
+// candidate keys of the work-group (MSB-first radix select over LDS histograms
+// of at most 8-bit digits) and kk, the number of candidates equal to T that
+// are kept.  visit(f) calls f(key) once for every candidate key this thread
+// holds; every thread must visit the same keys on each call.  The caller may
+// pass the number of leading bits `known` (0..32) that every candidate shares
+// with `prefix` (e.g. the common prefix of the candidates' minimum and
+// maximum); the digits then start below them.  kc == 0 gives T = 0xFFFFFFFF,
+// kk = 0.  hist: 256 uints of LDS; sh: 2 uints of LDS.
+template <int BLOCK, typename Visit>
+__device__ __forceinline__ void radix_threshold_v(const Visit& visit, int kc, uint32_t* hist, uint32_t* sh,
+                                                  uint32_t& T, uint32_t& kk_out, uint32_t prefix = 0,
+                                                  int known = 0) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t mask = known == 0 ? 0u : ~0u << (32 - known);
+  prefix &= mask;
   uint32_t kk = uint32_t(kc);
   if (kc == 0) {
     T = 0xFFFFFFFFu;
     kk_out = 0;
     return;
   }
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int hi = 32 - known; hi > 0;) {
+    const int shift = hi > 8 ? hi - 8 : 0;
+    const uint32_t wmask = (1u << (hi - shift)) - 1u;
     for (int d = tid; d < 256; d += BLOCK) hist[d] = 0;
     __syncthreads();
-    for (int j = P + tid; j < n - R; j += BLOCK) {
-      const uint32_t key = key_at(j);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
+    visit([&](uint32_t key) {
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & wmask], 1u);
+    });
     __syncthreads();
     if (tid < 64) {
       // lane l owns digits 255-4l .. 252-4l (descending)
@@ -106,11 +112,24 @@ __device__ __forceinline__ void radix_threshold(const KeyAt& key_at, int P, int 
     __syncthreads();
     prefix = sh[0];
     kk = sh[1];
-    mask |= 255u << shift;
+    mask |= wmask << shift;
+    hi = shift;
     __syncthreads();
   }
   T = prefix;
   kk_out = kk;
+}
+
+// Protected form over one segment: candidates are the slots j in [P, n-R),
+// key_at(j) returns slot j's order key.
+template <int BLOCK, typename KeyAt>
+__device__ __forceinline__ void radix_threshold(const KeyAt& key_at, int P, int n, int R, int kc, uint32_t* hist,
+                                                uint32_t* sh, uint32_t& T, uint32_t& kk_out) {
+  radix_threshold_v<BLOCK>(
+      [&](const auto& f) {
+        for (int j = P + int(threadIdx.x); j < n - R; j += BLOCK) f(key_at(j));
+      },
+      kc, hist, sh, T, kk_out);
 }
 
 }  // namespace kve
