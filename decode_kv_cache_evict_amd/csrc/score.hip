@@ -49,38 +49,53 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 // ------------------------------------------------------------ query rotation
 // Rotate every observation row to its q_pos (double-precision angle and
 // rotation) and round to the storage dtype; rows past n_obs are zeroed.  One
-// thread per (request, observation row, frequency): the angle is shared by all
-// query heads, so its sine and cosine are formed once and applied to every head.
+// thread per (request, observation row, run of V frequencies): the angles are
+// shared by all query heads, so their sines and cosines are formed once and
+// applied to every head, with 16-byte loads and stores of both halves.
 template <typename T>
 __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
                                   const int32_t* __restrict__ n_obs, T* __restrict__ qr,
                                   int64_t n_work, int n_q, int max_obs, int D, double theta) {
+  constexpr int V = 16 / int(sizeof(T));          // frequencies per thread
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n_work) return;
   const int half = D / 2;
-  const int i = int(idx % half);
-  const int64_t bo = idx / half;                  // b * max_obs + o
+  const int runs = half / V;
+  const int i0 = int(idx % runs) * V;
+  const int64_t bo = idx / runs;                  // b * max_obs + o
   const int o = int(bo % max_obs);
   const int b = int(bo / max_obs);
   const int no = n_obs ? n_obs[b] : max_obs;
   const bool live = o < no;
-  double s = 0.0, c = 1.0;
-  if (live) {
-    const double ang = double(q_pos[bo]) * pow(theta, -2.0 * double(i) / double(D));
-    sincos(ang, &s, &c);
+  double sn[V], cs[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    sn[v] = 0.0;
+    cs[v] = 1.0;
+    if (live) {
+      const double ang = double(q_pos[bo]) * pow(theta, -2.0 * double(i0 + v) / double(D));
+      sincos(ang, &sn[v], &cs[v]);
+    }
   }
   for (int h = 0; h < n_q; ++h) {
     const int64_t row = (int64_t(b) * n_q + h) * max_obs + o;
-    const T* src = q + row * D;
-    T* dst = qr + row * D;
-    if (!live) {
-      dst[i] = Elem<T>::from_f64(0.0);
-      dst[i + half] = Elem<T>::from_f64(0.0);
-      continue;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (live) {
+      const uint4 x = *reinterpret_cast<const uint4*>(q + row * D + i0);
+      const uint4 y = *reinterpret_cast<const uint4*>(q + row * D + i0 + half);
+      const T* xe = reinterpret_cast<const T*>(&x);
+      const T* ye = reinterpret_cast<const T*>(&y);
+      T* le = reinterpret_cast<T*>(&lo);
+      T* he = reinterpret_cast<T*>(&hi);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const RotPair r = rotate_pair(double(Elem<T>::widen(xe[v])), double(Elem<T>::widen(ye[v])), cs[v], sn[v]);
+        le[v] = Elem<T>::from_f64(r.a);
+        he[v] = Elem<T>::from_f64(r.b);
+      }
     }
-    RotPair r = rotate_pair(double(Elem<T>::widen(src[i])), double(Elem<T>::widen(src[i + half])), c, s);
-    dst[i] = Elem<T>::from_f64(r.a);
-    dst[i + half] = Elem<T>::from_f64(r.b);
+    *reinterpret_cast<uint4*>(qr + row * D + i0) = lo;
+    *reinterpret_cast<uint4*>(qr + row * D + i0 + half) = hi;
   }
 }
 
@@ -618,12 +633,17 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
           a.scores[off + j] = fast_exp2(m);
       }
     };
-    load_batch(0);
+    // pass 2 walks the chunk backwards: its first batches are the ones pass 1
+    // read last (the likeliest still in L2), and it ends where the gather of the
+    // kept rows begins
+    const int ntl = (span + kBK - 1) / kBK;
+    auto kb_at = [&](int it) { return P2 ? (ntl - 1 - it) * kBK : it * kBK; };
+    load_batch(kb_at(0));
     store_batch(0);
-    if (kBK < span) load_batch(kBK);
+    if (ntl > 1) load_batch(kb_at(1));
     __syncthreads();
     int cur = 0;
-    for (int kb = 0; kb < span; kb += kBK) {
+    for (int it = 0; it < ntl; ++it) {
       int kpos[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) kpos[q4] = kps[cur][q4 * 16 + col];
@@ -641,13 +661,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
         if (!P2) stats_update<RT>(st0, st1, acc, c);
         else key_max2<RT>(acc, st0, c, red[cur][w], 2 * h, col, quad);
       }
-      if (kb + kBK < span) store_batch(cur ^ 1);
-      if (kb + 2 * kBK < span) load_batch(kb + 2 * kBK);
-      if (P2 && kb > 0) finish_keys(cur ^ 1, kb - kBK);
+      if (it + 1 < ntl) store_batch(cur ^ 1);
+      if (it + 2 < ntl) load_batch(kb_at(it + 2));
+      if (P2 && it > 0) finish_keys(cur ^ 1, kb_at(it - 1));
       __syncthreads();
       cur ^= 1;
     }
-    if (P2) finish_keys(cur ^ 1, ((span - 1) / kBK) * kBK);
+    if (P2) finish_keys(cur ^ 1, kb_at(ntl - 1));
   };
 
   if (MODE == kModePass2) {
@@ -891,7 +911,7 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   a.lse = reinterpret_cast<float*>(w);
   w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
   int* ctl = reinterpret_cast<int*>(w);
-  const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2);
+  const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2) / (16 / int64_t(elem));
   const dim3 rg(unsigned((n_work + 255) / 256));
   if (n_work > 0) {
     if (a.dtype == 0)

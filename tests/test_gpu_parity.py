@@ -225,6 +225,34 @@ def test_fps_matches_oracle(name):
     print(f"{name}: {exact}/{n_buf - len(range(0, n_buf, 7))} pick sequences identical to the oracle's")
 
 
+@pytest.mark.parametrize("cap,k_keep,d", [(64, 33, 128), (40, 20, 64), (16, 8, 128), (17, 1, 64)])
+def test_fps_capacities_and_head_sizes(cap, k_keep, d):
+    """Capacities that are not a multiple of the 16-row tiles, the 64-row limit,
+    both head sizes, k_keep = 1; some buffers not full (copied through)."""
+    g = torch.Generator().manual_seed(cap * 1000 + k_keep)
+    n_buf = 37
+    buf = (torch.randn(n_buf, cap, d, generator=g) + 0.3 * torch.randn(n_buf, 1, d, generator=g)).to(torch.bfloat16)
+    buf = buf.cuda()
+    count = torch.full((n_buf,), cap, dtype=torch.int32, device="cuda")
+    count[::5] = cap // 2
+    out = torch.zeros_like(buf)
+    cnt_out = torch.zeros_like(count)
+    picks = torch.zeros(n_buf, k_keep, dtype=torch.int32, device="cuda")
+    kv.beacon_fps_update(buf, out, count, cnt_out, k_keep, picks)
+    torch.cuda.synchronize()
+    X = np64(buf)
+    P = picks.cpu().numpy()
+    for p in range(n_buf):
+        if p % 5 == 0:
+            assert int(cnt_out[p]) == cap // 2 and np.all(P[p] == -1)
+            assert torch.equal(out[p, :cap // 2], buf[p, :cap // 2])
+            continue
+        assert int(cnt_out[p]) == k_keep
+        ok, step = oracle.fps_acceptable(X[p], P[p], 2e-3)
+        assert ok, f"buffer {p}: pick {step} not a farthest point"
+        assert torch.equal(out[p, :k_keep], buf[p, np.sort(P[p]).tolist()])
+
+
 def test_epikv_matches_oracle():
     w = get_workload("long-65k")
     B, T, Dm, W = 2, 1500, 512, 256
