@@ -17,8 +17,8 @@ __all__ = [
     "round_bf16", "to_storage", "rope", "visible_mask", "segment_probabilities",
     "segment_scores", "layer_scores", "normalized_entropy", "waterfill",
     "largest_remainder", "head_budgets", "layer_wave_budgets", "select_kept",
-    "compact_rows", "fps", "fps_acceptable", "epikv_g", "rolling_z", "epikv_score",
-    "layer_select_compact",
+    "compact_rows", "fps", "fps_acceptable", "epikv_g", "rolling_z", "rolling_mean", "epikv_score",
+    "layer_select_compact", "head_weights",
 ]
 
 
@@ -110,22 +110,31 @@ def segment_probabilities(k, key_pos, q_rot, q_pos, causal=True):
     return np.where(vis & has, np.exp(logits - lse), 0.0)
 
 
-def segment_scores(k, key_pos, q_rot, q_pos, causal=True):
+def segment_scores(k, key_pos, q_rot, q_pos, causal=True, aggregate="max"):
     """Importance of every cached key of one KV head: the maximum, over the
     observation rows of all query heads sharing this KV head, of that row's
     softmax probability.
 
     BeaconKV, section "打分时的 RoPE 对齐": importance is max-aggregated over
     the observation queries (max, not mean, so a single beacon that rates a key
-    highly keeps it).  READING: the maximum also runs over the GQA group."""
+    highly keeps it).  READING: the maximum also runs over the GQA group.
+
+    aggregate="mean" is the ablation the same page reports in its experiments
+    section (max vs mean aggregation): the mean over the same rows.  READING: a
+    key that a row cannot see contributes 0 for that row, and every observation
+    row counts in the denominator (a row that sees no key at all contributes 0)."""
     p = segment_probabilities(k, key_pos, q_rot, q_pos, causal)
     if p.shape[0] == 0:
         return np.zeros(p.shape[1])
+    if aggregate == "mean":
+        return p.sum(axis=0) / p.shape[0]
+    if aggregate != "max":
+        raise ValueError(aggregate)
     return p.max(axis=0)
 
 
 def layer_scores(k_cache, key_pos, seg_off, seg_len, q_obs, q_pos, n_obs, n_kv_heads,
-                 theta, dtype, causal=True):
+                 theta, dtype, causal=True, aggregate="max"):
     """Scores for every row of one layer's segmented cache (O1-O4).
 
     k_cache [rows, d] exact stored values; q_obs [B, Hq, max_obs, d] pre-RoPE
@@ -148,7 +157,7 @@ def layer_scores(k_cache, key_pos, seg_off, seg_len, q_obs, q_pos, n_obs, n_kv_h
                 rows.append(to_storage(rope(q_obs[b, h, :no], qp, theta), dtype))
             qr = np.concatenate(rows, axis=0)
             qpos_rows = np.tile(qp, G)
-            out[o:o + n] = segment_scores(k_cache[o:o + n], key_pos[o:o + n], qr, qpos_rows, causal)
+            out[o:o + n] = segment_scores(k_cache[o:o + n], key_pos[o:o + n], qr, qpos_rows, causal, aggregate)
     return out
 
 
@@ -229,6 +238,16 @@ def largest_remainder(x, total):
     for g in order[:r]:
         out[g] += 1
     return out
+
+
+def head_weights(entropy, inverse=False):
+    """Head weights for the budget split.  The direct reading takes the
+    normalised entropy itself; ReasonAlloc, "Key Concepts" (head utility), says
+    the focused, low-entropy heads are the useful ones that gain budget, which
+    is the inverse reading 1 - E (the two passages of the page disagree; both
+    are offered)."""
+    E = np.asarray(entropy, dtype=np.float64)
+    return 1.0 - E if inverse else E
 
 
 def head_budgets(weights, seg_len, layer_total, min_per_head):
@@ -371,7 +390,26 @@ def rolling_z(g, window, eps):
     return z
 
 
-def epikv_score(h_a, h_b, window, eps):
-    """Eviction score s(t) = z_a(t) - z_b(t) (EPIKV, part 3: z_10 - z_21);
-    higher keeps.  h_a, h_b: [T, d_model] hidden states of the two layers."""
+def rolling_mean(g, window):
+    """Causal rolling mean g_bar(t) over the same window as rolling_z:
+    {max(1, t-W+1), ..., t}; g_bar(0) = 0.
+
+    EPIKV, part 2 (双带层解剖结构): the band score is stated on rolling means of g."""
+    g = np.asarray(g, dtype=np.float64)
+    T = g.shape[0]
+    m = np.zeros(T)
+    for t in range(1, T):
+        m[t] = g[max(1, t - window + 1): t + 1].mean()
+    return m
+
+
+def epikv_score(h_a, h_b, window, eps, form="z"):
+    """Eviction score; higher keeps.  h_a, h_b: [T, d_model] hidden states of
+    the two layers.  form="z": s(t) = z_a(t) - z_b(t) (EPIKV, part 3:
+    z_10 - z_21, the trend-corrected score); form="mean": s(t) = g_bar_a(t) -
+    g_bar_b(t) (EPIKV, part 2: the rolling-mean form stated first)."""
+    if form == "mean":
+        return rolling_mean(epikv_g(h_a), window) - rolling_mean(epikv_g(h_b), window)
+    if form != "z":
+        raise ValueError(form)
     return rolling_z(epikv_g(h_a), window, eps) - rolling_z(epikv_g(h_b), window, eps)

@@ -96,3 +96,16 @@ def test_layer_wave_budgets_shape():
     x = _bisect(32768.0, w, 64.0, np.full(32, 1e9))
     assert np.all(np.abs(b - x) < 1)
     assert b[0] == 64                                              # raw share 62.7 < 64 is floored
+
+
+def test_inverse_entropy_weights_favour_focused_heads():
+    """ReasonAlloc, Key Concepts: low-entropy heads gain budget.  With weights
+    1 - E = (0.9, 0.5, 0.1) and room everywhere the split is 180/100/20."""
+    from oracle import head_weights
+    E = np.array([0.1, 0.5, 0.9])
+    assert np.allclose(head_weights(E, inverse=True), [0.9, 0.5, 0.1])
+    assert np.array_equal(head_weights(E), E)
+    b = head_budgets(head_weights(E, inverse=True), [1000, 1000, 1000], 300, 0)
+    assert b.tolist() == [180, 100, 20]
+    b2 = head_budgets(head_weights(E), [1000, 1000, 1000], 300, 0)
+    assert b2.tolist() == [20, 100, 180]

@@ -63,3 +63,34 @@ def test_score_is_difference_of_the_two_layers():
     assert np.allclose(s, -epikv_score(b, a, 32, 1e-6))
     assert np.allclose(epikv_score(a, a, 32, 1e-6), 0.0)
     assert s[0] == 0.0
+
+
+def test_rolling_mean_closed_forms():
+    """EPIKV part 2's g_bar over the window {max(1, t-W+1) .. t}: for the ramp
+    g(u) = a + b u the warm-up mean is a + b (t+1)/2 and the full-window mean
+    a + b (t - (W-1)/2); a constant stays constant."""
+    from oracle import rolling_mean
+    W, a, b = 64, 5.0, 2.0
+    g = np.array([0.0] + [a + b * u for u in range(1, 400)])
+    m = rolling_mean(g, W)
+    assert m[0] == 0.0
+    for t in (1, 2, 30, W):
+        assert m[t] == pytest.approx(a + b * (t + 1) / 2, rel=1e-14)
+    for t in (W + 1, 200, 399):
+        assert m[t] == pytest.approx(a + b * (t - (W - 1) / 2), rel=1e-14)
+    assert np.allclose(rolling_mean(np.array([0.0] + [0.7] * 100), 16)[1:], 0.7)
+
+
+def test_mean_form_score():
+    from oracle import rolling_mean
+    rng = np.random.default_rng(2)
+    a = np.cumsum(rng.standard_normal((300, 8)), axis=0)
+    b = np.cumsum(rng.standard_normal((300, 8)), axis=0)
+    s = epikv_score(a, b, 32, 1e-6, form="mean")
+    assert np.allclose(s, rolling_mean(epikv_g(a), 32) - rolling_mean(epikv_g(b), 32))
+    assert np.allclose(s, -epikv_score(b, a, 32, 1e-6, form="mean"))
+    # steps of constant size c in layer a and 2c in layer b: s = -c after t = 0
+    ha = _trace_with_steps([0.0] + [0.5] * 100)
+    hb = _trace_with_steps([0.0] + [1.0] * 100)
+    sm = epikv_score(ha, hb, 16, 1e-6, form="mean")
+    assert sm[0] == 0.0 and np.allclose(sm[1:], -0.5)

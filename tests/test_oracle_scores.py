@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import segment_probabilities, segment_scores, layer_scores, visible_mask, rope, to_storage
@@ -99,3 +100,32 @@ def test_layer_scores_gqa_mapping_and_rotation():
 def test_visible_mask_shapes():
     m = visible_mask(np.arange(5), np.array([2, 4]))
     assert m.tolist() == [[True, True, True, False, False], [True] * 5]
+
+
+def test_mean_aggregation_hand_example_and_row_sum_invariant():
+    """Mean over observation rows (BeaconKV experiments, max vs mean ablation).
+    Two keys with equal logits for row 0, and a row 1 at position 0 that sees
+    only key 0: probabilities [0.5, 0.5] and [1, 0], so mean = [0.75, 0.25] and
+    max = [1, 0.5]."""
+    k = np.array([[1.0, 0.0], [1.0, 0.0]])
+    q = np.array([[2.0, 0.0], [3.0, 0.0]])
+    kpos, qpos = np.array([0, 1]), np.array([1, 0])
+    assert np.allclose(segment_scores(k, kpos, q, qpos, True, "mean"), [0.75, 0.25], rtol=1e-15)
+    assert np.allclose(segment_scores(k, kpos, q, qpos, True, "max"), [1.0, 0.5], rtol=1e-15)
+    # each row's probabilities sum to 1 (0 for a row that sees nothing), so the
+    # mean scores sum to (rows that see a key) / (all rows)
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((40, 16))
+    kpos = np.arange(40) + 10
+    qpos = np.array([5, 12, 30, 49, 49, 60, 9])          # rows 0 and 6 see no key
+    s = segment_scores(k, kpos, rng.standard_normal((7, 16)), qpos, True, "mean")
+    assert s.sum() == pytest.approx(5 / 7, rel=1e-13)
+    # one row: mean and max agree; mean never exceeds max
+    q1 = rng.standard_normal((1, 16))
+    assert np.allclose(segment_scores(k, kpos, q1, [60], True, "mean"), segment_scores(k, kpos, q1, [60]))
+    q3 = rng.standard_normal((5, 16)) * 3
+    assert np.all(segment_scores(k, kpos, q3, [45, 50, 60, 60, 60], True, "mean")
+                  <= segment_scores(k, kpos, q3, [45, 50, 60, 60, 60]) + 1e-15)
+    # and matches the dense softmax's column means
+    brute = _brute(k, kpos, q3, np.array([45, 50, 60, 60, 60]), True).mean(axis=0)
+    assert np.allclose(segment_scores(k, kpos, q3, [45, 50, 60, 60, 60], True, "mean"), brute, rtol=1e-12)
