@@ -15,9 +15,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVE_LIB") or os.path.join(_HERE, "_lib", "libkvevict.so")
 
 KVE_BF16, KVE_F32 = 0, 1
+KVE_AGG_MAX, KVE_AGG_MEAN = 0, 1
+KVE_EPIKV_Z, KVE_EPIKV_MEAN = 0, 1
 STATUS = {0: "KVE_OK", 1: "KVE_EINVAL", 2: "KVE_ESHAPE", 3: "KVE_EALIAS", 4: "KVE_EBUDGET",
           5: "KVE_EWORKSPACE", 6: "KVE_EDEVICE"}
-EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv_evict_wave_budgets",
+EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv_evict_entropy_budgets",
+           "kv_evict_wave_budgets",
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_score_select_compact_workspace",
            "kv_evict_score_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "kv_rope_apply", "kve_last_error", "kve_abi_version"]
@@ -40,7 +43,7 @@ class KveCache(ctypes.Structure):
 class KveObs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("q_pos", ctypes.c_void_p), ("n_obs", ctypes.c_void_p),
                 ("n_q_heads", ctypes.c_int32), ("max_obs", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("causal", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("causal", ctypes.c_int32), ("aggregate", ctypes.c_int32)]
 
 
 _lib = None
@@ -60,6 +63,7 @@ def lib():
             "kv_evict_score_workspace": (SZ, [CP, OP]),
             "kv_evict_score": (I32, [CP, OP, P, P, P, SZ, P]),
             "kv_evict_budgets": (I32, [P, P, P, I32, I32, I32, P, P]),
+            "kv_evict_entropy_budgets": (I32, [P, I32, P, P, I32, I32, I32, P, P]),
             "kv_evict_wave_budgets": (I32, [I32, D, D, I32, I32, P, P]),
             "kv_evict_select_workspace": (SZ, [CP, I32]),
             "kv_evict_select_compact": (I32, [CP, P, P, I64, P, I32, I32, I32, P, CP, P, SZ, P]),
@@ -67,7 +71,7 @@ def lib():
             "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
-            "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, P, P, P, SZ, P]),
+            "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, I32, P, P, P, SZ, P]),
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
             "kve_last_error": (ctypes.c_char_p, []),
             "kve_abi_version": (I32, []),
@@ -121,13 +125,15 @@ def make_cache(k, v, pos, seg_off, seg_len, n_kv_heads, max_seg_len):
     return c
 
 
-def make_obs(q, q_pos, n_obs, rope_theta, causal=True):
-    """kve_obs over q [B, Hq, max_obs, d] (pre-RoPE), q_pos [B, max_obs] i32, n_obs [B] i32 or None."""
+def make_obs(q, q_pos, n_obs, rope_theta, causal=True, aggregate=KVE_AGG_MAX):
+    """kve_obs over q [B, Hq, max_obs, d] (pre-RoPE), q_pos [B, max_obs] i32, n_obs [B] i32 or None.
+    aggregate: KVE_AGG_MAX (0) or KVE_AGG_MEAN (1)."""
     o = KveObs()
     o.q, o.q_pos = q.data_ptr(), q_pos.data_ptr()
     o.n_obs = n_obs.data_ptr() if n_obs is not None else None
     o.n_q_heads, o.max_obs = int(q.shape[1]), int(q.shape[2])
     o.rope_theta, o.causal = float(rope_theta), int(bool(causal))
+    o.aggregate = int(aggregate)
     o._keep = (q, q_pos, n_obs)
     return o
 
@@ -161,6 +167,12 @@ def kv_evict_score(cache, obs, scores, head_entropy=None, ws=None, stream=None):
 def kv_evict_budgets(weights, layer_total, cap, batch, n_heads, min_per_head, budget_out, stream=None):
     _check(lib().kv_evict_budgets(_ptr(weights), _ptr(layer_total), _ptr(cap), int(batch), int(n_heads),
                                   int(min_per_head), _ptr(budget_out), _stream(stream)))
+
+
+def kv_evict_entropy_budgets(head_entropy, inverse, layer_total, cap, batch, n_heads, min_per_head, budget_out,
+                             stream=None):
+    _check(lib().kv_evict_entropy_budgets(_ptr(head_entropy), int(inverse), _ptr(layer_total), _ptr(cap), int(batch),
+                                          int(n_heads), int(min_per_head), _ptr(budget_out), _stream(stream)))
 
 
 def kv_evict_wave_budgets(n_layers, center, sigma, total, min_per_layer, out, stream=None):
@@ -212,14 +224,15 @@ def epikv_workspace_size(batch, T):
     return int(lib().epikv_workspace_size(int(batch), int(T)))
 
 
-def epikv_score(h_a, h_b, window, eps, scores, g_out=None, ws=None, stream=None):
-    """h_a/h_b bf16 [B, T, d_model]; scores fp32 [B, T]; g_out optional fp32 [2, B, T]."""
+def epikv_score(h_a, h_b, window, eps, scores, g_out=None, ws=None, stream=None, form=KVE_EPIKV_Z):
+    """h_a/h_b bf16 [B, T, d_model]; scores fp32 [B, T]; g_out optional fp32 [2, B, T];
+    form: KVE_EPIKV_Z (0) or KVE_EPIKV_MEAN (1)."""
     B, T, D = h_a.shape
     if ws is None and g_out is None:
         ws = _ws(epikv_workspace_size(B, T), scores.device)
     wp, wn = _aligned(ws)
-    _check(lib().epikv_score(_ptr(h_a), _ptr(h_b), int(B), int(T), int(D), int(window), float(eps), _ptr(g_out),
-                             _ptr(scores), wp, wn, _stream(stream)))
+    _check(lib().epikv_score(_ptr(h_a), _ptr(h_b), int(B), int(T), int(D), int(window), float(eps), int(form),
+                             _ptr(g_out), _ptr(scores), wp, wn, _stream(stream)))
 
 
 def kv_rope_apply(src, dst, pos, rope_theta, stream=None):

@@ -79,6 +79,7 @@ kve_status check_obs(const kve_cache* c, const kve_obs* o, int32_t* rows) {
   if (r > kve::kMaxObsRows) return fail(KVE_ESHAPE, "group*max_obs = %lld > %d", (long long)r, kve::kMaxObsRows);
   if (!(o->rope_theta > 0.0)) return fail(KVE_EINVAL, "rope_theta must be > 0");
   if (o->causal != 0 && o->causal != 1) return fail(KVE_EINVAL, "causal must be 0 or 1");
+  if (o->aggregate != KVE_AGG_MAX && o->aggregate != KVE_AGG_MEAN) return fail(KVE_EINVAL, "aggregate must be 0 or 1");
   if (c->n_seg > 0 && (!o->q || !o->q_pos)) return fail(KVE_EINVAL, "null query pointers");
   if (!aligned16(o->q)) return fail(KVE_EINVAL, "queries not 16-byte aligned");
   *rows = int32_t(r);
@@ -106,6 +107,7 @@ kve::ScoreArgs score_args(const kve_cache* c, const kve_obs* o, int32_t rows, fl
   a.rows = rows;
   a.causal = o->causal;
   a.theta = o->rope_theta;
+  a.aggregate = o->aggregate;
   a.scores = scores;
   return a;
 }
@@ -174,6 +176,22 @@ kve_status kv_evict_budgets(const float* weights, const int32_t* layer_total, co
   return device_status(kve::launch_budgets(weights, layer_total, cap, batch, n_heads, min_per_head, budget_out,
                                            static_cast<hipStream_t>(stream)),
                        "kv_evict_budgets");
+}
+
+kve_status kv_evict_entropy_budgets(const float* head_entropy, int32_t inverse, const int32_t* layer_total,
+                                    const int32_t* cap, int32_t batch, int32_t n_heads, int32_t min_per_head,
+                                    int32_t* budget_out, void* stream) {
+  if (inverse != 0 && inverse != 1) return fail(KVE_EINVAL, "inverse must be 0 or 1");
+  if (batch < 0 || min_per_head < 0) return fail(KVE_EINVAL, "negative batch or floor");
+  if (n_heads < 1 || n_heads > 64) return fail(KVE_ESHAPE, "n_heads %d not in [1, 64]", n_heads);
+  if (batch > 0 && (!head_entropy || !layer_total || !cap || !budget_out)) return fail(KVE_EINVAL, "null pointer");
+  const size_t nb = size_t(batch) * n_heads * 4;
+  if (overlap(budget_out, nb, head_entropy, nb) || overlap(budget_out, nb, cap, nb) ||
+      overlap(budget_out, nb, layer_total, size_t(batch) * 4))
+    return fail(KVE_EALIAS, "budget_out overlaps an input");
+  return device_status(kve::launch_budgets(head_entropy, layer_total, cap, batch, n_heads, min_per_head, budget_out,
+                                           static_cast<hipStream_t>(stream), inverse),
+                       "kv_evict_entropy_budgets");
 }
 
 kve_status kv_evict_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total, int32_t min_per_layer,
@@ -371,8 +389,9 @@ size_t epikv_workspace_size(int32_t batch, int32_t T) {
 }
 
 kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model, int32_t window,
-                       float eps, float* g_out, float* scores, void* ws, size_t ws_bytes, void* stream) {
+                       float eps, int32_t form, float* g_out, float* scores, void* ws, size_t ws_bytes, void* stream) {
   if (batch < 0 || T < 0) return fail(KVE_EINVAL, "negative batch or T");
+  if (form != KVE_EPIKV_Z && form != KVE_EPIKV_MEAN) return fail(KVE_EINVAL, "form must be 0 (z) or 1 (rolling mean)");
   if (d_model != 512 && d_model != 1024 && d_model != 2048 && d_model != 4096 && d_model != 8192)
     return fail(KVE_ESHAPE, "d_model %d", d_model);
   if (window < 1 || window > 2048) return fail(KVE_ESHAPE, "window %d not in [1, 2048]", window);
@@ -388,7 +407,7 @@ kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t 
   if (overlap(scores, n * 4, h_a, hb) || overlap(scores, n * 4, h_b, hb) || overlap(gbuf, gb, h_a, hb) ||
       overlap(gbuf, gb, h_b, hb) || overlap(gbuf, gb, scores, n * 4))
     return fail(KVE_EALIAS, "an output of epikv_score overlaps an input");
-  return device_status(kve::launch_epikv(h_a, h_b, batch, T, d_model, window, eps, g_out, scores, ws,
+  return device_status(kve::launch_epikv(h_a, h_b, batch, T, d_model, window, eps, form, g_out, scores, ws,
                                          static_cast<hipStream_t>(stream)),
                        "epikv_score");
 }

@@ -1,7 +1,8 @@
 // Budget allocation (ReasonAlloc, "Core Mechanism" and "Key Concepts"):
 //   * head budgets: each request's layer total is split over its heads in
-//     proportion to a utility weight (the head's normalised score entropy),
-//     with a per-head floor and a cap at the head's cached length;
+//     proportion to a utility weight (the head's normalised score entropy E, or
+//     1 - E when focused heads are to gain budget), with a per-head floor and a
+//     cap at the head's cached length;
 //   * layer budgets: a mid-peaked Gaussian over the layer index, floored.
 // Real shares x_g = clamp(lam * w_g, lo_g, hi_g) with sum x = total are found
 // exactly on the breakpoints of the piecewise-linear sum, then rounded by the
@@ -146,13 +147,14 @@ __device__ void allocate(const double* w_in, double lo_all, const double* hi, in
 }
 
 __global__ void head_budget_kernel(const float* __restrict__ wts, const int32_t* __restrict__ tot,
-                                   const int32_t* __restrict__ cap, int batch, int H, int lo,
+                                   const int32_t* __restrict__ cap, int batch, int H, int lo, int form,
                                    int32_t* __restrict__ out) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   double w[kMaxHeads], hi[kMaxHeads];
   for (int g = 0; g < H; ++g) {
-    w[g] = double(wts[b * H + g]);
+    const double e = double(wts[b * H + g]);
+    w[g] = form == 1 ? 1.0 - e : e;           // inverse entropy: focused heads gain budget
     hi[g] = double(cap[b * H + g] > 0 ? cap[b * H + g] : 0);
   }
   double sum_hi = 0.0;
@@ -175,10 +177,10 @@ __global__ void wave_budget_kernel(int L, double center, double sigma, int total
 }  // namespace
 
 hipError_t launch_budgets(const float* w, const int32_t* total, const int32_t* cap, int32_t batch,
-                          int32_t n_heads, int32_t min_per_head, int32_t* out, hipStream_t st) {
+                          int32_t n_heads, int32_t min_per_head, int32_t* out, hipStream_t st, int weight_form) {
   if (batch == 0) return hipSuccess;
   hipLaunchKernelGGL(head_budget_kernel, dim3(unsigned((batch + 63) / 64)), dim3(64), 0, st, w, total, cap, batch,
-                     n_heads, min_per_head, out);
+                     n_heads, min_per_head, weight_form, out);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 // 时间趋势校正):
 //   g_l(t) = ||h_l(t) - h_l(t-1)||_2 for the two monitored layers,
 //   z_l(t) = (g_l(t) - mean) / (std + eps) over a causal window,
-//   score(t) = z_a(t) - z_b(t).
+//   score(t) = z_a(t) - z_b(t)  (part 3), or, in the rolling-mean form of
+//   part 2 (双带层解剖结构), score(t) = mean_a(t) - mean_b(t) over the same window.
 // g is a bandwidth-bound stream over the bf16 traces: one wavefront walks a run
 // of consecutive steps of one (layer, request), keeping the previous row in
 // registers so every row is read once.  z works on LDS tiles of g in double.
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void epikv_g_kernel(const uint16_t* __restrict
 
 // z for both layers and their difference over one tile of steps of one request.
 __global__ __launch_bounds__(kZTile) void epikv_z_kernel(const float* __restrict__ g, int batch, int T, int W,
-                                                         float eps, float* __restrict__ out) {
+                                                         float eps, int form, float* __restrict__ out) {
   extern __shared__ double zs[];               // [2][kZTile + W - 1]
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * kZTile;
@@ -90,6 +91,10 @@ __global__ __launch_bounds__(kZTile) void epikv_z_kernel(const float* __restrict
     double s = 0.0;
     for (int k = 0; k < cnt; ++k) s += u[k];
     const double mu = s / cnt;
+    if (form == 1) {                           // rolling-mean form: g_bar(t)
+      z[l] = mu;
+      continue;
+    }
     double v = 0.0;
     for (int k = 0; k < cnt; ++k) {
       const double d = u[k] - mu;
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kZTile) void epikv_z_kernel(const float* __restrict
 size_t epikv_ws_bytes(int32_t batch, int32_t T) { return size_t(2) * batch * T * sizeof(float); }
 
 hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model, int32_t window,
-                        float eps, float* g_out, float* scores, void* ws, hipStream_t st) {
+                        float eps, int32_t form, float* g_out, float* scores, void* ws, hipStream_t st) {
   if (batch == 0 || T == 0) return hipSuccess;
   float* g = g_out ? g_out : static_cast<float*>(ws);
   const int runs = (T + kRun - 1) / kRun;
@@ -126,7 +131,7 @@ hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t
   if (e != hipSuccess) return e;
   const size_t sh = size_t(2) * (kZTile + window - 1) * sizeof(double);
   hipLaunchKernelGGL(epikv_z_kernel, dim3(unsigned((T + kZTile - 1) / kZTile), unsigned(batch)), dim3(kZTile), sh, st,
-                     g, batch, T, window, eps, scores);
+                     g, batch, T, window, eps, form, scores);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct ScoreArgs {
   const int32_t* q_pos;   // [B, max_obs]
   const int32_t* n_obs;   // [B] or null
   int32_t n_q, max_obs, group, rows, causal;
+  int32_t aggregate;      // 0: max over the observation rows, 1: mean
   double theta;
   // outputs and workspace
   float* scores;
@@ -68,8 +69,9 @@ struct SelectArgs {
 };
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st);
 
+// weight_form 0: weights as given; 1: 1 - weight (inverse entropy).
 hipError_t launch_budgets(const float* w, const int32_t* total, const int32_t* cap, int32_t batch,
-                          int32_t n_heads, int32_t min_per_head, int32_t* out, hipStream_t st);
+                          int32_t n_heads, int32_t min_per_head, int32_t* out, hipStream_t st, int weight_form = 0);
 hipError_t launch_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total, int32_t lo,
                                int32_t* out, hipStream_t st);
 
@@ -78,8 +80,9 @@ hipError_t launch_fps(const void* q_in, void* q_out, const int32_t* count_in, in
                       int32_t* picks, hipStream_t st);
 
 size_t epikv_ws_bytes(int32_t batch, int32_t T);
+// form 0: z_a - z_b; 1: rolling mean g_bar_a - g_bar_b.
 hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model,
-                        int32_t window, float eps, float* g_out, float* scores, void* ws, hipStream_t st);
+                        int32_t window, float eps, int32_t form, float* g_out, float* scores, void* ws, hipStream_t st);
 
 hipError_t launch_rope_rows(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
                             double theta, int32_t dtype, hipStream_t st);

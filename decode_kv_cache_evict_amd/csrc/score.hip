@@ -40,6 +40,14 @@ __device__ __forceinline__ int64_t row_qr_index(const ScoreArgs& a, int b, int g
   return (int64_t(b) * a.n_q + h) * a.max_obs + i;
 }
 
+// 1 / (number of observation rows that exist for request b): the denominator of
+// the mean aggregation (every existing row counts, including a row that sees
+// no key yet).
+__device__ __forceinline__ float live_row_inverse(const ScoreArgs& a, int b) {
+  const int no = a.n_obs ? min(a.n_obs[b], a.max_obs) : a.max_obs;
+  return no > 0 ? 1.f / float(a.group * no) : 0.f;
+}
+
 __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& off, int& n) {
   off = a.seg_off[s];
   n = a.seg_len[s];
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
   for (int d = 0; d < D; ++d) kv[d] = valid ? Elem<T>::widen(kp[d]) : 0.f;
   if (valid) kpos = a.pos[off + j];
 
-  float best = -kInf;
+  float best = -kInf, sum = 0.f;
   for (int r = 0; r < a.rows; ++r) {
     const T* qrow = qs + r * D;
     float x = 0.f;
@@ -168,6 +176,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
     if (PASS2) {
       const float y = vis ? fmaf(x, c, -lse_s[r]) : -kInf;
       best = fmaxf(best, y);
+      if (a.aggregate) sum += vis ? exp2f(y) : 0.f;
     } else {
       const float xv = vis ? x : -kInf;
       const float m = wave_max(fmaxf(xv, kNegBig));
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
     }
   }
   if (PASS2) {
-    if (valid) a.scores[off + j] = exp2f(best);
+    if (valid) a.scores[off + j] = a.aggregate ? sum * live_row_inverse(a, b) : exp2f(best);
     return;
   }
   __syncthreads();
@@ -333,19 +342,23 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
 }
 
 // Pass-2: per key of tiles q0, q0+1, the max over this wave's rows of
-// c*x - lse, combined over the 4 lane groups; written to redw[key].
-template <int RT>
+// c*x - lse (MEAN: the sum of exp2(c*x - lse)), combined over the 4 lane
+// groups; written to redw[key].
+template <int RT, bool MEAN>
 __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float (&lse)[RT][4], float c, float* redw,
                                          int q0, int col, int quad) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float best = -kInf;
+    float best = MEAN ? 0.f : -kInf;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) best = fmaxf(best, fmaf(acc[j][rt][i], c, -lse[rt][i]));
-    best = fmaxf(best, __shfl_xor(best, 16, kWave));
-    best = fmaxf(best, __shfl_xor(best, 32, kWave));
+      for (int i = 0; i < 4; ++i) {
+        const float y = fmaf(acc[j][rt][i], c, -lse[rt][i]);
+        best = MEAN ? best + fast_exp2(y) : fmaxf(best, y);
+      }
+    best = MEAN ? best + __shfl_xor(best, 16, kWave) : fmaxf(best, __shfl_xor(best, 16, kWave));
+    best = MEAN ? best + __shfl_xor(best, 32, kWave) : fmaxf(best, __shfl_xor(best, 32, kWave));
     if (quad == 0) redw[(q0 + j) * 16 + col] = best;
   }
 }
@@ -580,6 +593,8 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   const int nch = (n + kMfmaChunk - 1) / kMfmaChunk;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
+  const bool mean = a.aggregate != 0;
+  const float inv_live = live_row_inverse(a, b);
 
   // per-row metadata, once per work-group
   for (int r = tid; r < 16 * 4 * RT; r += 256) {
@@ -623,14 +638,16 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
       for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[buf][(key0 + u * KPU) * LS + part * 8]) = pre[u];
       if (tid < kBK) kps[buf][tid] = prepos;
     };
-    auto finish_keys = [&](int bi, int kb) {  // per-key max over the 4 waves -> score
+    auto finish_keys = [&](int bi, int kb) {  // per-key max (sum) over the 4 waves -> score
       const int j = k0 + kb + tid;
       if (tid < kBK && j < k1) {
-        const float m = fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid]));
+        const float sc =
+            mean ? (red[bi][0][tid] + red[bi][1][tid] + red[bi][2][tid] + red[bi][3][tid]) * inv_live
+                 : fast_exp2(fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid])));
         if (MODE == kModeStep)   // read back by the segment's other work-groups: coherent store
-          __hip_atomic_store(&a.scores[off + j], fast_exp2(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&a.scores[off + j], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
-          a.scores[off + j] = fast_exp2(m);
+          a.scores[off + j] = sc;
       }
     };
     // pass 2 walks the chunk backwards: its first batches are the ones pass 1
@@ -659,7 +676,8 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
           rows.mask2(acc, kp2, rpos_s, w, quad);
         }
         if (!P2) stats_update<RT>(st0, st1, acc, c);
-        else key_max2<RT>(acc, st0, c, red[cur][w], 2 * h, col, quad);
+        else if (mean) key_max2<RT, true>(acc, st0, c, red[cur][w], 2 * h, col, quad);
+        else key_max2<RT, false>(acc, st0, c, red[cur][w], 2 * h, col, quad);
       }
       if (it + 1 < ntl) store_batch(cur ^ 1);
       if (it + 2 < ntl) load_batch(kb_at(it + 2));

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVE_ABI_VERSION 1
+#define KVE_ABI_VERSION 2
 
 typedef enum {
   KVE_OK = 0,
@@ -60,6 +60,12 @@ typedef enum {
 } kve_status;
 
 typedef enum { KVE_BF16 = 0, KVE_F32 = 1 } kve_dtype;
+
+/* Aggregation of the observation rows' softmax probabilities into a key's score. */
+typedef enum { KVE_AGG_MAX = 0, KVE_AGG_MEAN = 1 } kve_aggregate;
+
+/* Form of the attention-free score. */
+typedef enum { KVE_EPIKV_Z = 0, KVE_EPIKV_MEAN = 1 } kve_epikv_form;
 
 typedef struct kve_cache {
   int32_t dtype;            /* kve_dtype of k and v */
@@ -85,7 +91,7 @@ typedef struct kve_obs {
   int32_t max_obs;          /* (n_q_heads/n_kv_heads) * max_obs <= 256 */
   double rope_theta;        /* RoPE base; pairs (x_i, x_{i+d/2}), frequency theta^(-2i/d) */
   int32_t causal;           /* 1: key j visible to row i iff pos[j] <= q_pos[i]; 0: all keys visible */
-  int32_t reserved;
+  int32_t aggregate;        /* kve_aggregate: KVE_AGG_MAX (BeaconKV's choice) or KVE_AGG_MEAN (its ablation) */
 } kve_obs;
 
 /* Workspace bytes kv_evict_score needs for this cache/observation shape. */
@@ -96,7 +102,10 @@ size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o);
  * its q_pos (angle formed in double precision, rotated value rounded to the cache
  * dtype), take logits q.k/sqrt(d) in fp32 over every visible cached key of the
  * segment, a per-row softmax over the segment, and
- *   scores[row] = max over the group's query heads and observation rows of p.
+ *   scores[row] = max over the group's query heads and observation rows of p
+ * (o->aggregate = KVE_AGG_MAX), or, for the max-vs-mean ablation of BeaconKV's
+ * "📊 实验", the mean over those rows (KVE_AGG_MEAN: every existing row counts,
+ * a key a row cannot see contributes 0 for that row).
  * scores: [c->n_rows] fp32, aligned with the cache rows (rows outside every
  * segment are not written).  head_entropy: optional [n_seg] fp32, the
  * normalised entropy of each segment's score distribution (ReasonAlloc "Key
@@ -130,6 +139,18 @@ kve_status kv_evict_budgets(const float* weights, const int32_t* layer_total, co
  */
 kve_status kv_evict_wave_budgets(int32_t n_layers, double center, double sigma, int32_t total,
                                  int32_t min_per_layer, int32_t* out, void* stream);
+
+/*
+ * kv_evict_entropy_budgets — kv_evict_budgets with the weights formed from the
+ * heads' normalised score entropy E (kv_evict_score's head_entropy, [batch *
+ * n_heads] fp32): weight = E (inverse = 0) or 1 - E (inverse = 1, ReasonAlloc
+ * "Key Concepts": low-entropy, focused heads are the useful ones and gain
+ * budget).  Every other argument and rule as kv_evict_budgets.
+ * Errors: EINVAL (inverse not 0/1, null pointers), ESHAPE, EALIAS, EDEVICE.
+ */
+kve_status kv_evict_entropy_budgets(const float* head_entropy, int32_t inverse, const int32_t* layer_total,
+                                    const int32_t* cap, int32_t batch, int32_t n_heads, int32_t min_per_head,
+                                    int32_t* budget_out, void* stream);
 
 /* Workspace bytes kv_evict_select_compact needs (0 when kept_idx is supplied). */
 size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx);
@@ -215,13 +236,15 @@ size_t epikv_workspace_size(int32_t batch, int32_t T);
  *   g(t) = ||h(t) - h(t-1)||_2 (t >= 1), g(0) = 0,
  *   z(t) = (g(t) - mean) / (std + eps) over the causal window
  *          {max(1, t-window+1) .. t} (population std), z(0) = 0,
- *   scores[b*T + t] = z_a(t) - z_b(t)   (higher keeps).
+ *   scores[b*T + t] = z_a(t) - z_b(t)   (higher keeps; form = KVE_EPIKV_Z), or
+ *   scores[b*T + t] = gbar_a(t) - gbar_b(t), the rolling means of g over the
+ *   same window (form = KVE_EPIKV_MEAN; 方法论 part 2), gbar(0) = 0.
  * g_out: optional [2, batch, T] fp32 (the two g series).  Window sums in double.
  * d_model is 512, 1024, 2048, 4096 or 8192; the traces and scores are 16-byte aligned.
- * Errors: EINVAL, ESHAPE (d_model, window < 1 or > 2048), EWORKSPACE, EDEVICE.
+ * Errors: EINVAL (form, null pointers), ESHAPE (d_model, window < 1 or > 2048), EWORKSPACE, EDEVICE.
  */
 kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model,
-                       int32_t window, float eps, float* g_out, float* scores,
+                       int32_t window, float eps, int32_t form, float* g_out, float* scores,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*

@@ -23,14 +23,14 @@ def cache_of(D, w):
     return kv.make_cache(D["k"], D["v"], D["pos"], D["seg_off"], D["seg_len"], w.n_kv_heads, D["max_len"])
 
 
-def obs_of(D, w):
-    return kv.make_obs(D["q_obs"], D["q_pos"], D["n_obs"], w.rope_theta, bool(w.causal))
+def obs_of(D, w, aggregate=0):
+    return kv.make_obs(D["q_obs"], D["q_pos"], D["n_obs"], w.rope_theta, bool(w.causal), aggregate)
 
 
-def score_layer(D, w, entropy=False):
+def score_layer(D, w, entropy=False, aggregate=0):
     scores = torch.zeros(D["k"].shape[0], dtype=torch.float32, device=D["k"].device)
     ent = torch.zeros(D["seg_off"].numel(), dtype=torch.float32, device=D["k"].device) if entropy else None
-    kv.kv_evict_score(cache_of(D, w), obs_of(D, w), scores, ent)
+    kv.kv_evict_score(cache_of(D, w), obs_of(D, w, aggregate), scores, ent)
     return scores, ent
 
 
@@ -56,10 +56,11 @@ def select_compact(D, w, scores, out, budget=None, uniform=0, score_off=None):
                                score_off=score_off, uniform_budget=uniform)
 
 
-def score_select_compact(D, w, out, budget=None, uniform=0, with_kept=True):
+def score_select_compact(D, w, out, budget=None, uniform=0, with_kept=True, aggregate=0):
     """One fused trigger (kv_evict_score_select_compact); returns the scores it wrote."""
     scores = torch.zeros(D["k"].shape[0], dtype=torch.float32, device=D["k"].device)
     cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, out["cap"])
-    kv.kv_evict_score_select_compact(cache_of(D, w), obs_of(D, w), scores, budget, w.n_prefix, w.n_recent, cout,
+    kv.kv_evict_score_select_compact(cache_of(D, w), obs_of(D, w, aggregate), scores, budget, w.n_prefix, w.n_recent,
+                                     cout,
                                      kept_idx=out["kept"] if with_kept else None, uniform_budget=uniform)
     return scores

@@ -15,9 +15,9 @@ def oracle_cache_keys(layer, w):
     return oracle.to_storage(oracle.rope(np64(layer["k_pre"]), layer["pos"].cpu().numpy(), w.rope_theta), w.dtype)
 
 
-def oracle_layer_scores(layer, w, k=None):
+def oracle_layer_scores(layer, w, k=None, aggregate="max"):
     k = oracle_cache_keys(layer, w) if k is None else k
     return oracle.layer_scores(
         k, layer["pos"].cpu().numpy(), layer["seg_off"].cpu().numpy(), layer["seg_len"].cpu().numpy(),
         np64(layer["q_obs"]), layer["q_pos"].cpu().numpy(), layer["n_obs"].cpu().numpy(),
-        w.n_kv_heads, w.rope_theta, w.dtype, bool(w.causal))
+        w.n_kv_heads, w.rope_theta, w.dtype, bool(w.causal), aggregate)

@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
     L = kv.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert kv.kve_abi_version() == 1
+    assert kv.kve_abi_version() == 2
 
 
 def _fail(fn, *args):
@@ -64,9 +64,18 @@ def test_host_validation_without_gpu():
     assert _fail(L.beacon_fps_update, 0x1000, 0x1000, 0x2000, 0x2000, 4, 65, 16, 128, 0, None, None)[0] == 2
     assert _fail(L.beacon_fps_update, 0x1000, 0x1010, 0x2000, 0x3000, 4, 32, 16, 128, 0, None, None)[0] == 3
     # EPIKV shapes
-    assert _fail(L.epikv_score, 0x1000, 0x2000, 2, 10, 4000, 256, 1e-6, None, 0x3000, 0x4000, 1 << 20, None)[0] == 2
-    assert _fail(L.epikv_score, 0x1000, 0x2000, 2, 10, 4096, 0, 1e-6, None, 0x3000, 0x4000, 1 << 20, None)[0] == 2
+    assert _fail(L.epikv_score, 0x1000, 0x2000, 2, 10, 4000, 256, 1e-6, 0, None, 0x3000, 0x4000, 1 << 20, None)[0] == 2
+    assert _fail(L.epikv_score, 0x1000, 0x2000, 2, 10, 4096, 0, 1e-6, 0, None, 0x3000, 0x4000, 1 << 20, None)[0] == 2
     # budgets
     assert _fail(L.kv_evict_budgets, 0x1000, 0x2000, 0x3000, 4, 65, 64, 0x4000, None)[0] == 2
     assert _fail(L.kv_evict_wave_budgets, 32, 16.0, 6.0, 100, 64, 0x1000, None)[0] == 2
+    # variant flags outside their enums
+    o4 = kv.KveObs(q=0x6000, q_pos=0x7000, n_obs=None, n_q_heads=32, max_obs=48, rope_theta=1e6, causal=1,
+                   aggregate=2)
+    st, msg = _fail(L.kv_evict_score, ctypes.byref(c), ctypes.byref(o4), 0x8000, None, None, 0, None)
+    assert st == 1 and "aggregate" in msg
+    assert _fail(L.epikv_score, 0x1000, 0x2000, 2, 10, 4096, 256, 1e-6, 2, None, 0x3000, 0x4000, 1 << 20,
+                 None)[0] == 1
+    assert _fail(L.kv_evict_entropy_budgets, 0x1000, 2, 0x2000, 0x3000, 4, 8, 64, 0x4000, None)[0] == 1
+    assert _fail(L.kv_evict_entropy_budgets, 0x1000, 1, 0x2000, 0x3000, 4, 65, 64, 0x4000, None)[0] == 2
     assert _fail(L.kv_rope_apply, 0x1000, 0x1000, 0x2000, 4, 128, 1e4, 0, None)[0] == 3

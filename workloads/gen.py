@@ -181,3 +181,28 @@ def make_traces(w: Workload, device="cpu", T=None, d_model=None, batch=None, chu
         out[:, :, t0:t0 + c] = h.to(torch.bfloat16)
         carry = h[:, :, -1]
     return out
+
+
+def initial_recent_obs(L, w: Workload, n_initial: int, device="cpu"):
+    """Observation set of the Initial+Recent alternative that the BeaconKV page
+    ablates against (section 打分时的 RoPE 对齐, Table 3): the first n_initial
+    queries of the sequence, at their own positions 0 .. n_initial-1, in place
+    of the beacons, followed by the layer's recent queries.  An initial query
+    of head h is the pre-RoPE key of its KV head at that position plus noise
+    (the same construction as the recent queries, which sit near the key at
+    their position).  Returns (q_obs [B, Hq, n_initial + Rq, d], q_pos, n_obs)."""
+    dt = _DT[w.dtype]
+    B, Hkv, Hq, G, d, Rq = w.batch, w.n_kv_heads, w.n_q_heads, w.group, w.head_dim, w.n_recent_q
+    g = _g("cpu", _seed(w, 0, 7))
+    k_pre = L["k_pre"].to("cpu")
+    seg_off = L["seg_off"].to("cpu")
+    init = torch.empty(B, Hq, n_initial, d)
+    for b in range(B):
+        for h in range(Hq):
+            o = int(seg_off[b * Hkv + h // G])
+            init[b, h] = k_pre[o:o + n_initial] + w.key_sigma * torch.randn(n_initial, d, generator=g)
+    q_obs = torch.cat([init.to(dt), L["q_obs"][:, :, :Rq].to("cpu")], dim=2).to(device)
+    q_pos = torch.cat([torch.arange(n_initial, dtype=torch.int32).expand(B, n_initial),
+                       L["q_pos"][:, :Rq].to("cpu")], dim=1).contiguous().to(device)
+    n_obs = torch.full((B,), n_initial + Rq, dtype=torch.int32, device=device)
+    return q_obs, q_pos, n_obs
