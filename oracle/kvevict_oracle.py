@@ -18,7 +18,7 @@ __all__ = [
     "segment_scores", "layer_scores", "normalized_entropy", "waterfill",
     "largest_remainder", "head_budgets", "layer_wave_budgets", "select_kept",
     "compact_rows", "fps", "fps_acceptable", "epikv_g", "rolling_z", "rolling_mean", "epikv_score",
-    "layer_select_compact", "head_weights",
+    "layer_select_compact", "head_weights", "hole_fill",
 ]
 
 
@@ -294,6 +294,30 @@ def select_kept(scores, n, budget, n_prefix, n_recent):
 def compact_rows(rows, kept):
     """Stable gather: out[i] = rows[kept[i]] (BeaconKV "📊 实验": permanent eviction)."""
     return np.asarray(rows)[np.asarray(kept)]
+
+
+def hole_fill(kept, n):
+    """In-place compaction by hole filling.  With K = len(kept) survivors of a
+    segment of n rows, survivors already in [0, K) stay where they are and the
+    survivors in [K, n), in ascending order, move into the evicted slots of
+    [0, K), in ascending order.  Returns src [K]: the slot whose row ends up at
+    position i.  At most min(K, n - K) rows move.
+
+    BeaconKV, "📊 实验": eviction is permanent; attention does not depend on the
+    order of the cached rows (each row keeps its position, which carries RoPE
+    and causality), so the survivors need not stay in slot order.  READING:
+    the pairing (holes and movers both ascending) is this library's choice."""
+    kept = np.sort(np.asarray(kept, dtype=np.int64))
+    K = len(kept)
+    keep = np.zeros(int(n), dtype=bool)
+    keep[kept] = True
+    holes = [j for j in range(K) if not keep[j]]
+    movers = [j for j in range(K, int(n)) if keep[j]]
+    assert len(holes) == len(movers)
+    src = np.arange(K)
+    for h, m in zip(holes, movers):
+        src[h] = m
+    return src
 
 
 def layer_select_compact(scores, seg_off, seg_len, budgets, n_prefix, n_recent):

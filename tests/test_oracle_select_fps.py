@@ -133,3 +133,26 @@ def test_fps_duplicates_and_zero_rows():
     X[5] = 0.0                                     # zero norm row: treated as distance 1 from all
     p = fps(X, 3)
     assert p.tolist() == [0, 5, 1]
+
+
+def test_hole_fill_hand_example_and_invariants():
+    """n = 10, survivors {0, 2, 3, 5, 7, 9}: K = 6, holes 1 and 4 take movers 7
+    and 9."""
+    from oracle import hole_fill
+    assert hole_fill([0, 2, 3, 5, 7, 9], 10).tolist() == [0, 7, 2, 3, 9, 5]
+    assert hole_fill(list(range(6)), 10).tolist() == list(range(6))      # nothing to move
+    assert hole_fill([4, 5, 6, 7], 8).tolist() == [4, 5, 6, 7]           # every survivor moves
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(rng.integers(1, 80))
+        K = int(rng.integers(0, n + 1))
+        kept = np.sort(rng.choice(n, K, replace=False))
+        src = hole_fill(kept, n)
+        assert sorted(src.tolist()) == kept.tolist()                      # a permutation of the survivors
+        stay = kept[kept < K]
+        assert np.all(src[stay] == stay)                                  # survivors below K do not move
+        moved = int((src != np.arange(K)).sum())
+        assert moved == int((kept >= K).sum()) <= min(K, n - K)
+        # the movers fill the holes in ascending order of both
+        holes = np.setdiff1d(np.arange(K), kept)
+        assert np.all(np.diff(src[holes]) > 0) and np.all(src[holes] >= K)
