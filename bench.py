@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
     ap.add_argument("--graph", type=int, default=0, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
-    ap.add_argument("--call", choices=["split", "fused"], default="fused",
+    ap.add_argument("--call", choices=["split", "fused", "inplace"], default="fused",
                     help="split: kv_evict_score then kv_evict_select_compact; "
-                         "fused: kv_evict_score_select_compact (one kernel per call)")
+                         "fused: kv_evict_score_select_compact (one kernel per call); "
+                         "inplace: kv_evict_score then kv_evict_select_compact_inplace (hole filling)")
     return ap.parse_args()
 
 
@@ -181,8 +182,9 @@ class StepRunner:
         import decode_kv_cache_evict_amd as kv
         self.w, self.states, self.scores, self.kept, self.fps_out = w, states, scores, kept, fps_out
         self.ws_score, self.schedule, self.call = ws_score, schedule, call
-        if call == "fused":
+        if call in ("fused", "inplace"):
             select_group = score_group
+        self.new_len = torch.empty_like(states[0].seg_len)
         L, B, Hkv = w.n_layers, w.batch, w.n_kv_heads
         select_group = max(select_group, score_group)
         self.sgroups = [(g0, min(L, g0 + score_group)) for g0 in range(0, L, score_group)]
@@ -217,6 +219,22 @@ class StepRunner:
         if side is not main:
             side.wait_stream(main)
         kv.beacon_fps_update(st.buf, self.fps_out[0], st.count, self.fps_out[1], w.fps_keep, stream=side)
+        if self.call == "inplace":
+            # scoring, then hole filling within the trigger's own cache; the new
+            # lengths go to a separate array so every step sees the same n
+            for ci, ((_, cache, obs), (_, ccache, _)) in enumerate(zip(sc, cc)):
+                if timing is not None:
+                    timing[ci][0].record(main)
+                kv.kv_evict_score(cache, obs, self.scores, ws=self.ws_score, stream=main)
+                l0, l1 = self.cgroups[ci]
+                seg = slice(l0 * w.batch * w.n_kv_heads, l1 * w.batch * w.n_kv_heads)
+                kv.kv_evict_select_compact_inplace(ccache, self.scores, None, w.n_prefix, w.n_recent,
+                                                   self.new_len[seg], uniform_budget=w.budget, stream=main)
+                if timing is not None:
+                    timing[ci][1].record(main)
+            if side is not main:
+                main.wait_stream(side)
+            return
         if self.call == "fused":
             # one call per layer group: score, select and gather in one kernel;
             # the output cache (K, V, pos, lengths) is the result, no index list
@@ -287,7 +305,7 @@ def measured_traffic(call="split"):
     return float(kv_pairs["traffic_bytes_per_launch"])
 
 
-def step_bytes(w):
+def step_bytes(w, call="fused"):
     """Algorithmic HBM bytes of one trigger (every input read once, every output written once)."""
     S = w.n_layers * w.batch * w.n_kv_heads
     n, keep, d = w.len_hi, w.budget, w.head_dim
@@ -306,9 +324,14 @@ def step_bytes(w):
     b["fused_step"] = (b["score_k"] + b["score_pos"] + b["score_q"] + b["score_out"]
                        + 3 * S * keep * row + S * keep * 4)
     b["score"] = b["score_k"] + b["score_pos"] + b["score_q"] + b["score_out"]
+    # in place (hole filling): scoring, the scores read back, and at most
+    # min(K, n-K) rows per segment moved (K, V, pos read and written)
+    b["inplace_moves"] = 2 * S * min(keep, n - keep) * (2 * row + 4)
+    b["inplace_step"] = b["score"] + b["select_scores"] + b["inplace_moves"]
     # the step's algorithmic bytes: the one-kernel form's (the split form adds
-    # a write and re-read of the scores and a second read of the kept K rows)
-    b["total"] = b["fused_step"] + b["fps"]
+    # a write and re-read of the scores and a second read of the kept K rows);
+    # the in-place form moves only the displaced survivors
+    b["total"] = (b["inplace_step"] if call == "inplace" else b["fused_step"]) + b["fps"]
     return b
 
 
@@ -428,9 +451,9 @@ def main():
     torch.cuda.synchronize()
     sc_ms = sum(t[0].elapsed_time(t[1]) for step in tev for t in step) / (timing_steps * len(runner.cgroups))
     tokens = w.n_layers * w.batch * w.len_hi
-    nb = step_bytes(w)
+    nb = step_bytes(w, args.call)
     dom_layers = runner.cgroups[0][1] - runner.cgroups[0][0]
-    dom_key = "fused_step" if args.call == "fused" else "select_compact"
+    dom_key = {"fused": "fused_step", "split": "select_compact", "inplace": "inplace_step"}[args.call]
     dom_bytes = nb[dom_key] * dom_layers / w.n_layers
     achieved = dom_bytes / (sc_ms * 1e-3) / 1e9
     res = {
@@ -452,13 +475,14 @@ def main():
                      "layers_per_select_call": runner.cgroups[0][1] - runner.cgroups[0][0],
                      "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("kv_evict_score_select_compact (score, radix select and gather in one kernel)"
-                                if args.call == "fused" else
-                                "kv_evict_select_compact (radix select + gather compaction)")
+                     "kernel": {"fused": "kv_evict_score_select_compact (score, radix select and gather in one kernel)",
+                                "split": "kv_evict_select_compact (radix select + gather compaction)",
+                                "inplace": "kv_evict_score + kv_evict_select_compact_inplace (hole filling; at most "
+                                           "min(K, n-K) rows moved per segment)"}[args.call]
                      + f", {dom_layers} layer(s) per launch",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": measured_traffic(args.call) if dom_layers == w.n_layers else None,
+                     "traffic": measured_traffic(args.call) if dom_layers == w.n_layers and args.call in TRAFFIC else None,
                      "bytes_per_launch": dom_bytes,
                      "avg_launch_ms": sc_ms},
     }

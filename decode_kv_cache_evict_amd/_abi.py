@@ -21,7 +21,8 @@ STATUS = {0: "KVE_OK", 1: "KVE_EINVAL", 2: "KVE_ESHAPE", 3: "KVE_EALIAS", 4: "KV
           5: "KVE_EWORKSPACE", 6: "KVE_EDEVICE"}
 EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv_evict_entropy_budgets",
            "kv_evict_wave_budgets",
-           "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_score_select_compact_workspace",
+           "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
+           "kv_evict_score_select_compact_workspace",
            "kv_evict_score_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "kv_rope_apply", "kve_last_error", "kve_abi_version"]
 
@@ -67,6 +68,7 @@ def lib():
             "kv_evict_wave_budgets": (I32, [I32, D, D, I32, I32, P, P]),
             "kv_evict_select_workspace": (SZ, [CP, I32]),
             "kv_evict_select_compact": (I32, [CP, P, P, I64, P, I32, I32, I32, P, CP, P, SZ, P]),
+            "kv_evict_select_compact_inplace": (I32, [CP, P, P, I64, P, I32, I32, I32, P, P]),
             "kv_evict_score_select_compact_workspace": (SZ, [CP, OP, CP, I32]),
             "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
@@ -194,6 +196,14 @@ def kv_evict_select_compact(cache_in, scores, budget, n_prefix, n_recent, cache_
                                          int(scores.numel()), _ptr(budget), int(uniform_budget), int(n_prefix),
                                          int(n_recent), _ptr(kept_idx), ctypes.byref(cache_out), wp, wn,
                                          _stream(stream)))
+
+
+def kv_evict_select_compact_inplace(cache, scores, budget, n_prefix, n_recent, new_len, score_off=None,
+                                    uniform_budget=0, stream=None):
+    """Hole-filling compaction within `cache`; new_len int32 [n_seg] (may be the cache's seg_len tensor)."""
+    _check(lib().kv_evict_select_compact_inplace(ctypes.byref(cache), _ptr(scores), _ptr(score_off),
+                                                 int(scores.numel()), _ptr(budget), int(uniform_budget),
+                                                 int(n_prefix), int(n_recent), _ptr(new_len), _stream(stream)))
 
 
 def kv_evict_score_select_compact_workspace(cache_in, obs, cache_out, have_kept_idx):

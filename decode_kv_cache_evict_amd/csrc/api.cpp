@@ -278,6 +278,58 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   return device_status(kve::launch_select_compact(a, static_cast<hipStream_t>(stream)), "kv_evict_select_compact");
 }
 
+kve_status kv_evict_select_compact_inplace(kve_cache* c, const float* scores, const int64_t* score_off,
+                                           int64_t n_scores, const int32_t* budget, int32_t uniform_budget,
+                                           int32_t n_prefix, int32_t n_recent, int32_t* new_len, void* stream) {
+  kve_status st = check_cache(c, "cache", true);
+  if (st != KVE_OK) return st;
+  if (n_prefix < 0 || n_recent < 0 || n_scores < 0) return fail(KVE_EINVAL, "negative prefix/recent/n_scores");
+  if (c->n_seg > 0 && (!scores || !new_len)) return fail(KVE_EINVAL, "null scores or new_len");
+  if (!budget && uniform_budget < n_prefix + n_recent)
+    return fail(KVE_EBUDGET, "budget %d below prefix %d + recent %d", uniform_budget, n_prefix, n_recent);
+  const size_t rb = rows_bytes(c), pb = size_t(c->n_rows) * 4, ns = size_t(c->n_seg);
+  const void* ins[] = {scores, c->seg_off, budget, score_off};
+  const size_t insz[] = {size_t(n_scores) * 4, ns * 8, budget ? ns * 4 : 0, score_off ? ns * 8 : 0};
+  const void* outs[] = {c->k, c->v, c->pos};
+  const size_t outsz[] = {rb, rb, pb};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "cache array %d overlaps input %d", i, j);
+  // new_len may be the cache's own seg_len (read before it is written, by the same work-group)
+  if (new_len != c->seg_len) {
+    const void* all[] = {c->k, c->v, c->pos, scores, c->seg_off, c->seg_len, budget, score_off};
+    const size_t allsz[] = {rb, rb, pb, size_t(n_scores) * 4, ns * 8, ns * 4, budget ? ns * 4 : 0,
+                            score_off ? ns * 8 : 0};
+    for (int j = 0; j < 8; ++j)
+      if (overlap(new_len, ns * 4, all[j], allsz[j])) return fail(KVE_EALIAS, "new_len overlaps argument %d", j);
+  }
+  if (c->n_seg == 0) return KVE_OK;
+  kve::SelectArgs a{};
+  a.k_in = c->k;
+  a.v_in = c->v;
+  a.pos_in = c->pos;
+  a.in_off = c->seg_off;
+  a.in_len = c->seg_len;
+  a.in_rows = c->n_rows;
+  a.in_max = c->max_seg_len;
+  a.scores = scores;
+  a.score_off = score_off;
+  a.n_scores = n_scores;
+  a.budget = budget;
+  a.uniform_budget = uniform_budget;
+  a.n_prefix = n_prefix;
+  a.n_recent = n_recent;
+  a.k_out = c->k;
+  a.v_out = c->v;
+  a.pos_out = c->pos;
+  a.out_len = new_len;
+  a.n_seg = c->n_seg;
+  a.head_dim = c->head_dim;
+  a.elem_bytes = int32_t(elem_bytes(c->dtype));
+  return device_status(kve::launch_select_inplace(a, static_cast<hipStream_t>(stream)),
+                       "kv_evict_select_compact_inplace");
+}
+
 size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
                                                int32_t have_kept_idx) {
   int32_t rows = 0;

@@ -68,6 +68,8 @@ struct SelectArgs {
   int32_t n_seg, head_dim, elem_bytes;
 };
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st);
+// In place: k_out/v_out/pos_out are the input cache; out_len receives the new lengths.
+hipError_t launch_select_inplace(const SelectArgs& a, hipStream_t st);
 
 // weight_form 0: weights as given; 1: 1 - weight (inverse entropy).
 hipError_t launch_budgets(const float* w, const int32_t* total, const int32_t* cap, int32_t batch,

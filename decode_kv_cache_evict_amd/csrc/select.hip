@@ -10,6 +10,7 @@
 // ballot scan.
 // compact: a grid over (segment, 64-row tiles) that gathers kept K/V rows with
 // 16-byte loads and stores, and their positions.
+// inplace: hole filling within the input cache (one work-group per segment).
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -141,7 +142,134 @@ hipError_t launch_compact(const SelectArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// In-place compaction by hole filling, one work-group per segment: the same
+// protected top-K threshold as select_kernel, then the survivors in [K, n)
+// move, in ascending order, into the evicted slots of [0, K), in ascending
+// order (survivors below K stay).  Slots are ranked block by block (512 at a
+// time) into two short lists in LDS, pending holes and pending movers, which
+// are paired and copied as they fill; at most min(K, n - K) rows move.  Mover
+// rows are only read and hole rows only written, so no row is both.
+template <int CPR>
+__global__ __launch_bounds__(kSelBlock) void inplace_kernel(SelectArgs a) {
+  constexpr int RPP = kSelBlock / CPR;      // rows per copy pass
+  constexpr int UNR = 4;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int wtot_a[kSelWaves], wtot_b[kSelWaves];
+  __shared__ int hl[kSelBlock], ml[kSelBlock];   // pending holes / movers (slots), ascending
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t io = a.in_off[s];
+  const int n = a.in_len[s];
+  const bool in_ok = n >= 0 && n <= a.in_max && io >= 0 && io + n <= a.in_rows;
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  const int64_t so = a.score_off ? a.score_off[s] : io;
+  const bool sc_ok = so >= 0 && so + n <= a.n_scores;
+  const bool bud_ok = K >= n || (K >= P + R && K >= 0);
+  if (!(in_ok && sc_ok && bud_ok)) {
+    if (tid == 0) a.out_len[s] = -1;
+    return;
+  }
+  if (K >= n) {                              // every row survives where it is
+    if (tid == 0) a.out_len[s] = n;
+    return;
+  }
+  const float* sc = a.scores + so;
+  auto key_at = [&](int j) { return float_order_key(sc[j]); };
+  uint32_t T, kk;
+  radix_threshold<kSelBlock>(key_at, P, n, R, K - P - R, hist, sh, T, kk);
+  // candidates equal to T below K: the tie rank the mover scan starts from
+  int eq_lo = 0;
+  for (int j = P + tid; j < min(K, n - R); j += kSelBlock) eq_lo += key_at(j) == T;
+  eq_lo = block_sum<kSelBlock>(eq_lo, wtot_a);
+
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4* kc = static_cast<u32x4*>(a.k_out);
+  u32x4* vc = static_cast<u32x4*>(a.v_out);
+  const int part = tid % CPR, rsub = tid / CPR;
+  // one block of slots [j0, j1): keep flags with running tie ranks; returns
+  // this thread's flag for "wanted" (a hole below K or a survivor at or above K)
+  auto scan_block = [&](int j0, int j1, int& eq_seen, bool want_kept, int* list, int& count) {
+    const int j = j0 + tid;
+    const bool in = j < j1;
+    const bool cand = in && j >= P && j < n - R;
+    const uint32_t key = cand ? key_at(j) : 0u;
+    const bool eq = cand && key == T;
+    int eq_tot;
+    const int eq_rank = eq_seen + block_flag_scan<kSelBlock>(eq, wtot_a, eq_tot);
+    const bool keep = !cand || key > T || (eq && uint32_t(eq_rank) < kk);
+    const bool want = in && (keep == want_kept);
+    int tot;
+    const int at = block_flag_scan<kSelBlock>(want, wtot_b, tot);
+    if (want) list[at] = j;
+    count = tot;
+    eq_seen += eq_tot;
+  };
+  int hc = 0, h_eq = 0, nH = 0;              // holes: next slot to scan, ties seen, pending
+  int mc = K, m_eq = eq_lo, nM = 0;          // movers
+  for (;;) {
+    if (nH == 0 && hc < K) {
+      scan_block(hc, min(hc + kSelBlock, K), h_eq, false, hl, nH);
+      hc = min(hc + kSelBlock, K);
+    }
+    if (nM == 0 && mc < n) {
+      scan_block(mc, min(mc + kSelBlock, n), m_eq, true, ml, nM);
+      mc = min(mc + kSelBlock, n);
+    }
+    __syncthreads();
+    if (nH == 0 || nM == 0) {
+      if ((nH == 0 && hc >= K) || (nM == 0 && mc >= n)) break;
+      continue;
+    }
+    const int p = min(nH, nM);
+    for (int r0 = 0; r0 < p; r0 += RPP * UNR) {
+      u32x4 kb[UNR], vb[UNR];
+      int src[UNR], dst[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int r = r0 + u * RPP + rsub;
+        src[u] = r < p ? ml[r] : -1;
+        dst[u] = r < p ? hl[r] : -1;
+        if (src[u] >= 0) {
+          kb[u] = __builtin_nontemporal_load(&kc[(io + src[u]) * CPR + part]);
+          vb[u] = __builtin_nontemporal_load(&vc[(io + src[u]) * CPR + part]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (src[u] >= 0) {
+          __builtin_nontemporal_store(kb[u], &kc[(io + dst[u]) * CPR + part]);
+          __builtin_nontemporal_store(vb[u], &vc[(io + dst[u]) * CPR + part]);
+          if (part == 0) a.pos_out[io + dst[u]] = a.pos_in[io + src[u]];
+        }
+    }
+    // drop the p paired entries from both lists
+    const int h_rest = tid < nH - p ? hl[p + tid] : 0;
+    const int m_rest = tid < nM - p ? ml[p + tid] : 0;
+    __syncthreads();
+    if (tid < nH - p) hl[tid] = h_rest;
+    if (tid < nM - p) ml[tid] = m_rest;
+    nH -= p;
+    nM -= p;
+    __syncthreads();
+  }
+  if (tid == 0) a.out_len[s] = K;
+}
+
 }  // namespace
+
+hipError_t launch_select_inplace(const SelectArgs& a, hipStream_t st) {
+  if (a.n_seg == 0) return hipSuccess;
+  const dim3 grid(unsigned(a.n_seg));
+  switch (a.head_dim * a.elem_bytes / 16) {
+    case 8: hipLaunchKernelGGL(inplace_kernel<8>, grid, dim3(kSelBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(inplace_kernel<16>, grid, dim3(kSelBlock), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(inplace_kernel<32>, grid, dim3(kSelBlock), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st) {
   if (a.n_seg == 0) return hipSuccess;

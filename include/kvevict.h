@@ -181,6 +181,25 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
                                    int32_t n_prefix, int32_t n_recent, int32_t* kept_idx,
                                    kve_cache* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * kv_evict_select_compact_inplace — the same per-segment selection as
+ * kv_evict_select_compact (same budget, protection and tie rules), compacted
+ * within the cache c itself by hole filling: with K survivors, those already
+ * in slots [0, K) stay, and the survivors in [K, n), in ascending slot order,
+ * move into the evicted slots of [0, K), in ascending slot order (K, V and pos
+ * rows; at most min(K, n-K) rows move per segment).  Rows [K, n) are left as
+ * they were.  The survivors are therefore not in slot order; attention does
+ * not depend on the order of the cached rows (BeaconKV "📊 实验": eviction is
+ * permanent; each row keeps its position, which carries RoPE and causality).
+ * new_len: [n_seg] int32, receives K (n when K >= n, -1 for a segment rejected
+ * as in kv_evict_select_compact); it may be c->seg_len itself.  No workspace.
+ * Errors: EINVAL, ESHAPE, EALIAS (scores/budget/score_off/seg_off overlapping the
+ * cache rows; new_len overlapping anything but c->seg_len), EBUDGET, EDEVICE.
+ */
+kve_status kv_evict_select_compact_inplace(kve_cache* c, const float* scores, const int64_t* score_off,
+                                           int64_t n_scores, const int32_t* budget, int32_t uniform_budget,
+                                           int32_t n_prefix, int32_t n_recent, int32_t* new_len, void* stream);
+
 /* Workspace bytes kv_evict_score_select_compact needs. */
 size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
                                                int32_t have_kept_idx);

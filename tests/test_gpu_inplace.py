@@ -1,0 +1,119 @@
+"""In-place hole-filling compaction (kv_evict_select_compact_inplace) against
+the oracle: the survivors are the oracle's kept set (ties within tolerance),
+their layout is exactly oracle.hole_fill of that set, the moved rows are
+byte-exact copies, and rows beyond the new length are untouched."""
+import numpy as np
+import pytest
+import torch
+
+import decode_kv_cache_evict_amd as kv
+import oracle
+from tests.gpu_side import cache_of, device_layer, score_layer
+from tests.oracle_side import oracle_cache_keys, oracle_layer_scores
+from tests.parity import kept_matches
+from workloads import get_workload, make_layer
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "qwen3-4b-1l": (get_workload("qwen3-4b-1l").scaled(batch=4), 1792),
+    "llama-ragged": (get_workload("r1-llama-8b").scaled(batch=3, len_lo=700, len_hi=1100, n_layers=1), 640),
+    "long-5k": (get_workload("long-65k").scaled(batch=1, len_lo=5000, len_hi=5000), 1024),
+    "tiny-f32": (get_workload("tiny-f32"), 448),
+    "d64-bf16": (get_workload("tiny-f32").scaled(dtype="bf16", batch=3, len_lo=900, len_hi=2100), 700),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.lib()
+
+
+def _ints(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+def _run(w, L, D, budgets, uniform, alias):
+    """Score, then compact in place on a copy of the cache; returns the copy."""
+    scores, _ = score_layer(D, w)
+    C = dict(D, k=D["k"].clone(), v=D["v"].clone(), pos=D["pos"].clone(), seg_len=D["seg_len"].clone())
+    new_len = C["seg_len"] if alias else torch.full_like(C["seg_len"], -9)
+    kv.kv_evict_select_compact_inplace(cache_of(C, w), scores, budgets, w.n_prefix, w.n_recent, new_len,
+                                       uniform_budget=uniform)
+    torch.cuda.synchronize()
+    return C, new_len.cpu().numpy()
+
+
+def _check(w, L, D, C, new_len, budgets_np, s_orc):
+    k0, v0, p0 = _ints(D["k"]), _ints(D["v"]), D["pos"].cpu().numpy()
+    k1, v1, p1 = _ints(C["k"]), _ints(C["v"]), C["pos"].cpu().numpy()
+    moved = 0
+    for s in range(len(L["seg_len"])):
+        o, n, K = int(L["seg_off"][s]), int(L["seg_len"][s]), int(budgets_np[s])
+        if K < n and K < w.n_prefix + w.n_recent:
+            assert new_len[s] == -1
+            assert np.array_equal(p1[o:o + n], p0[o:o + n])
+            continue
+        m = min(K, n)
+        assert new_len[s] == m, (s, new_len[s], m)
+        src = p1[o:o + m] - p0[o]                  # positions are the slots in these segments
+        kept = np.sort(src)
+        ok, _, msg = kept_matches(kept, s_orc[o:o + n], n, K, w.n_prefix, w.n_recent)
+        assert ok, f"segment {s}: {msg}"
+        assert np.array_equal(src, oracle.hole_fill(kept, n)), f"segment {s}: layout"
+        assert np.array_equal(k1[o:o + m], k0[o + src]) and np.array_equal(v1[o:o + m], v0[o + src])
+        assert np.array_equal(k1[o + m:o + n], k0[o + m:o + n]) and np.array_equal(p1[o + m:o + n], p0[o + m:o + n])
+        moved += int((src != np.arange(m)).sum())
+    return moved
+
+
+@pytest.mark.parametrize("alias", [False, True])
+@pytest.mark.parametrize("name", list(CASES))
+def test_inplace_matches_oracle(name, alias):
+    w, budget = CASES[name]
+    L = make_layer(w, 0)
+    assert all(np.array_equal(L["pos"][int(L["seg_off"][s]):int(L["seg_off"][s]) + int(L["seg_len"][s])].numpy(),
+                              np.arange(int(L["seg_len"][s]))) for s in range(len(L["seg_len"])))
+    D = device_layer(L, w)
+    s_orc = oracle_layer_scores(L, w, oracle_cache_keys(L, w))
+    C, new_len = _run(w, L, D, None, budget, alias)
+    moved = _check(w, L, D, C, new_len, np.full(len(L["seg_len"]), budget), s_orc)
+    bound = sum(min(budget, int(n) - budget) for n in L["seg_len"] if int(n) > budget)
+    assert 0 < moved <= bound
+    print(f"{name}: {moved} rows moved of {int(L['seg_len'].sum())} (at most {bound})")
+
+
+def test_inplace_per_segment_budgets_and_degenerate_segments():
+    w, _ = CASES["llama-ragged"]
+    L = make_layer(w, 0)
+    D = device_layer(L, w)
+    s_orc = oracle_layer_scores(L, w, oracle_cache_keys(L, w))
+    S = len(L["seg_len"])
+    lens = [int(x) for x in L["seg_len"]]
+    rng = np.random.default_rng(5)
+    bud = rng.integers(w.n_prefix + w.n_recent, 1200, size=S)
+    bud[0] = lens[0]                       # K == n
+    bud[1] = lens[1] + 7                   # K > n
+    bud[2] = w.n_prefix + w.n_recent - 1   # rejected
+    bud[3] = w.n_prefix + w.n_recent       # only the protected slots survive
+    bud[4] = lens[4] - 1                   # one eviction
+    budget = torch.tensor(bud, dtype=torch.int32, device="cuda")
+    C, new_len = _run(w, L, D, budget, 0, False)
+    _check(w, L, D, C, new_len, bud, s_orc)
+
+
+def test_inplace_rejects_overlaps():
+    w, budget = CASES["llama-ragged"]
+    L = make_layer(w, 0)
+    D = device_layer(L, w)
+    scores = D["k"].view(torch.float32).view(-1)[:D["k"].shape[0]]    # scores inside the key rows
+    nl = torch.zeros_like(D["seg_len"])
+    with pytest.raises(kv.KveError) as ei:
+        kv.kv_evict_select_compact_inplace(cache_of(D, w), scores, None, 4, 16, nl, uniform_budget=budget)
+    assert ei.value.name == "KVE_EALIAS"
+    with pytest.raises(kv.KveError) as ei:
+        kv.kv_evict_select_compact_inplace(cache_of(D, w), torch.zeros(D["k"].shape[0], device="cuda"), None, 4, 16,
+                                           nl, uniform_budget=19)
+    assert ei.value.name == "KVE_EBUDGET"
