@@ -18,7 +18,7 @@ __all__ = [
     "segment_scores", "layer_scores", "normalized_entropy", "waterfill",
     "largest_remainder", "head_budgets", "layer_wave_budgets", "select_kept",
     "compact_rows", "fps", "fps_acceptable", "epikv_g", "rolling_z", "rolling_mean", "epikv_score",
-    "layer_select_compact", "head_weights", "hole_fill",
+    "layer_select_compact", "head_weights", "hole_fill", "decode_attention",
 ]
 
 
@@ -382,6 +382,29 @@ def fps_acceptable(X, picks, rtol, atol=1e-6):
         taken[j] = True
         dist = np.minimum(dist, 1.0 - U @ U[j])
     return True, -1
+
+
+# ------------------------------------------------------ decode attention
+def decode_attention(k, v, q):
+    """Attention of the new token's queries over one KV head's cache: for each
+    query row, softmax(q . k / sqrt(d)) over every cached row, applied to V.
+    Returns (out [rows, d], lse [rows], natural log).
+
+    The step that follows eviction in the decode loop (EPIKV page, part 4:
+    the eviction score stays compatible with a fused attention kernel; the
+    BeaconKV page's throughput figures are decode throughput over the
+    compacted cache).  Every cached row is visible to the new token, and the
+    result does not depend on the order of the rows."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
+    logits = q @ k.T / math.sqrt(k.shape[1])
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e / l) @ v, (m + np.log(l))[:, 0]
 
 
 # ------------------------------------------------------ O10: EPIKV
