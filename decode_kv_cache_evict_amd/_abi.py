@@ -24,7 +24,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
            "kv_evict_score_select_compact_workspace",
            "kv_evict_score_select_compact", "beacon_fps_update",
-           "epikv_workspace_size", "epikv_score", "kv_rope_apply", "kve_last_error", "kve_abi_version"]
+           "epikv_workspace_size", "epikv_score", "kv_decode_attention_workspace", "kv_decode_attention",
+           "kv_rope_apply", "kve_last_error", "kve_abi_version"]
 
 
 class KveError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
             "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, I32, P, P, P, SZ, P]),
+            "kv_decode_attention_workspace": (SZ, [CP, I32]),
+            "kv_decode_attention": (I32, [CP, P, I32, P, P, P, SZ, P]),
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
             "kve_last_error": (ctypes.c_char_p, []),
             "kve_abi_version": (I32, []),
@@ -243,6 +246,20 @@ def epikv_score(h_a, h_b, window, eps, scores, g_out=None, ws=None, stream=None,
     wp, wn = _aligned(ws)
     _check(lib().epikv_score(_ptr(h_a), _ptr(h_b), int(B), int(T), int(D), int(window), float(eps), int(form),
                              _ptr(g_out), _ptr(scores), wp, wn, _stream(stream)))
+
+
+def kv_decode_attention_workspace(cache, n_q_heads):
+    return int(lib().kv_decode_attention_workspace(ctypes.byref(cache), int(n_q_heads)))
+
+
+def kv_decode_attention(cache, q, out, lse=None, ws=None, stream=None):
+    """q [B, Hq, d] rotated (cache dtype); out fp32 [B, Hq, d]; lse optional fp32 [B, Hq]."""
+    n_q = int(q.shape[1])
+    if ws is None:
+        ws = _ws(kv_decode_attention_workspace(cache, n_q), out.device)
+    wp, wn = _aligned(ws)
+    _check(lib().kv_decode_attention(ctypes.byref(cache), _ptr(q), n_q, _ptr(out), _ptr(lse), wp, wn,
+                                     _stream(stream)))
 
 
 def kv_rope_apply(src, dst, pos, rope_theta, stream=None):

@@ -464,6 +464,56 @@ kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t 
                        "epikv_score");
 }
 
+size_t kv_decode_attention_workspace(const kve_cache* c, int32_t n_q_heads) {
+  if (check_cache(c, "cache", true) != KVE_OK || n_q_heads < c->n_kv_heads || n_q_heads % c->n_kv_heads) return 0;
+  return kve::attn_workspace_bytes(c->n_seg, c->max_seg_len, n_q_heads / c->n_kv_heads, c->head_dim);
+}
+
+kve_status kv_decode_attention(const kve_cache* c, const void* q, int32_t n_q_heads, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  kve_status st = check_cache(c, "cache", true);
+  if (st != KVE_OK) return st;
+  if (n_q_heads < c->n_kv_heads || n_q_heads % c->n_kv_heads != 0)
+    return fail(KVE_ESHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads, c->n_kv_heads);
+  const int32_t group = n_q_heads / c->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return fail(KVE_ESHAPE, "group %d not 1, 2, 4 or 8", group);
+  if (c->n_seg > 0 && (!q || !out)) return fail(KVE_EINVAL, "null q or out");
+  const size_t need = kve::attn_workspace_bytes(c->n_seg, c->max_seg_len, group, c->head_dim);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  const size_t batch = size_t(c->n_seg / c->n_kv_heads);
+  const size_t ob = batch * n_q_heads * c->head_dim * 4, lb = batch * n_q_heads * 4;
+  const size_t qb = batch * n_q_heads * c->head_dim * elem_bytes(c->dtype);
+  const void* ins[] = {c->k, c->v, c->seg_off, c->seg_len, q};
+  const size_t insz[] = {rows_bytes(c), rows_bytes(c), size_t(c->n_seg) * 8, size_t(c->n_seg) * 4, qb};
+  const void* outs[] = {out, lse, ws};
+  const size_t outsz[] = {ob, lse ? lb : 0, need};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
+  if (c->n_seg == 0) return KVE_OK;
+  kve::AttnArgs a{};
+  a.k = c->k;
+  a.v = c->v;
+  a.seg_off = c->seg_off;
+  a.seg_len = c->seg_len;
+  a.n_rows = c->n_rows;
+  a.n_seg = c->n_seg;
+  a.n_kv = c->n_kv_heads;
+  a.max_seg_len = c->max_seg_len;
+  a.head_dim = c->head_dim;
+  a.dtype = c->dtype;
+  a.q = q;
+  a.n_q = n_q_heads;
+  a.group = group;
+  a.out = out;
+  a.lse = lse;
+  a.part = static_cast<float*>(ws);
+  return device_status(kve::launch_decode_attention(a, static_cast<hipStream_t>(stream)), "kv_decode_attention");
+}
+
 kve_status kv_rope_apply(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
                          double rope_theta, int32_t dtype, void* stream) {
   if (dtype != KVE_BF16 && dtype != KVE_F32) return fail(KVE_EINVAL, "bad dtype %d", dtype);

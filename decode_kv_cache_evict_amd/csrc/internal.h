@@ -86,6 +86,20 @@ size_t epikv_ws_bytes(int32_t batch, int32_t T);
 hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t T, int32_t d_model,
                         int32_t window, float eps, int32_t form, float* g_out, float* scores, void* ws, hipStream_t st);
 
+struct AttnArgs {
+  const void* k; const void* v;
+  const int64_t* seg_off; const int32_t* seg_len;
+  int64_t n_rows; int32_t n_seg, n_kv, max_seg_len, head_dim, dtype;
+  const void* q;          // [B, n_q, head_dim] rotated queries of the new token, cache dtype
+  int32_t n_q, group;
+  float* out;             // [B, n_q, head_dim]
+  float* lse;             // [B, n_q] or null
+  float* part;            // [n_seg, n_chunks, group, head_dim + 2] workspace
+  int32_t n_chunks;
+};
+size_t attn_workspace_bytes(int32_t n_seg, int32_t max_seg_len, int32_t group, int32_t head_dim);
+hipError_t launch_decode_attention(AttnArgs& a, hipStream_t st);
+
 hipError_t launch_rope_rows(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
                             double theta, int32_t dtype, hipStream_t st);
 

@@ -266,6 +266,27 @@ kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t 
                        int32_t window, float eps, int32_t form, float* g_out, float* scores,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes kv_decode_attention needs. */
+size_t kv_decode_attention_workspace(const kve_cache* c, int32_t n_q_heads);
+
+/*
+ * kv_decode_attention — the decode step's attention over the (compacted) cache,
+ * the step that follows eviction (EPIKV 方法论 part 4: the eviction score stays
+ * compatible with a fused attention kernel; BeaconKV "📊 实验" reports decode
+ * throughput over the compacted cache): for every request b and query head h,
+ *   out[b, h] = softmax_j(q[b, h] . k_j / sqrt(head_dim)) v_j
+ * over all rows j of segment b*n_kv_heads + h/(n_q_heads/n_kv_heads), in any
+ * row order (the in-place compaction's layout works as is).  q: [batch,
+ * n_q_heads, head_dim] rotated queries of the new token, cache dtype.  out:
+ * fp32 [batch, n_q_heads, head_dim]; lse: optional fp32 [batch, n_q_heads],
+ * natural-log normaliser.  fp32 accumulation.  An empty segment (or one whose
+ * metadata is out of range) gives zeros and lse = -inf.  n_q_heads/n_kv_heads
+ * must be 1, 2, 4 or 8.
+ * Errors: EINVAL, ESHAPE, EALIAS, EWORKSPACE, EDEVICE.
+ */
+kve_status kv_decode_attention(const kve_cache* c, const void* q, int32_t n_q_heads, float* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /*
  * kv_rope_apply — write keys into a cache the way a decoder layer does: rotate
  * fp32 pre-RoPE rows src[n_rows, head_dim] to positions pos[n_rows] (half-split
