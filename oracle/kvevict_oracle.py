@@ -18,7 +18,8 @@ __all__ = [
     "segment_scores", "layer_scores", "normalized_entropy", "waterfill",
     "largest_remainder", "head_budgets", "layer_wave_budgets", "select_kept",
     "compact_rows", "fps", "fps_acceptable", "epikv_g", "rolling_z", "rolling_mean", "epikv_score",
-    "layer_select_compact", "head_weights", "hole_fill", "decode_attention",
+    "layer_select_compact", "head_weights", "hole_fill", "decode_attention", "sentence_means",
+    "pss_later_max", "skipkv_token_scores",
 ]
 
 
@@ -382,6 +383,52 @@ def fps_acceptable(X, picks, rtol, atol=1e-6):
         taken[j] = True
         dist = np.minimum(dist, 1.0 - U @ U[j])
     return True, -1
+
+
+# ------------------------------------------------------ SkipKV sentence redundancy
+def sentence_means(h, starts):
+    """Sentence embeddings: the mean of the last-layer hidden states over each
+    sentence's tokens, sentence i = tokens [starts[i], starts[i+1]).
+
+    SkipKV page, 核心方法 §4.1 (and observation 2: the mean of last-layer
+    hidden states stands in for a sentence embedding)."""
+    h = np.asarray(h, dtype=np.float64)
+    starts = np.asarray(starts, dtype=np.int64)
+    return np.stack([h[starts[i]:starts[i + 1]].mean(axis=0) for i in range(len(starts) - 1)]) \
+        if len(starts) > 1 else np.zeros((0, h.shape[1]))
+
+
+def pss_later_max(e):
+    """For each sentence i, the largest pairwise sentence similarity (cosine of
+    the sentence means) with any LATER sentence j > i; -1 for the last one.
+
+    SkipKV §4.1: of a redundant pair (PSS >= tau) the earlier sentence is the
+    one marked evictable, so what matters for sentence i is its most similar
+    successor.  READING: a zero-norm mean has cosine 0 with everything."""
+    e = np.asarray(e, dtype=np.float64)
+    S = e.shape[0]
+    nrm = np.sqrt((e * e).sum(axis=1))
+    out = np.full(S, -1.0)
+    for i in range(S):
+        for j in range(i + 1, S):
+            den = nrm[i] * nrm[j]
+            c = float(e[i] @ e[j]) / den if den > 0 else 0.0
+            out[i] = max(out[i], c)
+    return out
+
+
+def skipkv_token_scores(pss_max, starts, T):
+    """Per-token eviction score from the sentence redundancy: token t of sentence
+    i scores 1 - max(0, pss_max[i]) (a sentence that nearly repeats a later one
+    scores near 0 and goes first, whole sentences together); tokens after the
+    last complete sentence score 1.  READING: the page's combined score (its
+    eq. 6, with token importance and a weight lambda) is not printed; this is
+    the sentence term alone, so this score is partly unpinned."""
+    starts = np.asarray(starts, dtype=np.int64)
+    sc = np.ones(int(T))
+    for i in range(len(starts) - 1):
+        sc[starts[i]:starts[i + 1]] = 1.0 - max(0.0, float(pss_max[i]))
+    return sc
 
 
 # ------------------------------------------------------ decode attention
