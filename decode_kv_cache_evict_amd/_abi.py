@@ -24,7 +24,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
            "kv_evict_score_select_compact_workspace",
            "kv_evict_score_select_compact", "beacon_fps_update",
-           "epikv_workspace_size", "epikv_score", "kv_decode_attention_workspace", "kv_decode_attention",
+           "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
+           "kv_decode_attention_workspace", "kv_decode_attention",
            "kv_rope_apply", "kve_last_error", "kve_abi_version"]
 
 
@@ -75,6 +76,8 @@ def lib():
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
             "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, I32, P, P, P, SZ, P]),
+            "skipkv_workspace_size": (SZ, [I32, I32, I32]),
+            "skipkv_sentence_scores": (I32, [P, I32, I32, I32, P, P, I32, F, P, P, P, P, SZ, P]),
             "kv_decode_attention_workspace": (SZ, [CP, I32]),
             "kv_decode_attention": (I32, [CP, P, I32, P, P, P, SZ, P]),
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
@@ -246,6 +249,23 @@ def epikv_score(h_a, h_b, window, eps, scores, g_out=None, ws=None, stream=None,
     wp, wn = _aligned(ws)
     _check(lib().epikv_score(_ptr(h_a), _ptr(h_b), int(B), int(T), int(D), int(window), float(eps), int(form),
                              _ptr(g_out), _ptr(scores), wp, wn, _stream(stream)))
+
+
+def skipkv_workspace_size(batch, max_sent, d_model):
+    return int(lib().skipkv_workspace_size(int(batch), int(max_sent), int(d_model)))
+
+
+def skipkv_sentence_scores(h, starts, n_sent, tau, pss_max, token_scores, marks=None, ws=None, stream=None):
+    """h bf16 [B, T, d_model]; starts int32 [B, max_sent + 1]; n_sent int32 [B];
+    pss_max fp32 [B, max_sent]; token_scores fp32 [B, T]; marks optional int32 [B, max_sent]."""
+    B, T, Dm = h.shape
+    max_sent = int(starts.shape[1]) - 1
+    if ws is None:
+        ws = _ws(skipkv_workspace_size(B, max_sent, Dm), token_scores.device)
+    wp, wn = _aligned(ws)
+    _check(lib().skipkv_sentence_scores(_ptr(h), int(B), int(T), int(Dm), _ptr(starts), _ptr(n_sent), max_sent,
+                                        float(tau), _ptr(pss_max), _ptr(marks), _ptr(token_scores), wp, wn,
+                                        _stream(stream)))
 
 
 def kv_decode_attention_workspace(cache, n_q_heads):

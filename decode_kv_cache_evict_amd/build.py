@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
-SOURCES = ["api.cpp", "score.hip", "select.hip", "budgets.hip", "fps.hip", "epikv.hip", "rope.hip", "attention.hip"]
+SOURCES = ["api.cpp", "score.hip", "select.hip", "budgets.hip", "fps.hip", "epikv.hip", "rope.hip", "attention.hip", "skipkv.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

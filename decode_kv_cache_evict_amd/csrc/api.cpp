@@ -464,6 +464,53 @@ kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t 
                        "epikv_score");
 }
 
+size_t skipkv_workspace_size(int32_t batch, int32_t max_sent, int32_t d_model) {
+  if (batch < 0 || max_sent < 0 || d_model < 0) return 0;
+  return kve::skipkv_ws_bytes(batch, max_sent, d_model);
+}
+
+kve_status skipkv_sentence_scores(const void* h, int32_t batch, int32_t T, int32_t d_model, const int32_t* starts,
+                                  const int32_t* n_sent, int32_t max_sent, float tau, float* pss_max, int32_t* marks,
+                                  float* token_scores, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 0 || T < 0 || max_sent < 0) return fail(KVE_EINVAL, "negative batch, T or max_sent");
+  if (d_model < 64 || d_model > 16384 || d_model % 64 != 0)
+    return fail(KVE_ESHAPE, "d_model %d not a multiple of 64 in [64, 16384]", d_model);
+  if (max_sent > 65535) return fail(KVE_ESHAPE, "max_sent %d > 65535", max_sent);
+  if (!(tau == tau)) return fail(KVE_EINVAL, "tau is NaN");
+  const size_t nt = size_t(batch) * T, nsnt = size_t(batch) * max_sent;
+  if (batch > 0 && (!starts || !n_sent || !token_scores || (nsnt > 0 && !pss_max) || (T > 0 && !h)))
+    return fail(KVE_EINVAL, "null pointer");
+  if (!aligned16(h)) return fail(KVE_EINVAL, "hidden states not 16-byte aligned");
+  const size_t need = kve::skipkv_ws_bytes(batch, max_sent, d_model);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
+  const void* ins[] = {h, starts, n_sent};
+  const size_t insz[] = {nt * d_model * 2, nsnt + batch, size_t(batch) * 4};
+  const void* outs[] = {pss_max, marks, token_scores, ws};
+  const size_t outsz[] = {nsnt * 4, marks ? nsnt * 4 : 0, nt * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], j == 1 ? insz[j] * 4 : insz[j]))
+        return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
+  if (batch == 0) return KVE_OK;
+  kve::SkipArgs a{};
+  a.h = h;
+  a.starts = starts;
+  a.n_sent = n_sent;
+  a.batch = batch;
+  a.T = T;
+  a.d_model = d_model;
+  a.max_sent = max_sent;
+  a.tau = tau;
+  a.pss_max = pss_max;
+  a.marks = marks;
+  a.token_scores = token_scores;
+  return device_status(kve::launch_skipkv(a, ws, static_cast<hipStream_t>(stream)), "skipkv_sentence_scores");
+}
+
 size_t kv_decode_attention_workspace(const kve_cache* c, int32_t n_q_heads) {
   if (check_cache(c, "cache", true) != KVE_OK || n_q_heads < c->n_kv_heads || n_q_heads % c->n_kv_heads) return 0;
   return kve::attn_workspace_bytes(c->n_seg, c->max_seg_len, n_q_heads / c->n_kv_heads, c->head_dim);

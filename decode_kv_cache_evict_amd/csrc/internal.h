@@ -100,6 +100,21 @@ struct AttnArgs {
 size_t attn_workspace_bytes(int32_t n_seg, int32_t max_seg_len, int32_t group, int32_t head_dim);
 hipError_t launch_decode_attention(AttnArgs& a, hipStream_t st);
 
+struct SkipArgs {
+  const void* h;          // [batch, T, d_model] bf16 last-layer hidden states
+  const int32_t* starts;  // [batch, max_sent + 1] sentence boundaries
+  const int32_t* n_sent;  // [batch] complete sentences
+  int32_t batch, T, d_model, max_sent;
+  float tau;
+  float* pss_max;         // [batch, max_sent]
+  int32_t* marks;         // [batch, max_sent] or null
+  float* token_scores;    // [batch, T]
+  float* emb;             // [batch, max_sent, d_model] unit sentence means (workspace)
+  uint32_t* pss_key;      // [batch, max_sent] order keys of the running maxima (workspace)
+};
+size_t skipkv_ws_bytes(int32_t batch, int32_t max_sent, int32_t d_model);
+hipError_t launch_skipkv(SkipArgs& a, void* ws, hipStream_t st);
+
 hipError_t launch_rope_rows(const float* src, void* dst, const int32_t* pos, int64_t n_rows, int32_t head_dim,
                             double theta, int32_t dtype, hipStream_t st);
 

@@ -266,6 +266,36 @@ kve_status epikv_score(const void* h_a, const void* h_b, int32_t batch, int32_t 
                        int32_t window, float eps, int32_t form, float* g_out, float* scores,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes skipkv_sentence_scores needs. */
+size_t skipkv_workspace_size(int32_t batch, int32_t max_sent, int32_t d_model);
+
+/*
+ * skipkv_sentence_scores — SkipKV page (核心方法 §4.1): sentence-level
+ * redundancy.  Sentence i of request b covers tokens [starts[b][i],
+ * starts[b][i+1]) (starts: [batch, max_sent + 1] int32 device, n_sent[b] <=
+ * max_sent complete sentences; a reversed or out-of-range span counts as an
+ * empty sentence).  Its embedding is the mean of its tokens' last-layer hidden
+ * states h ([batch, T, d_model] bf16, fp32 sums); the pairwise sentence
+ * similarity (PSS) is the cosine of two embeddings (0 for an empty or zero
+ * embedding).  Outputs:
+ *   pss_max[b][i]      the largest PSS of sentence i with a later sentence j > i
+ *                      (-1 when there is none, also for i >= n_sent[b]);
+ *   marks[b][i]        optional: 1 if pss_max >= tau (the earlier sentence of a
+ *                      redundant pair is the evictable one; the page uses 0.95);
+ *   token_scores[b][t] 1 - max(0, pss_max) of token t's sentence, 1 after the
+ *                      last complete sentence — higher keeps, whole sentences
+ *                      go together.  The page's combined score (its eq. 6,
+ *                      with token importance weighted by lambda) is not
+ *                      printed; this is the sentence term alone.
+ * token_scores feeds kv_evict_select_compact through score_off (one score per
+ * token shared by every KV head of a request).  d_model: a multiple of 64 in
+ * [64, 16384]; h 16-byte aligned.
+ * Errors: EINVAL, ESHAPE, EALIAS, EWORKSPACE, EDEVICE.
+ */
+kve_status skipkv_sentence_scores(const void* h, int32_t batch, int32_t T, int32_t d_model, const int32_t* starts,
+                                  const int32_t* n_sent, int32_t max_sent, float tau, float* pss_max,
+                                  int32_t* marks, float* token_scores, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes kv_decode_attention needs. */
 size_t kv_decode_attention_workspace(const kve_cache* c, int32_t n_q_heads);
 

@@ -394,8 +394,11 @@ def sentence_means(h, starts):
     hidden states stands in for a sentence embedding)."""
     h = np.asarray(h, dtype=np.float64)
     starts = np.asarray(starts, dtype=np.int64)
-    return np.stack([h[starts[i]:starts[i + 1]].mean(axis=0) for i in range(len(starts) - 1)]) \
-        if len(starts) > 1 else np.zeros((0, h.shape[1]))
+    out = np.zeros((max(len(starts) - 1, 0), h.shape[1]))
+    for i in range(len(starts) - 1):
+        if starts[i + 1] > starts[i]:            # READING: an empty sentence has a zero embedding
+            out[i] = h[starts[i]:starts[i + 1]].mean(axis=0)
+    return out
 
 
 def pss_later_max(e):

@@ -11,6 +11,7 @@ def test_sentence_means_hand_example():
     h = np.array([[1.0, 0.0], [3.0, 0.0], [0.0, 2.0], [0.0, 4.0], [2.0, 2.0], [5.0, 5.0]])
     e = sentence_means(h, [0, 2, 4, 5])
     assert e.tolist() == [[2.0, 0.0], [0.0, 3.0], [2.0, 2.0]]
+    assert sentence_means(h, [0, 2, 2, 6]).tolist() == [[2.0, 0.0], [0.0, 0.0], [1.75, 3.25]]   # empty sentence
 
 
 def test_pss_closed_forms():

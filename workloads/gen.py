@@ -206,3 +206,50 @@ def initial_recent_obs(L, w: Workload, n_initial: int, device="cpu"):
                        L["q_pos"][:, :Rq].to("cpu")], dim=1).contiguous().to(device)
     n_obs = torch.full((B,), n_initial + Rq, dtype=torch.int32, device=device)
     return q_obs, q_pos, n_obs
+
+
+def make_sentences(batch: int, T: int, d_model: int, seed: int = 0, len_lo: int = 6, len_hi: int = 40,
+                   repeat_frac: float = 0.25, near_frac: float = 0.1, noise: float = 0.5, common: float = 0.5):
+    """Last-layer hidden states with sentence structure, for the sentence
+    redundancy score (SkipKV page, §4.1 and observation 2: reasoning traces
+    revisit earlier sentences).  Sentence lengths are uniform in [len_lo,
+    len_hi]; the tokens after the last complete sentence form an unfinished
+    one.  Each sentence has a topic vector (entries N(0, 1)): a fresh one, the
+    topic of a random earlier sentence (probability repeat_frac: that earlier
+    sentence gets a near-duplicate successor), or a blend 0.97 old + 0.25 new
+    (probability near_frac: similarities around 0.95).  A token is its
+    sentence's topic plus a component shared by the whole request (scale
+    `common`) plus N(0, noise^2) per entry.
+    Returns (h bf16 [B, T, d_model], starts int32 [B, max_sent + 1], n_sent int32 [B])."""
+    g = torch.Generator().manual_seed(seed)
+    hs, all_starts, n_sent = [], [], []
+    for _ in range(batch):
+        shared = common * torch.randn(d_model, generator=g)
+        starts, topics = [0], []
+        while True:
+            L = int(torch.randint(len_lo, len_hi + 1, (1,), generator=g))
+            if starts[-1] + L > T:
+                break
+            starts.append(starts[-1] + L)
+            u = float(torch.rand(1, generator=g))
+            if topics and u < repeat_frac:
+                topics.append(topics[int(torch.randint(0, len(topics), (1,), generator=g))].clone())
+            elif topics and u < repeat_frac + near_frac:
+                old = topics[int(torch.randint(0, len(topics), (1,), generator=g))]
+                topics.append(0.97 * old + 0.25 * torch.randn(d_model, generator=g))
+            else:
+                topics.append(torch.randn(d_model, generator=g))
+        h = noise * torch.randn(T, d_model, generator=g) + shared
+        for i, t in enumerate(topics):
+            h[starts[i]:starts[i + 1]] += t
+        tail_topic = torch.randn(d_model, generator=g)
+        h[starts[-1]:] += tail_topic
+        hs.append(h.to(torch.bfloat16))
+        all_starts.append(starts)
+        n_sent.append(len(starts) - 1)
+    max_sent = max(n_sent)
+    st = torch.zeros(batch, max_sent + 1, dtype=torch.int32)
+    for b, s in enumerate(all_starts):
+        st[b, :len(s)] = torch.tensor(s, dtype=torch.int32)
+        st[b, len(s):] = s[-1]
+    return torch.stack(hs), st, torch.tensor(n_sent, dtype=torch.int32)
