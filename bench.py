@@ -42,8 +42,9 @@ def parse():
     ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
     ap.add_argument("--graph", type=int, default=0, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
-    ap.add_argument("--op", choices=["evict", "attention"], default="evict",
-                    help="attention: time kv_decode_attention over the compacted cache instead of the eviction step")
+    ap.add_argument("--op", choices=["evict", "attention", "skipkv"], default="evict",
+                    help="attention: time kv_decode_attention over the compacted cache; skipkv: time the "
+                         "sentence-redundancy score (SkipKV) on sentence-structured hidden states")
     ap.add_argument("--call", choices=["split", "fused", "inplace"], default="fused",
                     help="split: kv_evict_score then kv_evict_select_compact; "
                          "fused: kv_evict_score_select_compact (one kernel per call); "
@@ -378,6 +379,48 @@ def cpu_baseline(w, target_s):
                       f"({tokens} tokens, {spent:.1f} s, float64 numpy, {platform.processor() or platform.machine()})"}
 
 
+def skipkv_bench(args):
+    """Sentence-redundancy score of R1-Llama-8B-shaped last-layer hidden states
+    (d_model 4096), batch 10, 8192 tokens per request."""
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    from workloads import make_sentences
+    B, T, Dm = 10, 8192, 4096
+    h, st, ns = make_sentences(B, T, Dm, seed=1)
+    h, st, ns = h.cuda(), st.cuda(), ns.cuda()
+    max_sent = st.shape[1] - 1
+    pss = torch.empty(B, max_sent, device="cuda")
+    marks = torch.empty(B, max_sent, dtype=torch.int32, device="cuda")
+    tok = torch.empty(B, T, device="cuda")
+    ws = torch.empty(kv.skipkv_workspace_size(B, max_sent, Dm) + 256, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        kv.skipkv_sentence_scores(h, st, ns, 0.95, pss, tok, marks=marks, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        kv.skipkv_sentence_scores(h, st, ns, 0.95, pss, tok, marks=marks, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = e0.elapsed_time(e1) / args.steps
+    nbytes = B * T * Dm * 2 + B * T * 4 + B * max_sent * 8
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "scored tokens/sec, sentence-redundancy score", "value": B * T / (ms * 1e-3),
+        "unit": "scored tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic sentence-structured hidden states",
+        "config": {"workload": f"skipkv: batch {B} x {T} tokens, d_model {Dm}, {int(ns.float().mean())} sentences "
+                               f"per request on average",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "skipkv_sentence_scores (means, tiled cosines, token scores)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": nbytes, "avg_launch_ms": call_ms},
+    }), flush=True)
+
+
 def attention_bench(args, w, states, out):
     """Decode attention of one new token per request over the compacted cache
     (every layer, request and query head), after one eviction trigger."""
@@ -436,6 +479,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     kv.lib()
+    if args.op == "skipkv":
+        skipkv_bench(args)
+        return
     w = get_workload(args.workload)
     if w.n_layers * w.batch * w.n_kv_heads > 65535 or w.budget == 0:
         print(f"workload {w.name} is not a bench workload", file=sys.stderr)
