@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--select-group", type=int, default=0, help="layers per select/compact call (0 = all)")
     ap.add_argument("--graph", type=int, default=0, help="replay each trigger as a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
-    ap.add_argument("--op", choices=["evict", "attention", "skipkv"], default="evict",
+    ap.add_argument("--op", choices=["evict", "attention", "skipkv", "epikv"], default="evict",
                     help="attention: time kv_decode_attention over the compacted cache; skipkv: time the "
-                         "sentence-redundancy score (SkipKV) on sentence-structured hidden states")
+                         "sentence-redundancy score (SkipKV) on sentence-structured hidden states; epikv: "
+                         "the attention-free hidden-state score and its select/compact (long-65k)")
     ap.add_argument("--call", choices=["split", "fused", "inplace"], default="fused",
                     help="split: kv_evict_score then kv_evict_select_compact; "
                          "fused: kv_evict_score_select_compact (one kernel per call); "
@@ -348,6 +349,8 @@ def cpu_baseline(w, target_s):
     from tests.oracle_side import oracle_cache_keys, np64
     one = w.scaled(batch=1)
     spent, tokens, reqs = 0.0, 0, 0
+    wave = (None if w.budget else
+            oracle.layer_wave_budgets(w.n_layers, w.wave_center, w.wave_sigma, w.wave_total, w.min_per_head))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -362,13 +365,19 @@ def cpu_baseline(w, target_s):
         buf = np64(lay["fps_buf"])
         t0 = time.perf_counter()
         sc = oracle.layer_scores(k, pos, off, ln, q, qp, no, one.n_kv_heads, one.rope_theta, one.dtype)
+        if one.budget:
+            buds = [one.budget] * one.n_kv_heads
+        else:
+            ent = [oracle.normalized_entropy(sc[int(off[s]):int(off[s]) + int(ln[s])]) for s in range(one.n_kv_heads)]
+            buds = oracle.head_budgets(oracle.head_weights(ent), ln, one.n_kv_heads * int(wave[reqs // w.batch]),
+                                       one.min_per_head)
         for s in range(one.n_kv_heads):
             o, n = int(off[s]), int(ln[s])
-            kept = oracle.select_kept(sc[o:o + n], n, one.budget, one.n_prefix, one.n_recent)
+            kept = oracle.select_kept(sc[o:o + n], n, int(buds[s]), one.n_prefix, one.n_recent)
             oracle.compact_rows(k[o:o + n], kept)
             oracle.compact_rows(v[o:o + n], kept)
             oracle.compact_rows(pos[o:o + n], kept)
-        for p in range(buf.shape[0]):
+        for p in range(buf.shape[0] if one.fps_cap else 0):
             picks = oracle.fps(buf[p], one.fps_keep)
             oracle.compact_rows(buf[p], np.sort(picks))
         spent += time.perf_counter() - t0
@@ -466,6 +475,241 @@ def attention_bench(args, w, states, out):
     }), flush=True)
 
 
+def fold_layers(w, device):
+    """Every layer of one trigger folded into one unpadded segment table
+    (ragged per-request lengths kept as they are), K stored post-RoPE."""
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    from workloads import make_layer, request_lengths
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    L, B, Hkv, Hq, d = w.n_layers, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    lengths = request_lengths(w)
+    per_layer = Hkv * sum(lengths)
+    c = {"lengths": lengths, "rows": L * per_layer,
+         "k": torch.empty(L * per_layer, d, dtype=dt, device=device),
+         "v": torch.empty(L * per_layer, d, dtype=dt, device=device),
+         "pos": torch.empty(L * per_layer, dtype=torch.int32, device=device),
+         "seg_len": torch.empty(L * B * Hkv, dtype=torch.int32, device=device),
+         "q": torch.empty(L * B, Hq, w.n_obs, d, dtype=dt, device=device),
+         "q_pos": torch.empty(L * B, w.n_obs, dtype=torch.int32, device=device),
+         "n_obs": torch.full((L * B,), w.n_obs, dtype=torch.int32, device=device),
+         "buf": torch.empty(L * B * Hq, w.fps_cap, d, dtype=dt, device=device) if w.fps_cap else None,
+         "count": torch.full((L * B * Hq,), w.fps_cap, dtype=torch.int32, device=device) if w.fps_cap else None}
+    for l in range(L):
+        lay = make_layer(w, l, device=device, lengths=lengths)
+        rows = slice(l * per_layer, (l + 1) * per_layer)
+        kv.kv_rope_apply(lay["k_pre"], c["k"][rows], lay["pos"], w.rope_theta)
+        c["v"][rows] = lay["v"]
+        c["pos"][rows] = lay["pos"]
+        c["seg_len"][l * B * Hkv:(l + 1) * B * Hkv] = lay["seg_len"]
+        c["q"][l * B:(l + 1) * B] = lay["q_obs"]
+        c["q_pos"][l * B:(l + 1) * B] = lay["q_pos"]
+        if w.fps_cap:
+            c["buf"][l * B * Hq:(l + 1) * B * Hq] = lay["fps_buf"]
+        del lay
+    off = torch.zeros(L * B * Hkv, dtype=torch.int64, device=device)
+    off[1:] = torch.cumsum(c["seg_len"].to(torch.int64), 0)[:-1]
+    c["seg_off"] = off
+    torch.cuda.synchronize()
+    return c
+
+
+def _time_calls(calls, steps, warmup):
+    """Run the list of (name, fn) `warmup` times, then `steps` timed times with
+    HIP events around every call on the current stream; returns the wall ms per
+    step and the mean ms of each call."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for (_, fn), (a, b) in zip(calls, ev[i]):
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = {name: sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)) / steps
+           for j, (name, _) in enumerate(calls)}
+    return wall, per
+
+
+def _result(metric, value, unit, args, ms, data, config, calls_ms, call_bytes, dominant, kernel_desc, dtype="bf16"):
+    achieved = call_bytes[dominant] / (calls_ms[dominant] * 1e-3) / 1e9
+    step_b = sum(call_bytes.values())
+    return {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": data, "config": config,
+        "step_hbm": {"algorithmic_bytes": step_b, "gb_per_s": step_b / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": step_b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "calls": {k: {"ms": calls_ms[k], "bytes": call_bytes[k],
+                      "gb_per_s": call_bytes[k] / (calls_ms[k] * 1e-3) / 1e9} for k in calls_ms},
+        "roofline": {"bound": "hbm", "kernel": kernel_desc, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": call_bytes[dominant], "avg_launch_ms": calls_ms[dominant]},
+    }
+
+
+def config_bench(args, w):
+    """One trigger of a single-state workload (every layer folded into one
+    segment table): the one-kernel call where it applies (uniform budget,
+    short bf16 segments; the library falls back to the two calls otherwise),
+    or scoring with per-head entropies, entropy-driven head budgets and
+    select/compact for the per-head-budget workload; FPS where the workload
+    has beacon buffers."""
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    dev = "cuda"
+    c = fold_layers(w, dev)
+    L, B, Hkv, Hq, d = w.n_layers, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    S, rows, esz = L * B * Hkv, c["rows"], (2 if w.dtype == "bf16" else 4)
+    row = d * esz
+    cache = kv.make_cache(c["k"], c["v"], c["pos"], c["seg_off"], c["seg_len"], Hkv, w.len_hi)
+    obs = kv.make_obs(c["q"], c["q_pos"], c["n_obs"], w.rope_theta, bool(w.causal))
+    scores = torch.empty(rows, dtype=torch.float32, device=dev)
+    q_bytes = L * B * Hq * w.n_obs * row + L * B * w.n_obs * 4
+    score_bytes = rows * row + rows * 4 + q_bytes + rows * 4
+    calls, nbytes = [], {}
+    if w.budget:
+        cap = w.budget
+        o = {"k": torch.empty(S * cap, d, dtype=c["k"].dtype, device=dev),
+             "v": torch.empty(S * cap, d, dtype=c["k"].dtype, device=dev),
+             "pos": torch.empty(S * cap, dtype=torch.int32, device=dev),
+             "seg_off": torch.arange(S, dtype=torch.int64, device=dev) * cap,
+             "seg_len": torch.empty(S, dtype=torch.int32, device=dev)}
+        cout = kv.make_cache(o["k"], o["v"], o["pos"], o["seg_off"], o["seg_len"], Hkv, cap)
+        ws = torch.empty(kv.kv_evict_score_select_compact_workspace(cache, obs, cout, False) + 256,
+                         dtype=torch.uint8, device=dev)
+        kept_rows = sum(min(cap, n) for n in c["lengths"]) * L * Hkv
+        calls.append(("score_select_compact", lambda: kv.kv_evict_score_select_compact(
+            cache, obs, scores, None, w.n_prefix, w.n_recent, cout, uniform_budget=cap, ws=ws)))
+        nbytes["score_select_compact"] = score_bytes + 3 * kept_rows * row + kept_rows * 4
+        what = (f"{w.len_lo}" if w.len_lo == w.len_hi else f"U[{w.len_lo}, {w.len_hi}]") + f" -> {cap} per head"
+    else:
+        ent = torch.empty(S, dtype=torch.float32, device=dev)
+        budget = torch.empty(S, dtype=torch.int32, device=dev)
+        wave = torch.empty(L, dtype=torch.int32, device=dev)
+        kv.kv_evict_wave_budgets(L, w.wave_center, w.wave_sigma, w.wave_total, w.min_per_head, wave)
+        layer_total = (wave.to(torch.int32) * Hkv).repeat_interleave(B).contiguous()
+        # output segments of the longest input length: a head may keep every row
+        cap = w.len_hi
+        o = {"k": torch.empty(S * cap, d, dtype=c["k"].dtype, device=dev),
+             "v": torch.empty(S * cap, d, dtype=c["k"].dtype, device=dev),
+             "pos": torch.empty(S * cap, dtype=torch.int32, device=dev),
+             "seg_off": torch.arange(S, dtype=torch.int64, device=dev) * cap,
+             "seg_len": torch.empty(S, dtype=torch.int32, device=dev)}
+        cout = kv.make_cache(o["k"], o["v"], o["pos"], o["seg_off"], o["seg_len"], Hkv, cap)
+        ws_s = torch.empty(kv.kv_evict_score_workspace(cache, obs) + 256, dtype=torch.uint8, device=dev)
+        ws_c = torch.empty(kv.kv_evict_select_workspace(cout, False) + 256, dtype=torch.uint8, device=dev)
+        calls.append(("score", lambda: kv.kv_evict_score(cache, obs, scores, head_entropy=ent, ws=ws_s)))
+        calls.append(("budgets", lambda: kv.kv_evict_entropy_budgets(ent, 0, layer_total, c["seg_len"], L * B, Hkv,
+                                                                     w.min_per_head, budget)))
+        calls.append(("select_compact", lambda: kv.kv_evict_select_compact(
+            cache, scores, budget, w.n_prefix, w.n_recent, cout, ws=ws_c)))
+        calls[0][1]()
+        calls[1][1]()
+        kept_rows = int(budget.sum())
+        nbytes["score"] = score_bytes + S * 4
+        nbytes["budgets"] = S * 4 * 4 + L * B * 4
+        nbytes["select_compact"] = rows * 4 + 4 * kept_rows * row + 2 * kept_rows * 4
+        what = f"U[{w.len_lo}, {w.len_hi}] -> entropy-driven per-head budgets ({kept_rows} rows kept in all)"
+    if w.fps_cap:
+        fb, fc = torch.empty_like(c["buf"]), torch.empty_like(c["count"])
+        calls.append(("fps", lambda: kv.beacon_fps_update(c["buf"], fb, c["count"], fc, w.fps_keep)))
+        nbytes["fps"] = L * B * Hq * (w.fps_cap + w.fps_keep) * row
+    log(f"{w.name}: {rows} rows folded; warmup {args.warmup}, timed {args.steps}")
+    ms, per = _time_calls(calls, args.steps, args.warmup)
+    dom = max(per, key=per.get)
+    tokens = L * sum(c["lengths"])
+    res = _result(
+        "scored KV tokens/sec (+ % HBM peak)", tokens / (ms * 1e-3), "scored KV tokens/s", args, ms,
+        "synthetic (seeded clustered keys/queries; no model weights needed)",
+        {"workload": f"{w.name}: {L} layer(s) x batch {B} x {Hkv} KV heads, head_dim {d}, {w.dtype}, {what}, "
+                     f"{w.n_recent_q} recent + {w.n_beacon} beacon queries per q-head"
+                     + (f", FPS {w.fps_cap}->{w.fps_keep}" if w.fps_cap else ""),
+         "global_batch": B, "seq_len": w.len_hi, "parallelism": "single GPU"},
+        per, nbytes, dom, dom, dtype=w.dtype)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def epikv_bench(args, w):
+    """Attention-free eviction (EPIKV): hidden-state change scores of the two
+    monitored layers' traces, then select/compact of every KV head with the
+    per-token score broadcast over heads."""
+    import numpy as np
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    from workloads import make_layer, make_traces
+    import oracle
+    dev = "cuda"
+    B, Hkv, d, n, cap = w.batch, w.n_kv_heads, w.head_dim, w.len_hi, w.budget
+    lay = make_layer(w, 0, device=dev)
+    k = torch.empty(lay["k_pre"].shape, dtype=torch.bfloat16, device=dev)
+    kv.kv_rope_apply(lay["k_pre"], k, lay["pos"], w.rope_theta)
+    del lay["k_pre"]
+    cache = kv.make_cache(k, lay["v"], lay["pos"], lay["seg_off"], lay["seg_len"], Hkv, n)
+    h = make_traces(w, device=dev)
+    Dm = h.shape[-1]
+    S = B * Hkv
+    o = {"k": torch.empty(S * cap, d, dtype=torch.bfloat16, device=dev),
+         "v": torch.empty(S * cap, d, dtype=torch.bfloat16, device=dev),
+         "pos": torch.empty(S * cap, dtype=torch.int32, device=dev),
+         "seg_off": torch.arange(S, dtype=torch.int64, device=dev) * cap,
+         "seg_len": torch.empty(S, dtype=torch.int32, device=dev)}
+    cout = kv.make_cache(o["k"], o["v"], o["pos"], o["seg_off"], o["seg_len"], Hkv, cap)
+    epi = torch.empty(B, n, dtype=torch.float32, device=dev)
+    score_off = (torch.arange(S, device=dev) // Hkv * n).to(torch.int64)
+    ws_e = torch.empty(kv.epikv_workspace_size(B, n) + 256, dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(kv.kv_evict_select_workspace(cout, False) + 256, dtype=torch.uint8, device=dev)
+    calls = [("epikv_score", lambda: kv.epikv_score(h[0], h[1], w.epikv_window, w.epikv_eps, epi, ws=ws_e)),
+             ("select_compact", lambda: kv.kv_evict_select_compact(
+                 cache, epi.view(-1), None, w.n_prefix, w.n_recent, cout, score_off=score_off, uniform_budget=cap,
+                 ws=ws_c))]
+    nbytes = {"epikv_score": 2 * B * n * Dm * 2 + B * n * 4,
+              "select_compact": B * n * 4 + 4 * S * cap * d * 2 + 2 * S * cap * 4}
+    log(f"{w.name} hidden-state score: traces {tuple(h.shape)}; warmup {args.warmup}, timed {args.steps}")
+    ms, per = _time_calls(calls, args.steps, args.warmup)
+    dom = max(per, key=per.get)
+    res = _result(
+        "scored KV tokens/sec (+ % HBM peak), attention-free hidden-state score", B * n / (ms * 1e-3),
+        "scored KV tokens/s", args, ms, "synthetic (seeded mean-reverting hidden-state traces, clustered keys)",
+        {"workload": f"{w.name} EPIKV: batch {B} x {n} steps, traces of 2 layers x d_model {Dm}, window "
+                     f"{w.epikv_window}, {Hkv} KV heads x {n} -> {cap}",
+         "global_batch": B, "seq_len": n, "parallelism": "single GPU"},
+        per, nbytes, dom, dom)
+    if not args.no_cpu_baseline:
+        # the oracle on the first Ts steps of request 0 (its cost is linear in T), then the
+        # per-head selection and compaction of a segment of that length
+        log("timing the CPU oracle sample")
+        Ts = 4096
+        spent, tokens = 0.0, 0
+        while spent < args.cpu_seconds and Ts <= n:
+            ha = h[0, 0, :Ts].float().cpu().numpy().astype(np.float64)
+            hb = h[1, 0, :Ts].float().cpu().numpy().astype(np.float64)
+            kk = k[:Ts].float().cpu().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            s = oracle.epikv_score(ha, hb, w.epikv_window, w.epikv_eps)
+            for _ in range(Hkv):
+                kept = oracle.select_kept(s, Ts, min(cap, Ts // 2), w.n_prefix, w.n_recent)
+                oracle.compact_rows(kk, kept)
+                oracle.compact_rows(kk, kept)
+            spent += time.perf_counter() - t0
+            tokens += Ts
+            Ts *= 2
+        res["cpu_baseline"] = {"value": tokens / spent, "unit": "scored KV tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"request 0, prefixes of 4096.. steps ({tokens} steps in all, {spent:.1f} s, "
+                                         f"float64 numpy, {platform.processor() or platform.machine()})"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -483,6 +727,15 @@ def main():
         skipkv_bench(args)
         return
     w = get_workload(args.workload)
+    if args.op == "epikv":
+        if not w.d_model:
+            print(f"workload {w.name} has no hidden-state traces", file=sys.stderr)
+            sys.exit(2)
+        epikv_bench(args, w)
+        return
+    if args.op == "evict" and w.triggers == 1:
+        config_bench(args, w)
+        return
     if w.n_layers * w.batch * w.n_kv_heads > 65535 or w.budget == 0:
         print(f"workload {w.name} is not a bench workload", file=sys.stderr)
         sys.exit(2)

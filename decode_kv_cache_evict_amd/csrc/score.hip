@@ -57,20 +57,22 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 // ------------------------------------------------------------ query rotation
 // Rotate every observation row to its q_pos (double-precision angle and
 // rotation) and round to the storage dtype; rows past n_obs are zeroed.  One
-// thread per (request, observation row, run of V frequencies): the angles are
-// shared by all query heads, so their sines and cosines are formed once and
-// applied to every head, with 16-byte loads and stores of both halves.
+// thread per (request, observation row, run of V frequencies, group of heads):
+// the angles are shared by all query heads, so their sines and cosines are
+// formed once per group and applied to each of its heads, with 16-byte loads
+// and stores of both halves.  Small batches split the heads over more groups.
 template <typename T>
 __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
                                   const int32_t* __restrict__ n_obs, T* __restrict__ qr,
-                                  int64_t n_work, int n_q, int max_obs, int D, double theta) {
+                                  int64_t n_work, int n_q, int max_obs, int D, double theta, int hsplit) {
   constexpr int V = 16 / int(sizeof(T));          // frequencies per thread
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n_work) return;
   const int half = D / 2;
   const int runs = half / V;
-  const int i0 = int(idx % runs) * V;
-  const int64_t bo = idx / runs;                  // b * max_obs + o
+  const int hg = int(idx % hsplit);               // this thread's share of the heads
+  const int i0 = int(idx / hsplit % runs) * V;
+  const int64_t bo = idx / hsplit / runs;         // b * max_obs + o
   const int o = int(bo % max_obs);
   const int b = int(bo / max_obs);
   const int no = n_obs ? n_obs[b] : max_obs;
@@ -85,7 +87,8 @@ __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __rest
       sincos(ang, &sn[v], &cs[v]);
     }
   }
-  for (int h = 0; h < n_q; ++h) {
+  const int hpg = (n_q + hsplit - 1) / hsplit;
+  for (int h = hg * hpg; h < min(n_q, (hg + 1) * hpg); ++h) {
     const int64_t row = (int64_t(b) * n_q + h) * max_obs + o;
     uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
     if (live) {
@@ -116,12 +119,18 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(ScoreArgs a) {
   const int n = a.seg_len[s];
   const int nch = (n >= 0 && n <= a.max_seg_len) ? (n + a.chunk - 1) / a.chunk : 0;
   const float2* st = a.stats + int64_t(s) * a.n_chunks * a.rows + r;
-  float M = kNegBig;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[int64_t(c) * a.rows].x);
-  float L = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float2 v = st[int64_t(c) * a.rows];
-    L += v.y * exp2f(v.x - M);
+  float M = kNegBig, L = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 8) {        // eight independent loads in flight, merged online
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? st[int64_t(c0 + u) * a.rows] : make_float2(kNegBig, 0.f);
+    float M2 = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M2 = fmaxf(M2, v[u].x);
+    L *= exp2f(M - M2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) L += v[u].y * exp2f(v[u].x - M2);
+    M = M2;
   }
   a.lse[idx] = L > 0.f ? M + log2f(L) : kInf;
 }
@@ -584,13 +593,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
     return;
   }
-  const int k0 = ch * kMfmaChunk;
+  const int k0 = ch * a.chunk;
   if (k0 >= n) {
     if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
     return;
   }
-  const int k1 = min(n, k0 + kMfmaChunk);
-  const int nch = (n + kMfmaChunk - 1) / kMfmaChunk;
+  const int k1 = min(n, k0 + a.chunk);
+  const int nch = (n + a.chunk - 1) / a.chunk;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
   const bool mean = a.aggregate != 0;
@@ -895,6 +904,14 @@ hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Keys per MFMA work-group: 1024, halved (down to 256) while the launch would
+// have fewer than 2048 work-groups, so that small batches still fill the chip.
+int mfma_chunk(int n_seg, int max_seg_len) {
+  int c = kMfmaChunk;
+  while (c > 256 && int64_t(n_seg) * ((max_seg_len + c - 1) / c) < 2048) c >>= 1;
+  return c;
+}
+
 }  // namespace
 
 size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
@@ -929,16 +946,19 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   a.lse = reinterpret_cast<float*>(w);
   w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
   int* ctl = reinterpret_cast<int*>(w);
-  const int64_t n_work = int64_t(batch) * a.max_obs * (a.head_dim / 2) / (16 / int64_t(elem));
+  const int64_t base_work = int64_t(batch) * a.max_obs * (a.head_dim / 2) / (16 / int64_t(elem));
+  int hsplit = 1;                              // head groups: about 64K threads in all
+  while (hsplit < a.n_q && base_work * hsplit < 65536) hsplit *= 2;
+  const int64_t n_work = base_work * hsplit;
   const dim3 rg(unsigned((n_work + 255) / 256));
   if (n_work > 0) {
     if (a.dtype == 0)
       hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
                          a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim,
-                         a.theta);
+                         a.theta, hsplit);
     else
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
-                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, a.theta);
+                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, a.theta, hsplit);
   }
   e = hipGetLastError();
   return ctl;
@@ -960,7 +980,7 @@ hipError_t launch_step(const ScoreArgs& a, int* ctl, hipStream_t st) {
 hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const bool mfma = a.dtype == 0 && a.impl == 0;
   const bool fused = a.dtype == 0 && a.impl == 2;
-  a.chunk = (fused || mfma) ? kMfmaChunk : kScoreChunk;
+  a.chunk = (fused || mfma) ? mfma_chunk(a.n_seg, a.max_seg_len) : kScoreChunk;
   hipError_t e;
   int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;
@@ -984,7 +1004,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
-  a.chunk = kMfmaChunk;
+  a.chunk = mfma_chunk(a.n_seg, a.max_seg_len);
   hipError_t e;
   int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;

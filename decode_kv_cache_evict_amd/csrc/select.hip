@@ -4,12 +4,13 @@
 // good).
 //
 // select: one work-group per segment.  The K-th largest candidate score is found
-// by an MSB-first radix select over order-preserving 32-bit keys (four 8-bit
-// digit passes over LDS histograms); ties at the threshold go to the lower
-// slots.  Kept slots are then emitted in ascending order by a block-wide
-// ballot scan.
-// compact: a grid over (segment, 64-row tiles) that gathers kept K/V rows with
-// 16-byte loads and stores, and their positions.
+// by an MSB-first radix select over order-preserving 32-bit keys (at most 8-bit
+// digits over LDS histograms, starting below the leading bits that the
+// candidates' minimum and maximum share); ties at the threshold go to the lower
+// slots.  Kept slots are then emitted in ascending order by block-wide scans,
+// 8 consecutive slots per thread and round.
+// compact: a grid over (segment, share of its 128-row tiles) that gathers kept
+// K/V rows with 16-byte loads and stores, and their positions.
 // inplace: hole filling within the input cache (one work-group per segment).
 #include "common.h"
 #include "internal.h"
@@ -22,10 +23,16 @@ namespace {
 constexpr int kSelBlock = 512;
 constexpr int kSelWaves = kSelBlock / kWave;
 
+// Keys a select work-group holds in LDS (48 KB); the scores of longer segments
+// are re-read from memory on each radix pass.
+constexpr int kSelLdsKeys = 12288;
+
 __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
+  __shared__ uint32_t keys[kSelLdsKeys];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
-  __shared__ int wtot_a[kSelWaves], wtot_b[kSelWaves];
+  __shared__ int wtot[kSelWaves];
+  __shared__ uint32_t mm[2 * kSelWaves];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
 
@@ -50,22 +57,104 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
     return;
   }
   const float* sc = a.scores + so;
+  const bool in_lds = n <= kSelLdsKeys;
+  const int c0 = P, c1 = n - R;              // candidate slots [c0, c1)
+  // one read of the scores, eight loads in flight per thread (clamped
+  // addresses): order keys into LDS when they fit, and the candidates' min and max
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j0 = 0; j0 < n; j0 += 8 * kSelBlock) {
+    float raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = sc[min(j0 + u * kSelBlock + tid, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kSelBlock + tid;
+      if (j < n) {
+        const uint32_t key = float_order_key(raw[u]);
+        if (in_lds) keys[j] = key;
+        if (j >= c0 && j < c1) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+  }
+  if ((tid & 63) == 0) {
+    mm[tid >> 6] = kmin;
+    mm[kSelWaves + (tid >> 6)] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSelWaves; ++q) {
+    kmin = min(kmin, mm[q]);
+    kmax = max(kmax, mm[kSelWaves + q]);
+  }
+  // every candidate shares the leading bits of its min and max: the radix digits start below them
+  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
   uint32_t T, kk;
-  radix_threshold<kSelBlock>([&](int j) { return float_order_key(sc[j]); }, P, n, R, K - P - R, hist, sh, T, kk);
-  // kept = protected, keys above T, and the first kk candidates equal to T
+  radix_threshold_v<kSelBlock>(
+      [&](const auto& f) {
+        if (in_lds) {
+          for (int j = c0 + tid; j < c1; j += kSelBlock) f(keys[j]);
+        } else {
+          for (int j0 = c0; j0 < c1; j0 += 8 * kSelBlock) {
+            float raw[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) raw[u] = sc[min(j0 + u * kSelBlock + tid, c1 - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (j0 + u * kSelBlock + tid < c1) f(float_order_key(raw[u]));
+          }
+        }
+      },
+      K - P - R, hist, sh, T, kk, kmin, known);
+  // kept = protected, keys above T, and the first kk candidates equal to T, in
+  // slot order; each thread takes 8 consecutive slots per round
   int base = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < n; j0 += kSelBlock) {
-    const int j = j0 + tid;
-    const bool in = j < n;
-    const bool cand = in && j >= P && j < n - R;
-    const uint32_t key = cand ? float_order_key(sc[j]) : 0u;
-    const bool eq = cand && key == T;
+  for (int j0 = 0; j0 < n; j0 += 8 * kSelBlock) {
+    const int jt = j0 + 8 * tid;
+    uint32_t kv[8];
+    if (in_lds) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = jt + u < n ? keys[jt + u] : 0u;
+    } else {
+      float raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = sc[min(jt + u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = float_order_key(raw[u]);
+    }
+    int n_eq = 0, n_sure = 0;                  // ties at T; protected or above T
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      n_eq += cand && kv[u] == T;
+      n_sure += j < n && (!cand || kv[u] > T);
+    }
     int eq_tot;
-    const int eq_rank = eq_seen + block_flag_scan<kSelBlock>(eq, wtot_a, eq_tot);
-    const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
+    const int eq_before = eq_seen + block_scan<kSelBlock>(n_eq, wtot, eq_tot);
+    const int n_keep = n_sure + min(n_eq, max(0, int(kk) - eq_before));
     int keep_tot;
-    const int at = base + block_flag_scan<kSelBlock>(keep, wtot_b, keep_tot);
-    if (keep && at < K) a.kept[oo + at] = j;
+    int at = base + block_scan<kSelBlock>(n_keep, wtot, keep_tot);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      const bool eq = cand && kv[u] == T;
+      const bool keep = j < n && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
+      eq_rank += eq;
+      if (keep) {
+        if (at < K) a.kept[oo + at] = j;
+        ++at;
+      }
+    }
     base += keep_tot;
     eq_seen += eq_tot;
   }
@@ -73,9 +162,9 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
 }
 
 // Gather kept rows.  CPR 16-byte chunks per row; each thread moves UNR rows of
-// K and V per pass (all loads issued before the stores), and a work-group
-// covers PASSES passes.  Loads and stores are non-temporal: every byte is
-// touched exactly once.
+// K and V per pass (all loads issued before the stores), a tile is PASSES
+// passes, and a work-group takes every gridDim.x-th tile of its segment.  Loads
+// and stores are non-temporal: every byte is touched exactly once.
 #ifndef KVE_COMPACT_UNR
 #define KVE_COMPACT_UNR 4
 #endif
@@ -93,8 +182,7 @@ __global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
   constexpr int RPW = RPP * UNR * kCompactPasses;
   const int s = blockIdx.y;
   const int out_n = a.out_len[s];
-  const int rw = blockIdx.x * RPW;
-  if (out_n <= 0 || out_n > a.out_cap || rw >= out_n) return;
+  if (out_n <= 0 || out_n > a.out_cap || int(blockIdx.x) * RPW >= out_n) return;
   const int64_t io = a.in_off[s], oo = a.out_off[s];
   const int n_in = a.in_len[s];
   const int part = threadIdx.x % CPR;
@@ -103,32 +191,34 @@ __global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
   const u32x4* vin = static_cast<const u32x4*>(a.v_in);
   u32x4* kout = static_cast<u32x4*>(a.k_out);
   u32x4* vout = static_cast<u32x4*>(a.v_out);
-  for (int p = 0; p < kCompactPasses; ++p) {
-    const int r0 = rw + p * RPP * UNR;
-    if (r0 >= out_n) break;
-    u32x4 kb[UNR], vb[UNR];
-    int src[UNR];
+  for (int rw = blockIdx.x * RPW; rw < out_n; rw += gridDim.x * RPW) {
+    for (int p = 0; p < kCompactPasses; ++p) {
+      const int r0 = rw + p * RPP * UNR;
+      if (r0 >= out_n) break;
+      u32x4 kb[UNR], vb[UNR];
+      int src[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int r = r0 + u * RPP + rsub;
-      int j = r < out_n ? a.kept[oo + r] : -1;
-      if (j >= n_in) j = -1;
-      src[u] = j;
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (src[u] >= 0) {
-        kb[u] = __builtin_nontemporal_load(&kin[(io + src[u]) * CPR + part]);
-        vb[u] = __builtin_nontemporal_load(&vin[(io + src[u]) * CPR + part]);
+      for (int u = 0; u < UNR; ++u) {
+        const int r = r0 + u * RPP + rsub;
+        int j = r < out_n ? a.kept[oo + r] : -1;
+        if (j >= n_in) j = -1;
+        src[u] = j;
       }
-    }
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int r = r0 + u * RPP + rsub;
-      if (src[u] >= 0) {
-        __builtin_nontemporal_store(kb[u], &kout[(oo + r) * CPR + part]);
-        __builtin_nontemporal_store(vb[u], &vout[(oo + r) * CPR + part]);
-        if (part == 0) a.pos_out[oo + r] = a.pos_in[io + src[u]];
+      for (int u = 0; u < UNR; ++u) {
+        if (src[u] >= 0) {
+          kb[u] = __builtin_nontemporal_load(&kin[(io + src[u]) * CPR + part]);
+          vb[u] = __builtin_nontemporal_load(&vin[(io + src[u]) * CPR + part]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int r = r0 + u * RPP + rsub;
+        if (src[u] >= 0) {
+          __builtin_nontemporal_store(kb[u], &kout[(oo + r) * CPR + part]);
+          __builtin_nontemporal_store(vb[u], &vout[(oo + r) * CPR + part]);
+          if (part == 0) a.pos_out[oo + r] = a.pos_in[io + src[u]];
+        }
       }
     }
   }
@@ -137,7 +227,16 @@ __global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
 template <int CPR>
 hipError_t launch_compact(const SelectArgs& a, hipStream_t st) {
   constexpr int RPW = (256 / CPR) * kCompactUnr * kCompactPasses;
-  const dim3 grid(unsigned((a.out_cap + RPW - 1) / RPW), unsigned(a.n_seg));
+  // work-groups per segment: one per RPW-row tile when a uniform budget fixes
+  // the kept counts; with per-segment budgets (known only on the device),
+  // enough for about 32K work-groups in all, each looping over its share of
+  // the segment's tiles, so that few are idle when the kept counts are far
+  // below the output capacity
+  const int tiles = (a.out_cap + RPW - 1) / RPW;
+  const int per_seg = !a.budget ? (min(a.uniform_budget, a.out_cap) + RPW - 1) / RPW
+                                : max(1, min(tiles, (32768 + a.n_seg - 1) / a.n_seg));
+  if (per_seg <= 0) return hipSuccess;
+  const dim3 grid(unsigned(per_seg), unsigned(a.n_seg));
   hipLaunchKernelGGL(compact_kernel<CPR>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

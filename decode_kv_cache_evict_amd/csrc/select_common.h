@@ -29,6 +29,31 @@ __device__ __forceinline__ int block_flag_scan(bool f, int* wtot, int& total) {
   return before + in_wave;
 }
 
+// Exclusive block scan of a non-negative int over BLOCK threads; returns this
+// thread's prefix and sets `total`.  wtot: BLOCK/64 ints of LDS.
+template <int BLOCK>
+__device__ __forceinline__ int block_scan(int x, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) wtot[w] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < BLOCK / kWave; ++q) {
+    const int t = wtot[q];
+    before += q < w ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + inc - x;
+}
+
 // Block sum of an int over BLOCK threads (wtot: BLOCK/64 ints of LDS).
 template <int BLOCK>
 __device__ __forceinline__ int block_sum(int v, int* wtot) {
