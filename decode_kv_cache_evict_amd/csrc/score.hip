@@ -317,9 +317,10 @@ struct WaveRows {
   }
 };
 
-// Pass-1 update of (m, l) with two key tiles of logits.
+// Pass-1 update of (m, l) with two key tiles of logits; m is kept scaled by c
+// (the exp2 argument's units), so the common case needs no multiply.
 template <int RT>
-__device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[2][RT],
+__device__ __forceinline__ void stats_update(float (&mc)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[2][RT],
                                              float c) {
   float lsum[RT][4];
   bool redo = false;
@@ -327,8 +328,8 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float mc = m[rt][i] * c;
-      const float v = l[rt][i] + fast_exp2(fmaf(acc[0][rt][i], c, -mc)) + fast_exp2(fmaf(acc[1][rt][i], c, -mc));
+      const float v = l[rt][i] + fast_exp2(fmaf(acc[0][rt][i], c, -mc[rt][i])) +
+                      fast_exp2(fmaf(acc[1][rt][i], c, -mc[rt][i]));
       lsum[rt][i] = v;
       redo |= !(v <= kBig);
     }
@@ -337,11 +338,11 @@ __device__ __forceinline__ void stats_update(float (&m)[RT][4], float (&l)[RT][4
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mn = fmaxf(m[rt][i], fmaxf(acc[0][rt][i], acc[1][rt][i]));
-        const float mc = mn * c;
-        lsum[rt][i] = l[rt][i] * fast_exp2((m[rt][i] - mn) * c) + fast_exp2(fmaf(acc[0][rt][i], c, -mc)) +
-                      fast_exp2(fmaf(acc[1][rt][i], c, -mc));
-        m[rt][i] = mn;
+        // scaling by c > 0 is monotone, so max(m, x0, x1) * c = max(m * c, max(x0, x1) * c)
+        const float mn = fmaxf(mc[rt][i], fmaxf(acc[0][rt][i], acc[1][rt][i]) * c);
+        lsum[rt][i] = l[rt][i] * fast_exp2(mc[rt][i] - mn) + fast_exp2(fmaf(acc[0][rt][i], c, -mn)) +
+                      fast_exp2(fmaf(acc[1][rt][i], c, -mn));
+        mc[rt][i] = mn;
       }
   }
 #pragma unroll
@@ -524,37 +525,63 @@ __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, i
   }
   if (first && tid == 0) a.out_len[s] = keep_n;
   __syncthreads();
-  // gather: 16-byte chunks, UNR rows per thread in flight
+  // gather: 16-byte chunks, GU rows per thread and batch, four batches in
+  // registers.  The memory counter retires loads and stores in issue order and
+  // a batch's registers may only be reloaded once its stores are done, so the
+  // loads run two batches ahead of the stores and a batch is reloaded two
+  // batches after its stores: every wait leaves two batches in flight.  Loads
+  // past the chunk's last kept row repeat that row (no branch, no fault).
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4* kin = static_cast<const u32x4*>(a.k);
   const u32x4* vin = static_cast<const u32x4*>(a.v);
   u32x4* kout = static_cast<u32x4*>(a.k_out);
   u32x4* vout = static_cast<u32x4*>(a.v_out);
   const int part = tid % CPR, rsub = tid / CPR;
-  for (int r0 = 0; r0 < cnt; r0 += RPP * UNR) {
-    u32x4 kb[UNR], vb[UNR];
-    int src[UNR];
+  constexpr int GU = 2;
+  constexpr int STEP = RPP * GU;
+  struct Batch {
+    u32x4 k[GU], v[GU];
+    int src[GU], pos[GU];
+  };
+  auto load = [&](Batch& bt, int r0) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int r = r0 + u * RPP + rsub;
-      src[u] = r < cnt ? mine[r] : -1;
-      if (src[u] >= 0) {
-        kb[u] = kin[(off + src[u]) * CPR + part];
-        vb[u] = __builtin_nontemporal_load(&vin[(off + src[u]) * CPR + part]);
-      }
+    for (int u = 0; u < GU; ++u) bt.src[u] = mine[min(r0 + u * RPP + rsub, cnt - 1)];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      bt.k[u] = kin[(off + bt.src[u]) * CPR + part];
+      bt.v[u] = __builtin_nontemporal_load(&vin[(off + bt.src[u]) * CPR + part]);
+      bt.pos[u] = a.pos[off + bt.src[u]];
     }
+  };
+  auto store = [&](const Batch& bt, int r0) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+    for (int u = 0; u < GU; ++u) {
       const int r = r0 + u * RPP + rsub;
-      if (src[u] >= 0) {
+      if (r < cnt) {
         const int64_t dst = oo + base + r;
-        __builtin_nontemporal_store(kb[u], &kout[dst * CPR + part]);
-        __builtin_nontemporal_store(vb[u], &vout[dst * CPR + part]);
+        __builtin_nontemporal_store(bt.k[u], &kout[dst * CPR + part]);
+        __builtin_nontemporal_store(bt.v[u], &vout[dst * CPR + part]);
         if (part == 0) {
-          a.pos_out[dst] = a.pos[off + src[u]];
-          if (a.kept) a.kept[dst] = src[u];
+          a.pos_out[dst] = bt.pos[u];
+          if (a.kept) a.kept[dst] = bt.src[u];
         }
       }
+    }
+  };
+  if (cnt > 0) {
+    Batch b0, b1, b2, b3;
+    load(b0, 0);
+    load(b1, STEP);
+    for (int r0 = 0; r0 < cnt; r0 += 4 * STEP) {
+      load(b2, r0 + 2 * STEP);
+      store(b0, r0);
+      load(b3, r0 + 3 * STEP);
+      store(b1, r0 + STEP);
+      if (r0 + 2 * STEP >= cnt) break;
+      load(b0, r0 + 4 * STEP);
+      store(b2, r0 + 2 * STEP);
+      load(b1, r0 + 5 * STEP);
+      store(b3, r0 + 3 * STEP);
     }
   }
 }
@@ -615,7 +642,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   __syncthreads();
   WaveRows<D, RT> rows;
   rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
-  float st0[RT][4], st1[RT][4];   // pass 1: (m, l); pass 2: st0 = lse (log2 units)
+  float st0[RT][4], st1[RT][4];   // pass 1: (m * c, l); pass 2: st0 = lse (log2 units)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -713,13 +740,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
       for (int o = 1; o < 16; o <<= 1) {
         const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
         const float M = fmaxf(mm, m2);
-        ll = ll * fast_exp2((mm - M) * c) + l2 * fast_exp2((m2 - M) * c);
+        ll = ll * fast_exp2(mm - M) + l2 * fast_exp2(m2 - M);
         mm = M;
       }
       const int r = 16 * (w * RT + rt) + 4 * quad + i;
       if (col == 0 && r < a.rows) {
-        if (MODE >= kModeFused) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm * c, ll));
-        else stats_seg[int64_t(ch) * a.rows + r] = make_float2(mm * c, ll);
+        if (MODE >= kModeFused) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm, ll));
+        else stats_seg[int64_t(ch) * a.rows + r] = make_float2(mm, ll);
       }
     }
   if (MODE < kModeFused) return;
