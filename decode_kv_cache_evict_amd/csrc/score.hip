@@ -430,8 +430,6 @@ template <int D>
 __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
                                                     uint32_t* keys, int tid) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;             // rows per pass
-  constexpr int UNR = 4;
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int wtot[4];
@@ -525,65 +523,9 @@ __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, i
   }
   if (first && tid == 0) a.out_len[s] = keep_n;
   __syncthreads();
-  // gather: 16-byte chunks, GU rows per thread and batch, four batches in
-  // registers.  The memory counter retires loads and stores in issue order and
-  // a batch's registers may only be reloaded once its stores are done, so the
-  // loads run two batches ahead of the stores and a batch is reloaded two
-  // batches after its stores: every wait leaves two batches in flight.  Loads
-  // past the chunk's last kept row repeat that row (no branch, no fault).
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4* kin = static_cast<const u32x4*>(a.k);
-  const u32x4* vin = static_cast<const u32x4*>(a.v);
-  u32x4* kout = static_cast<u32x4*>(a.k_out);
-  u32x4* vout = static_cast<u32x4*>(a.v_out);
-  const int part = tid % CPR, rsub = tid / CPR;
-  constexpr int GU = 2;
-  constexpr int STEP = RPP * GU;
-  struct Batch {
-    u32x4 k[GU], v[GU];
-    int src[GU], pos[GU];
-  };
-  auto load = [&](Batch& bt, int r0) {
-#pragma unroll
-    for (int u = 0; u < GU; ++u) bt.src[u] = mine[min(r0 + u * RPP + rsub, cnt - 1)];
-#pragma unroll
-    for (int u = 0; u < GU; ++u) {
-      bt.k[u] = kin[(off + bt.src[u]) * CPR + part];
-      bt.v[u] = __builtin_nontemporal_load(&vin[(off + bt.src[u]) * CPR + part]);
-      bt.pos[u] = a.pos[off + bt.src[u]];
-    }
-  };
-  auto store = [&](const Batch& bt, int r0) {
-#pragma unroll
-    for (int u = 0; u < GU; ++u) {
-      const int r = r0 + u * RPP + rsub;
-      if (r < cnt) {
-        const int64_t dst = oo + base + r;
-        __builtin_nontemporal_store(bt.k[u], &kout[dst * CPR + part]);
-        __builtin_nontemporal_store(bt.v[u], &vout[dst * CPR + part]);
-        if (part == 0) {
-          a.pos_out[dst] = bt.pos[u];
-          if (a.kept) a.kept[dst] = bt.src[u];
-        }
-      }
-    }
-  };
-  if (cnt > 0) {
-    Batch b0, b1, b2, b3;
-    load(b0, 0);
-    load(b1, STEP);
-    for (int r0 = 0; r0 < cnt; r0 += 4 * STEP) {
-      load(b2, r0 + 2 * STEP);
-      store(b0, r0);
-      load(b3, r0 + 3 * STEP);
-      store(b1, r0 + STEP);
-      if (r0 + 2 * STEP >= cnt) break;
-      load(b0, r0 + 4 * STEP);
-      store(b2, r0 + 2 * STEP);
-      load(b1, r0 + 5 * STEP);
-      store(b3, r0 + 3 * STEP);
-    }
-  }
+  // gather this chunk's kept rows to output rows base .. base + cnt - 1
+  gather_rows<CPR>([&](int r) { return mine[r]; }, cnt, a.k, a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, a.kept,
+                   oo + base, tid);
 }
 
 template <int D, int RT, int MODE>

@@ -69,6 +69,73 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
   return t;
 }
 
+// Row gather of a 256-thread work-group: output rows dst0 + r <- input rows
+// in_off + src_at(r) for r in [0, cnt), K and V (CPR 16-byte chunks per row)
+// and the position; kept_out[dst0 + r] = src_at(r) when kept_out is set.
+// src_at reads LDS (it must not issue a memory load).  GU rows per thread and
+// batch, four batches in registers: the memory counter retires loads and
+// stores in issue order and a batch's registers may only be reloaded once its
+// stores are done, so the loads run two batches ahead of the stores and a
+// batch is reloaded two batches after its stores, which leaves two batches in
+// flight at every wait.  Loads past the last row repeat it (no branch).
+template <int CPR, int GU = 2, typename SrcAt>
+__device__ __forceinline__ void gather_rows(const SrcAt& src_at, int cnt, const void* k, const void* v,
+                                            const int32_t* pos, int64_t in_off, void* k_out, void* v_out,
+                                            int32_t* pos_out, int32_t* kept_out, int64_t dst0, int tid) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int RPP = 256 / CPR;             // rows per thread-row
+  constexpr int STEP = RPP * GU;
+  if (cnt <= 0) return;
+  const u32x4* kin = static_cast<const u32x4*>(k);
+  const u32x4* vin = static_cast<const u32x4*>(v);
+  u32x4* kout = static_cast<u32x4*>(k_out);
+  u32x4* vout = static_cast<u32x4*>(v_out);
+  const int part = tid % CPR, rsub = tid / CPR;
+  struct Batch {
+    u32x4 k[GU], v[GU];
+    int src[GU], pos[GU];
+  };
+  auto load = [&](Batch& bt, int r0) {
+#pragma unroll
+    for (int u = 0; u < GU; ++u) bt.src[u] = src_at(min(r0 + u * RPP + rsub, cnt - 1));
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      bt.k[u] = kin[(in_off + bt.src[u]) * CPR + part];
+      bt.v[u] = __builtin_nontemporal_load(&vin[(in_off + bt.src[u]) * CPR + part]);
+      bt.pos[u] = pos[in_off + bt.src[u]];
+    }
+  };
+  auto store = [&](const Batch& bt, int r0) {
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int r = r0 + u * RPP + rsub;
+      if (r < cnt) {
+        const int64_t dst = dst0 + r;
+        __builtin_nontemporal_store(bt.k[u], &kout[dst * CPR + part]);
+        __builtin_nontemporal_store(bt.v[u], &vout[dst * CPR + part]);
+        if (part == 0) {
+          pos_out[dst] = bt.pos[u];
+          if (kept_out) kept_out[dst] = bt.src[u];
+        }
+      }
+    }
+  };
+  Batch b0, b1, b2, b3;
+  load(b0, 0);
+  load(b1, STEP);
+  for (int r0 = 0; r0 < cnt; r0 += 4 * STEP) {
+    load(b2, r0 + 2 * STEP);
+    store(b0, r0);
+    load(b3, r0 + 3 * STEP);
+    store(b1, r0 + STEP);
+    if (r0 + 2 * STEP >= cnt) break;
+    load(b0, r0 + 4 * STEP);
+    store(b2, r0 + 2 * STEP);
+    load(b1, r0 + 5 * STEP);
+    store(b3, r0 + 3 * STEP);
+  }
+}
+
 // Threshold of a top-kc selection: find the kc-th largest order key T among the
 // candidate keys of the work-group (MSB-first radix select over LDS histograms
 // of at most 8-bit digits) and kk, the number of candidates equal to T that
