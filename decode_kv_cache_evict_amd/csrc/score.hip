@@ -88,25 +88,37 @@ __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __rest
     }
   }
   const int hpg = (n_q + hsplit - 1) / hsplit;
-  for (int h = hg * hpg; h < min(n_q, (hg + 1) * hpg); ++h) {
-    const int64_t row = (int64_t(b) * n_q + h) * max_obs + o;
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-    if (live) {
-      const uint4 x = *reinterpret_cast<const uint4*>(q + row * D + i0);
-      const uint4 y = *reinterpret_cast<const uint4*>(q + row * D + i0 + half);
-      const T* xe = reinterpret_cast<const T*>(&x);
-      const T* ye = reinterpret_cast<const T*>(&y);
-      T* le = reinterpret_cast<T*>(&lo);
-      T* he = reinterpret_cast<T*>(&hi);
+  const int h_beg = hg * hpg, h_end = min(n_q, h_beg + hpg);
+  constexpr int HB = 4;                           // heads whose loads are in flight together
+  for (int h0 = h_beg; h0 < h_end; h0 += HB) {
+    uint4 x[HB], y[HB];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const RotPair r = rotate_pair(double(Elem<T>::widen(xe[v])), double(Elem<T>::widen(ye[v])), cs[v], sn[v]);
-        le[v] = Elem<T>::from_f64(r.a);
-        he[v] = Elem<T>::from_f64(r.b);
-      }
+    for (int u = 0; u < HB; ++u) {
+      // a head past the group's end repeats its last head (same values, same place)
+      const int64_t row = (int64_t(b) * n_q + min(h0 + u, h_end - 1)) * max_obs + o;
+      x[u] = live ? *reinterpret_cast<const uint4*>(q + row * D + i0) : make_uint4(0, 0, 0, 0);
+      y[u] = live ? *reinterpret_cast<const uint4*>(q + row * D + i0 + half) : make_uint4(0, 0, 0, 0);
     }
-    *reinterpret_cast<uint4*>(qr + row * D + i0) = lo;
-    *reinterpret_cast<uint4*>(qr + row * D + i0 + half) = hi;
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      const int64_t row = (int64_t(b) * n_q + min(h0 + u, h_end - 1)) * max_obs + o;
+      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const T* xe = reinterpret_cast<const T*>(&x[u]);
+        const T* ye = reinterpret_cast<const T*>(&y[u]);
+        T* le = reinterpret_cast<T*>(&lo);
+        T* he = reinterpret_cast<T*>(&hi);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const RotPair r =
+              rotate_pair(double(Elem<T>::widen(xe[v])), double(Elem<T>::widen(ye[v])), cs[v], sn[v]);
+          le[v] = Elem<T>::from_f64(r.a);
+          he[v] = Elem<T>::from_f64(r.b);
+        }
+      }
+      *reinterpret_cast<uint4*>(qr + row * D + i0) = lo;
+      *reinterpret_cast<uint4*>(qr + row * D + i0 + half) = hi;
+    }
   }
 }
 
@@ -916,8 +928,8 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
   int* ctl = reinterpret_cast<int*>(w);
   const int64_t base_work = int64_t(batch) * a.max_obs * (a.head_dim / 2) / (16 / int64_t(elem));
-  int hsplit = 1;                              // head groups: about 64K threads in all
-  while (hsplit < a.n_q && base_work * hsplit < 65536) hsplit *= 2;
+  int hsplit = 1;                              // head groups of at least 4 heads: about 64K threads in all
+  while (a.n_q >= 8 * hsplit && base_work * hsplit < 65536) hsplit *= 2;
   const int64_t n_work = base_work * hsplit;
   const dim3 rg(unsigned((n_work + 255) / 256));
   if (n_work > 0) {

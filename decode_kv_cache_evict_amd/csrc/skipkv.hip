@@ -8,10 +8,10 @@
 //
 //   sent_mean_kernel: one work-group per (sentence, request): fp32 sums of the
 //     bf16 rows, 16-byte loads, then the mean scaled to unit length;
-//   pss_kernel: 32x32 tiles of sentence pairs (upper triangle only), the unit
-//     means staged through LDS 64 dimensions at a time, 2x2 dot products per
-//     thread in fp32; each row's best later partner goes to a global
-//     order-preserving atomic maximum;
+//   pss_kernel: 32x32 tiles of sentence pairs (upper triangle only), the dot
+//     products of the unit means on the fp32 matrix cores (four waves, a
+//     quarter of the dimensions each, summed in LDS); each row's best later
+//     partner goes to a global order-preserving atomic maximum;
 //   skipkv_finish_kernel: PSS, marks and per-token scores.
 #include <cmath>
 
@@ -23,7 +23,6 @@ namespace kve {
 namespace {
 
 constexpr int kPssTile = 32;
-constexpr int kPssK = 64;
 
 __device__ __forceinline__ float order_key_to_float(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -53,7 +52,19 @@ __global__ __launch_bounds__(256) void sent_mean_kernel(SkipArgs a) {
   const float inv_n = hi > lo ? 1.f / float(hi - lo) : 0.f;
   for (int cchunk = tid; cchunk < nc; cchunk += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = lo; t < hi; ++t) {
+    int t = lo;
+    for (; t + 4 <= hi; t += 4) {                    // four rows' loads in flight, summed in token order
+      uint4 raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = h[int64_t(t + u) * nc + cchunk];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t* v = reinterpret_cast<const uint16_t*>(&raw[u]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += bf16_to_f32(v[k]);
+      }
+    }
+    for (; t < hi; ++t) {
       const uint4 raw = h[int64_t(t) * nc + cchunk];
       const uint16_t* v = reinterpret_cast<const uint16_t*>(&raw);
 #pragma unroll
@@ -81,43 +92,65 @@ __global__ __launch_bounds__(256) void pss_init_kernel(uint32_t* key, int n) {
   if (i < n) key[i] = float_order_key(-1.f);
 }
 
+// One work-group per 32x32 tile of sentence pairs (upper triangle of tiles).
+// The tile's dot products run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: lane l holds A row l%16 and B column l%16 at
+// k-slot l/16, and result rows 4*(l/16)+i of column l%16); the four waves split
+// the dimensions into quarters and their partial tiles are summed in LDS.  A
+// dot product does not depend on the order of its terms, so lane group q takes
+// dimensions k + 4q .. k + 4q + 3 of each 16-dimension step with one 16-byte
+// load and feeds them to four successive products.
 __global__ __launch_bounds__(256) void pss_kernel(SkipArgs a) {
-  __shared__ float A[kPssTile][kPssK + 1], Bt[kPssTile][kPssK + 1];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float part[4][kPssTile][kPssTile + 1];
   __shared__ uint32_t best[kPssTile];
   const int b = blockIdx.z, ti = blockIdx.y, tj = blockIdx.x;
   if (tj < ti) return;                                // upper triangle of tiles only
   const int ns = min(max(a.n_sent[b], 0), a.max_sent);
   const int i0 = ti * kPssTile, j0 = tj * kPssTile;
   if (i0 >= ns || j0 >= ns) return;
-  const int tid = threadIdx.x;
-  const int ri = (tid / 16) * 2, cj = (tid % 16) * 2;   // this thread's 2x2 block
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
   const float* E = a.emb + int64_t(b) * a.max_sent * a.d_model;
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  if (tid < kPssTile) best[tid] = float_order_key(-1.f);
-  for (int k0 = 0; k0 < a.d_model; k0 += kPssK) {
-    __syncthreads();
-    for (int x = tid; x < kPssTile * kPssK; x += 256) {
-      const int r = x / kPssK, k = x % kPssK;
-      A[r][k] = i0 + r < ns ? E[int64_t(i0 + r) * a.d_model + k0 + k] : 0.f;
-      Bt[r][k] = j0 + r < ns ? E[int64_t(j0 + r) * a.d_model + k0 + k] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < kPssK; ++k) {
-      const float a0 = A[ri][k], a1 = A[ri + 1][k], b0 = Bt[cj][k], b1 = Bt[cj + 1][k];
-      acc[0][0] = fmaf(a0, b0, acc[0][0]);
-      acc[0][1] = fmaf(a0, b1, acc[0][1]);
-      acc[1][0] = fmaf(a1, b0, acc[1][0]);
-      acc[1][1] = fmaf(a1, b1, acc[1][1]);
+  const int last = a.max_sent - 1;                    // rows past the tile's end repeat a valid row (masked below)
+  const float4* pa0 = reinterpret_cast<const float4*>(E + int64_t(min(i0 + r16, last)) * a.d_model);
+  const float4* pa1 = reinterpret_cast<const float4*>(E + int64_t(min(i0 + 16 + r16, last)) * a.d_model);
+  const float4* pb0 = reinterpret_cast<const float4*>(E + int64_t(min(j0 + r16, last)) * a.d_model);
+  const float4* pb1 = reinterpret_cast<const float4*>(E + int64_t(min(j0 + 16 + r16, last)) * a.d_model);
+  const int kq = a.d_model / 4;                       // dimensions per wave (a multiple of 16)
+  const int kb = w * kq;
+  f32x4 c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00;
+#pragma unroll 4
+  for (int k = kb; k < kb + kq; k += 16) {
+    const int v = (k >> 2) + q;
+    const float4 xa0 = pa0[v], xa1 = pa1[v], xb0 = pb0[v], xb1 = pb1[v];
+    const float ea0[4] = {xa0.x, xa0.y, xa0.z, xa0.w}, ea1[4] = {xa1.x, xa1.y, xa1.z, xa1.w};
+    const float eb0[4] = {xb0.x, xb0.y, xb0.z, xb0.w}, eb1[4] = {xb1.x, xb1.y, xb1.z, xb1.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c00 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea0[u], eb0[u], c00, 0, 0, 0);
+      c01 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea0[u], eb1[u], c01, 0, 0, 0);
+      c10 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea1[u], eb0[u], c10, 0, 0, 0);
+      c11 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea1[u], eb1[u], c11, 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int i = i0 + ri + x, j = j0 + cj + y;
-      if (j > i && i < ns && j < ns) atomicMax(&best[ri + x], float_order_key(acc[x][y]));
+  for (int x = 0; x < 4; ++x) {
+    part[w][4 * q + x][r16] = c00[x];
+    part[w][4 * q + x][16 + r16] = c01[x];
+    part[w][16 + 4 * q + x][r16] = c10[x];
+    part[w][16 + 4 * q + x][16 + r16] = c11[x];
+  }
+  if (tid < kPssTile) best[tid] = float_order_key(-1.f);
+  __syncthreads();
+  for (int e = tid; e < kPssTile * kPssTile; e += 256) {
+    const int r = e / kPssTile, c = e % kPssTile;
+    const int i = i0 + r, j = j0 + c;
+    if (j > i && i < ns && j < ns) {
+      const float dot = (part[0][r][c] + part[1][r][c]) + (part[2][r][c] + part[3][r][c]);
+      atomicMax(&best[r], float_order_key(dot));
     }
+  }
   __syncthreads();
   if (tid < kPssTile && i0 + tid < ns) atomicMax(&a.pss_key[int64_t(b) * a.max_sent + i0 + tid], best[tid]);
 }
