@@ -54,6 +54,18 @@ kve_status check_cache(const kve_cache* c, const char* name, bool need_v) {
   return KVE_OK;
 }
 
+// Polls a single-read work-group makes at a segment barrier before it reports
+// the segment failed; KVE_SPIN_LIMIT (a positive count) overrides the default
+// so that tests can drive the timeout path on purpose.
+int32_t spin_limit() {
+  const char* e = std::getenv("KVE_SPIN_LIMIT");
+  if (e) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v > 0 && v <= (1L << 30)) return int32_t(v);
+  }
+  return 1 << 22;
+}
+
 size_t rows_bytes(const kve_cache* c) { return size_t(c->n_rows) * c->head_dim * elem_bytes(c->dtype); }
 
 // Scoring implementation for bf16 caches: two MFMA passes (default), the
@@ -109,6 +121,7 @@ kve::ScoreArgs score_args(const kve_cache* c, const kve_obs* o, int32_t rows, fl
   a.theta = o->rope_theta;
   a.aggregate = o->aggregate;
   a.scores = scores;
+  a.spin_limit = spin_limit();
   return a;
 }
 

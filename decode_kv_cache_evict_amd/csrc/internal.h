@@ -35,6 +35,7 @@ struct ScoreArgs {
   int32_t n_chunks;
   int32_t chunk;          // keys per work-group
   int32_t impl;           // 0: two-pass MFMA, 1: plain VALU, 2: single-read MFMA
+  int32_t spin_limit;     // polls at a segment barrier (single-read kernels) before giving up
   // fused score -> select -> compact (kv_evict_score_select_compact) only
   const void* v;
   void* k_out; void* v_out; int32_t* pos_out;

@@ -398,8 +398,7 @@ __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float 
 // a running work-group, so every chunk of a segment but those of the newest
 // segment in a queue is held by a running or finished work-group, and missing
 // chunks are taken as soon as any older work-group finishes.  The wait is
-// bounded (kSpinLimit polls).
-constexpr int kSpinLimit = 1 << 22;
+// bounded (ScoreArgs::spin_limit polls).
 constexpr int kQueues = 8;
 constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3;
 
@@ -416,6 +415,22 @@ __device__ __forceinline__ void store_stat(float2* p, float2 v) {
 __device__ __forceinline__ float2 load_stat(const float2* p) {
   return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Segment barrier of the single-read kernels, thread 0 only: count this
+// work-group in and poll until all nch work-groups of the segment are in, for
+// at most `limit` polls.  Returns false on a timeout (the scheduling above
+// rules it out; it would take a device stalled for that long) after pushing
+// the counter far below zero, so that no work-group of the segment passes this
+// barrier afterwards and each of them reports the segment as failed.
+__device__ __forceinline__ bool segment_barrier(int* arrive, int nch, int limit) {
+  atomicAdd(arrive, 1);
+  int spins = 0;
+  while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < limit)
+    __builtin_amdgcn_s_sleep(1);
+  if (spins < limit) return true;
+  atomicAdd(arrive, -(1 << 24));
+  return false;
 }
 
 // Ticket from the XCD-local queue, else from any other; -1 when all are empty.
@@ -439,8 +454,8 @@ __device__ __forceinline__ int take_ticket(const ScoreArgs& a, int* ctl) {
 // its own chunk's kept rows to their places in the output segment.
 // keys: LDS scratch of step_max_seg(D) words.
 template <int D>
-__device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
-                                                    uint32_t* keys, int tid) {
+__device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
+                                                   uint32_t* keys, int tid) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
@@ -455,7 +470,7 @@ __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, i
   const bool first = k0 == 0;
   if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D)) {
     if (first && tid == 0) a.out_len[s] = -1;
-    return;
+    return -1;
   }
   int base = 0, cnt = 0;                     // output row of this chunk's first kept slot; kept count
   if (K >= n) {
@@ -533,11 +548,11 @@ __device__ __forceinline__ void step_select_compact(const ScoreArgs& a, int s, i
       eq_seen += eq_tot;
     }
   }
-  if (first && tid == 0) a.out_len[s] = keep_n;
   __syncthreads();
   // gather this chunk's kept rows to output rows base .. base + cnt - 1
   gather_rows<CPR>([&](int r) { return mine[r]; }, cnt, a.k, a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, a.kept,
                    oo + base, tid);
+  return keep_n;
 }
 
 template <int D, int RT, int MODE>
@@ -581,6 +596,8 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   }
   const int k1 = min(n, k0 + a.chunk);
   const int nch = (n + a.chunk - 1) / a.chunk;
+  // the segment counts as failed until its last work-group has gathered its rows
+  if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
   const bool mean = a.aggregate != 0;
@@ -708,14 +725,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // segment barrier: the stores above are acknowledged before the arrival count
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    int* arrive = ctl + kQueues + s;
-    atomicAdd(arrive, 1);
-    int spins = 0;
-    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
-      __builtin_amdgcn_s_sleep(1);
-  }
+  if (tid == 0) sh_item = segment_barrier(ctl + kQueues + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
+  if (sh_item < 0) {                       // the segment's work-groups did not meet: it stays failed
+    if (MODE != kModeStep)
+      for (int j = k0 + tid; j < k1; j += 256) a.scores[off + j] = __builtin_nanf("");
+    return;
+  }
   for (int r = tid; r < 16 * 4 * RT; r += 256) {
     float lse = kInf;
     if (r < a.rows && rpos_s[r] >= 0) {
@@ -748,15 +764,18 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // second segment barrier: every chunk's scores are stored
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    int* arrive = ctl + kQueues + a.n_seg + s;
-    atomicAdd(arrive, 1);
-    int spins = 0;
-    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch && ++spins < kSpinLimit)
-      __builtin_amdgcn_s_sleep(1);
-  }
+  if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
-  step_select_compact<D>(a, s, off, n, k0, k1, reinterpret_cast<uint32_t*>(&kt[0][0]), tid);
+  if (sh_item < 0) return;
+  const int keep_n = step_select_compact<D>(a, s, off, n, k0, k1, reinterpret_cast<uint32_t*>(&kt[0][0]), tid);
+  if (keep_n < 0) return;
+  // every work-group of the segment has gathered its rows: the last one to
+  // finish publishes the segment's length (a work-group that gave up at a
+  // barrier never counts in, so a failed segment keeps -1)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
+    __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pass 1 and the single-read kernel carry the row statistics in registers; all
@@ -867,7 +886,7 @@ hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
 
 template <int D, int RT>
 hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
-  const int n_ctl = kQueues + 2 * a.n_seg;
+  const int n_ctl = kQueues + 3 * a.n_seg;       // tickets, two arrival counters and a finish counter per segment
   hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
   hipLaunchKernelGGL((score_step_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
@@ -902,7 +921,7 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
   const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
-  const size_t ct = align_up(size_t(2 * n_seg + kQueues) * sizeof(int));
+  const size_t ct = align_up(size_t(3 * n_seg + kQueues) * sizeof(int));
   return qr + st + ls + ct;
 }
 

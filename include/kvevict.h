@@ -219,6 +219,9 @@ size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_ob
  * ReasonAlloc's reallocation needs comes from kv_evict_score.  Ties between
  * near-equal scores may resolve differently from the two-call form, since the
  * softmax normaliser is summed in another order (scores agree to fp32 rounding).
+ * A segment's work-groups wait for each other with bounded polling; a segment
+ * whose work-groups could not all run within that bound (only possible on a
+ * device stalled for a long time) gets out->seg_len[s] = -1 like a rejected one.
  * Errors: the union of kv_evict_score's and kv_evict_select_compact's; scores,
  * the output cache, kept_idx and the workspace must not overlap any input or
  * each other (EALIAS).

@@ -5,7 +5,8 @@ Cases span several 1024-key chunks with ragged tails, both head sizes, the
 single-kernel path and the two-call fallback (fp32 caches, segments longer
 than the on-chip selection, a forced VALU scorer), per-segment budgets with
 the degenerate ones (K >= n, K below the protected slots, K above the output
-capacity) and repeated calls on the same workspace."""
+capacity), repeated calls on the same workspace, and the report of a segment
+whose work-groups did not meet within the barrier's poll bound."""
 import numpy as np
 import pytest
 import torch
@@ -216,3 +217,34 @@ def test_forced_valu_scorer_takes_the_two_call_path(monkeypatch):
     torch.cuda.synchronize()
     assert_scores_close(scores.cpu().numpy(), s_orc)
     _check_segments(w, L, D, out, s_orc, [budget] * len(L["seg_len"]))
+
+
+def test_barrier_timeout_reports_failed_segments(monkeypatch):
+    """With the segment barrier's poll bound forced down to one poll (the
+    failure handling path, driven from the host), a segment whose work-groups
+    do not all arrive at once is reported failed (seg_len -1) rather than
+    selected from partial row statistics; every kernel exits, and a segment
+    that did meet is exact.  A later call with the default bound is whole."""
+    w, budget, L, D, s_orc = _case("llama-ragged")
+    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    out = alloc_out(D, w, budget)
+    score_select_compact(D, w, out, uniform=budget)
+    torch.cuda.synchronize()
+    lens = out["seg_len"].cpu().numpy()
+    kept = out["kept"].cpu().numpy()
+    k_in, k_out = _ints(D["k"], w), _ints(out["k"], w)
+    cap = out["cap"]
+    for s in range(len(lens)):
+        o, n = int(L["seg_off"][s]), int(L["seg_len"][s])
+        if lens[s] == -1:
+            continue
+        assert lens[s] == min(budget, n), (s, lens[s])
+        ks = kept[s * cap:s * cap + lens[s]]
+        ok, _, msg = kept_matches(ks, s_orc[o:o + n], n, budget, w.n_prefix, w.n_recent)
+        assert ok, f"segment {s}: {msg}"
+        assert np.array_equal(k_out[s * cap:s * cap + lens[s]], k_in[o + ks])
+    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    out2 = alloc_out(D, w, budget)
+    score_select_compact(D, w, out2, uniform=budget)
+    torch.cuda.synchronize()
+    _check_segments(w, L, D, out2, s_orc, [budget] * len(L["seg_len"]))
