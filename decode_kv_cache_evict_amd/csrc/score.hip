@@ -808,19 +808,30 @@ __global__ void zero_ints_kernel(int* p, int n) {
 }
 
 // ------------------------------------------------------------ entropy
-// E = (ln S - sum(s ln s) / S) / ln n over one segment's scores, in double.
+// E = (ln S - sum(s ln s) / S) / ln n over one segment's scores: each term
+// s log2 s in fp32 (the hardware log2, about one ulp; scores under 1e-30 are
+// left out), the sums in double, four loads in flight per thread.
 __global__ __launch_bounds__(256) void entropy_kernel(ScoreArgs a) {
   __shared__ double part[2][4];
   const int s = blockIdx.x;
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) return;
-  double S = 0.0, Q = 0.0;
-  for (int j = threadIdx.x; j < n; j += 256) {
-    const double v = a.scores[off + j];
-    S += v;
-    if (v > 0.0) Q += v * log(v);
+  double S = 0.0, Q2 = 0.0;
+  const float* sc = a.scores + off;
+  for (int j0 = 0; j0 < n; j0 += 4 * 256) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = sc[min(j0 + u * 256 + int(threadIdx.x), n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u * 256 + int(threadIdx.x) < n) {
+        S += double(v[u]);
+        // terms below 1e-30 (and the denormals the hardware log2 does not take) add under 1e-28 each
+        if (v[u] > 1e-30f) Q2 += double(v[u] * __builtin_amdgcn_logf(v[u]));
+      }
   }
+  double Q = Q2 * 0.69314718055994530942;    // log2 -> ln
   S = wave_sum_f64(S);
   Q = wave_sum_f64(Q);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
