@@ -46,10 +46,11 @@ def parse():
                     help="attention: time kv_decode_attention over the compacted cache; skipkv: time the "
                          "sentence-redundancy score (SkipKV) on sentence-structured hidden states; epikv: "
                          "the attention-free hidden-state score and its select/compact (long-65k)")
-    ap.add_argument("--call", choices=["split", "fused", "inplace"], default="fused",
+    ap.add_argument("--call", choices=["split", "fused", "inplace", "inplace-split"], default="fused",
                     help="split: kv_evict_score then kv_evict_select_compact; "
                          "fused: kv_evict_score_select_compact (one kernel per call); "
-                         "inplace: kv_evict_score then kv_evict_select_compact_inplace (hole filling)")
+                         "inplace: kv_evict_score_select_compact_inplace (hole filling, one kernel per call); "
+                         "inplace-split: kv_evict_score then kv_evict_select_compact_inplace")
     return ap.parse_args()
 
 
@@ -186,7 +187,7 @@ class StepRunner:
         import decode_kv_cache_evict_amd as kv
         self.w, self.states, self.scores, self.kept, self.fps_out = w, states, scores, kept, fps_out
         self.ws_score, self.schedule, self.call = ws_score, schedule, call
-        if call in ("fused", "inplace"):
+        if call in ("fused", "inplace", "inplace-split"):
             select_group = score_group
         self.new_len = torch.empty_like(states[0].seg_len)
         L, B, Hkv = w.n_layers, w.batch, w.n_kv_heads
@@ -223,17 +224,23 @@ class StepRunner:
         if side is not main:
             side.wait_stream(main)
         kv.beacon_fps_update(st.buf, self.fps_out[0], st.count, self.fps_out[1], w.fps_keep, stream=side)
-        if self.call == "inplace":
-            # scoring, then hole filling within the trigger's own cache; the new
-            # lengths go to a separate array so every step sees the same n
+        if self.call in ("inplace", "inplace-split"):
+            # hole filling within the trigger's own cache (one call, or scoring
+            # then the in-place select); the new lengths go to a separate array
+            # so every step sees the same n
             for ci, ((_, cache, obs), (_, ccache, _)) in enumerate(zip(sc, cc)):
                 if timing is not None:
                     timing[ci][0].record(main)
-                kv.kv_evict_score(cache, obs, self.scores, ws=self.ws_score, stream=main)
                 l0, l1 = self.cgroups[ci]
                 seg = slice(l0 * w.batch * w.n_kv_heads, l1 * w.batch * w.n_kv_heads)
-                kv.kv_evict_select_compact_inplace(ccache, self.scores, None, w.n_prefix, w.n_recent,
-                                                   self.new_len[seg], uniform_budget=w.budget, stream=main)
+                if self.call == "inplace":
+                    kv.kv_evict_score_select_compact_inplace(ccache, obs, self.scores, None, w.n_prefix, w.n_recent,
+                                                             self.new_len[seg], uniform_budget=w.budget,
+                                                             ws=self.ws_score, stream=main)
+                else:
+                    kv.kv_evict_score(cache, obs, self.scores, ws=self.ws_score, stream=main)
+                    kv.kv_evict_select_compact_inplace(ccache, self.scores, None, w.n_prefix, w.n_recent,
+                                                       self.new_len[seg], uniform_budget=w.budget, stream=main)
                 if timing is not None:
                     timing[ci][1].record(main)
             if side is not main:
@@ -331,11 +338,14 @@ def step_bytes(w, call="fused"):
     # in place (hole filling): scoring, the scores read back, and at most
     # min(K, n-K) rows per segment moved (K, V, pos read and written)
     b["inplace_moves"] = 2 * S * min(keep, n - keep) * (2 * row + 4)
-    b["inplace_step"] = b["score"] + b["select_scores"] + b["inplace_moves"]
+    b["inplace_split_step"] = b["score"] + b["select_scores"] + b["inplace_moves"]
+    # one call: the scores are written once and the selection reads them back on chip
+    b["inplace_step"] = b["score"] + b["inplace_moves"]
     # the step's algorithmic bytes: the one-kernel form's (the split form adds
     # a write and re-read of the scores and a second read of the kept K rows);
     # the in-place form moves only the displaced survivors
-    b["total"] = (b["inplace_step"] if call == "inplace" else b["fused_step"]) + b["fps"]
+    b["total"] = {"inplace": b["inplace_step"], "inplace-split": b["inplace_split_step"]}.get(call, b["fused_step"]) \
+        + b["fps"]
     return b
 
 
@@ -759,6 +769,8 @@ def main():
         cout0 = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"][:per_group * w.batch * w.n_kv_heads],
                               out["seg_len"][:per_group * w.batch * w.n_kv_heads], w.n_kv_heads, out["cap"])
         nws = kv.kv_evict_score_select_compact_workspace(c0, o0, cout0, False)
+    elif args.call == "inplace":
+        nws = kv.kv_evict_score_select_compact_inplace_workspace(c0, o0)
     else:
         nws = kv.kv_evict_score_workspace(c0, o0)
     ws_score = torch.empty(nws + 256, dtype=torch.uint8, device=dev)
@@ -802,7 +814,8 @@ def main():
     tokens = w.n_layers * w.batch * w.len_hi
     nb = step_bytes(w, args.call)
     dom_layers = runner.cgroups[0][1] - runner.cgroups[0][0]
-    dom_key = {"fused": "fused_step", "split": "select_compact", "inplace": "inplace_step"}[args.call]
+    dom_key = {"fused": "fused_step", "split": "select_compact", "inplace": "inplace_step",
+               "inplace-split": "inplace_split_step"}[args.call]
     dom_bytes = nb[dom_key] * dom_layers / w.n_layers
     achieved = dom_bytes / (sc_ms * 1e-3) / 1e9
     res = {
@@ -826,8 +839,10 @@ def main():
         "roofline": {"bound": "hbm",
                      "kernel": {"fused": "kv_evict_score_select_compact (score, radix select and gather in one kernel)",
                                 "split": "kv_evict_select_compact (radix select + gather compaction)",
-                                "inplace": "kv_evict_score + kv_evict_select_compact_inplace (hole filling; at most "
-                                           "min(K, n-K) rows moved per segment)"}[args.call]
+                                "inplace": "kv_evict_score_select_compact_inplace (one kernel: score, select and "
+                                           "hole filling; at most min(K, n-K) rows moved per segment)",
+                                "inplace-split": "kv_evict_score + kv_evict_select_compact_inplace (hole filling; at "
+                                                 "most min(K, n-K) rows moved per segment)"}[args.call]
                      + f", {dom_layers} layer(s) per launch",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,

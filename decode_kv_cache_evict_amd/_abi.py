@@ -23,7 +23,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_wave_budgets",
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
            "kv_evict_score_select_compact_workspace",
-           "kv_evict_score_select_compact", "beacon_fps_update",
+           "kv_evict_score_select_compact", "kv_evict_score_select_compact_inplace_workspace",
+           "kv_evict_score_select_compact_inplace", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
            "kv_decode_attention_workspace", "kv_decode_attention",
            "kv_rope_apply", "kve_last_error", "kve_abi_version"]
@@ -73,6 +74,8 @@ def lib():
             "kv_evict_select_compact_inplace": (I32, [CP, P, P, I64, P, I32, I32, I32, P, P]),
             "kv_evict_score_select_compact_workspace": (SZ, [CP, OP, CP, I32]),
             "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
+            "kv_evict_score_select_compact_inplace_workspace": (SZ, [CP, OP]),
+            "kv_evict_score_select_compact_inplace": (I32, [CP, OP, P, P, I32, I32, I32, P, P, SZ, P]),
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
             "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, I32, P, P, P, SZ, P]),
@@ -227,6 +230,21 @@ def kv_evict_score_select_compact(cache_in, obs, scores, budget, n_prefix, n_rec
     _check(lib().kv_evict_score_select_compact(ctypes.byref(cache_in), ctypes.byref(obs), _ptr(scores), _ptr(budget),
                                                int(uniform_budget), int(n_prefix), int(n_recent), _ptr(kept_idx),
                                                ctypes.byref(cache_out), wp, wn, _stream(stream)))
+
+
+def kv_evict_score_select_compact_inplace_workspace(cache, obs):
+    return int(lib().kv_evict_score_select_compact_inplace_workspace(ctypes.byref(cache), ctypes.byref(obs)))
+
+
+def kv_evict_score_select_compact_inplace(cache, obs, scores, budget, n_prefix, n_recent, new_len, uniform_budget=0,
+                                          ws=None, stream=None):
+    """One trigger compacted in place by hole filling; new_len int32 [n_seg] (may be the cache's seg_len)."""
+    if ws is None:
+        ws = _ws(kv_evict_score_select_compact_inplace_workspace(cache, obs), scores.device)
+    wp, wn = _aligned(ws)
+    _check(lib().kv_evict_score_select_compact_inplace(ctypes.byref(cache), ctypes.byref(obs), _ptr(scores),
+                                                       _ptr(budget), int(uniform_budget), int(n_prefix),
+                                                       int(n_recent), _ptr(new_len), wp, wn, _stream(stream)))
 
 
 def beacon_fps_update(q_in, q_out, count_in, count_out, k_keep, picks=None, stream=None):

@@ -423,6 +423,86 @@ kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, 
                        "kv_evict_score_select_compact");
 }
 
+size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const kve_obs* o) {
+  int32_t rows = 0;
+  if (check_cache(c, "cache", true) != KVE_OK || check_obs(c, o, &rows) != KVE_OK) return 0;
+  return step_score_ws(c, o, rows);
+}
+
+kve_status kv_evict_score_select_compact_inplace(kve_cache* c, const kve_obs* o, float* scores, const int32_t* budget,
+                                                 int32_t uniform_budget, int32_t n_prefix, int32_t n_recent,
+                                                 int32_t* new_len, void* ws, size_t ws_bytes, void* stream) {
+  kve_status st = check_cache(c, "cache", true);
+  if (st != KVE_OK) return st;
+  int32_t rows = 0;
+  if ((st = check_obs(c, o, &rows)) != KVE_OK) return st;
+  if (n_prefix < 0 || n_recent < 0) return fail(KVE_EINVAL, "negative prefix/recent");
+  if (c->n_seg > 0 && (!scores || !new_len)) return fail(KVE_EINVAL, "null scores or new_len");
+  if (!budget && uniform_budget < n_prefix + n_recent)
+    return fail(KVE_EBUDGET, "budget %d below prefix %d + recent %d", uniform_budget, n_prefix, n_recent);
+  const bool fused = c->dtype == KVE_BF16 && score_impl() == 0 && c->max_seg_len > 0 &&
+                     c->max_seg_len <= kve::step_max_seg(c->head_dim);
+  const int impl = c->dtype == KVE_BF16 ? score_impl() : 1;
+  if (!fused && impl == 1 && valu_lds(rows, c->head_dim, c->dtype) > 65536)
+    return fail(KVE_ESHAPE, "rows*head_dim too large for the fp32 scoring path");
+  const size_t sw = step_score_ws(c, o, rows);
+  if (ws_bytes < sw || (sw > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, sw);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
+  const int32_t batch = c->n_seg / c->n_kv_heads;
+  const size_t ns = size_t(c->n_seg), rb = rows_bytes(c), pb = size_t(c->n_rows) * 4;
+  // inputs that are only read, and the cache arrays that are read and rewritten
+  const void* ins[] = {o->q, o->q_pos, o->n_obs, budget, c->seg_off};
+  const size_t insz[] = {size_t(batch) * o->n_q_heads * o->max_obs * c->head_dim * elem_bytes(c->dtype),
+                         size_t(batch) * o->max_obs * 4, size_t(batch) * 4, budget ? ns * 4 : 0, ns * 8};
+  const void* cache[] = {c->k, c->v, c->pos};
+  const size_t cachesz[] = {rb, rb, pb};
+  const void* outs[] = {scores, ws};
+  const size_t outsz[] = {size_t(c->n_rows) * 4, sw};
+  for (int i = 0; i < 2; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], cache[j], cachesz[j]))
+        return fail(KVE_EALIAS, "output %d overlaps cache array %d", i, j);
+    if (overlap(outs[i], outsz[i], c->seg_len, ns * 4)) return fail(KVE_EALIAS, "output %d overlaps seg_len", i);
+  }
+  if (overlap(scores, outsz[0], ws, sw)) return fail(KVE_EALIAS, "scores overlap the workspace");
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 5; ++j)
+      if (overlap(cache[i], cachesz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "cache array %d overlaps input %d", i, j);
+  // new_len may be the cache's own seg_len (every work-group reads its length before any is written)
+  if (new_len != c->seg_len) {
+    const void* all[] = {c->k, c->v, c->pos, scores, c->seg_off, c->seg_len, budget, ws, o->q, o->q_pos, o->n_obs};
+    const size_t allsz[] = {rb, rb, pb, size_t(c->n_rows) * 4, ns * 8, ns * 4, budget ? ns * 4 : 0, sw,
+                            insz[0], insz[1], insz[2]};
+    for (int j = 0; j < 11; ++j)
+      if (overlap(new_len, ns * 4, all[j], allsz[j])) return fail(KVE_EALIAS, "new_len overlaps argument %d", j);
+  }
+  if (c->n_seg == 0) return KVE_OK;
+  if (!fused) {
+    if ((st = kv_evict_score(c, o, scores, nullptr, ws, sw, stream)) != KVE_OK) return st;
+    return kv_evict_select_compact_inplace(c, scores, nullptr, c->n_rows, budget, uniform_budget, n_prefix, n_recent,
+                                           new_len, stream);
+  }
+  kve::ScoreArgs a = score_args(c, o, rows, scores);
+  a.v = c->v;
+  a.k_out = c->k;
+  a.v_out = c->v;
+  a.pos_out = c->pos;
+  a.out_off = c->seg_off;
+  a.out_len = new_len;
+  a.out_rows = c->n_rows;
+  a.out_cap = c->max_seg_len;
+  a.kept = nullptr;
+  a.budget = budget;
+  a.uniform_budget = uniform_budget;
+  a.n_prefix = n_prefix;
+  a.n_recent = n_recent;
+  a.inplace = 1;
+  return device_status(kve::launch_score_select_compact(a, ws, static_cast<hipStream_t>(stream)),
+                       "kv_evict_score_select_compact_inplace");
+}
+
 kve_status beacon_fps_update(const void* q_in, void* q_out, const int32_t* count_in, int32_t* count_out, int32_t n_buf,
                              int32_t cap, int32_t k_keep, int32_t head_dim, int32_t dtype, int32_t* picks,
                              void* stream) {

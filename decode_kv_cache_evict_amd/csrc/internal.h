@@ -43,9 +43,10 @@ struct ScoreArgs {
   int32_t* kept;          // optional, aligned with output rows
   const int32_t* budget;  // [n_seg] or null
   int32_t uniform_budget, n_prefix, n_recent;
+  int32_t inplace;        // 1: hole filling within the input cache (k_out = k, out_len = new lengths)
 };
 
-// Largest segment the fused step can select on chip: its order keys reuse the
+// Largest segment the one-kernel step can select on chip: its order keys reuse the
 // two 64-key tiles of padded bf16 rows (64 * (D + 8) 32-bit words).
 constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 8); }
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);

@@ -400,7 +400,7 @@ __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float 
 // chunks are taken as soon as any older work-group finishes.  The wait is
 // bounded (ScoreArgs::spin_limit polls).
 constexpr int kQueues = 8;
-constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3;
+constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3, kModeFill = 4;
 
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
@@ -550,9 +550,134 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   }
   __syncthreads();
   // gather this chunk's kept rows to output rows base .. base + cnt - 1
-  gather_rows<CPR>([&](int r) { return mine[r]; }, cnt, a.k, a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, a.kept,
-                   oo + base, tid);
+  const int64_t dst0 = oo + base;
+  gather_rows<CPR>([&](int r) { return mine[r]; }, [&](int r) { return dst0 + r; }, cnt, a.k, a.v, a.pos, off,
+                   a.k_out, a.v_out, a.pos_out, a.kept, tid);
   return keep_n;
+}
+
+// In-place form of the one-kernel trigger (kv_evict_score_select_compact_inplace):
+// the same threshold over the segment's scores in LDS, then hole filling
+// within the cache: the survivors in [K, n), in ascending slot order, move
+// into the evicted slots of [0, K), in ascending slot order.  One pass over
+// the slots (8 consecutive per thread and round, two block scans) replaces
+// each key in LDS by (kept << 31) | (kept slots before it); a mover's rank is
+// then its kept-before count minus that of slot K, and a hole's rank its slot
+// minus its kept-before count, so this work-group finds the holes that pair
+// with the movers of its own chunk by a plain sweep and copies them.
+// Returns the segment's new length (-1 for a rejected segment).
+template <int D>
+__device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
+                                                uint32_t* keys, int tid) {
+  constexpr int CPR = D / 8;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int wtot[4];
+  __shared__ int hole_at[kMfmaChunk], mover_at[kMfmaChunk];
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  if (K >= n) return n;                      // every row stays where it is
+  if (K < P + R || K < 0) {
+    if (k0 == 0 && tid == 0) a.out_len[s] = -1;
+    return -1;
+  }
+  // the segment's scores into LDS with the candidates' min and max (as in the copying form)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j0 = 0; j0 < n; j0 += 8 * 256) {
+    float raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      raw[u] = __hip_atomic_load(&a.scores[off + min(j0 + u * 256 + tid, n - 1)], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * 256 + tid;
+      if (j < n) {
+        const uint32_t key = float_order_key(raw[u]);
+        keys[j] = key;
+        if (j >= P && j < n - R) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+  }
+  if ((tid & 63) == 0) {
+    hist[tid >> 6] = kmin;
+    hist[4 + (tid >> 6)] = kmax;
+  }
+  __syncthreads();
+  kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
+  kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+  __syncthreads();
+  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  uint32_t T, kk;
+  radix_threshold_v<256>(
+      [&](const auto& f) {
+        for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
+      },
+      K - P - R, hist, sh, T, kk, kmin, known);
+  // keys -> (kept << 31) | kept slots before
+  int kept_seen = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < n; j0 += 8 * 256) {
+    const int jt = j0 + 8 * tid;
+    uint32_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kv[u] = jt + u < n ? keys[jt + u] : 0u;
+    int n_eq = 0, n_sure = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= P && j < n - R;
+      n_eq += cand && kv[u] == T;
+      n_sure += j < n && (!cand || kv[u] > T);
+    }
+    int eq_tot;
+    const int eq_before = eq_seen + block_scan<256>(n_eq, wtot, eq_tot);
+    const int n_keep = n_sure + min(n_eq, max(0, int(kk) - eq_before));
+    int keep_tot;
+    int before = kept_seen + block_scan<256>(n_keep, wtot, keep_tot);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= P && j < n - R;
+      const bool eq = cand && kv[u] == T;
+      const bool keep = j < n && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
+      eq_rank += eq;
+      if (j < n) keys[j] = (keep ? 0x80000000u : 0u) | uint32_t(before);
+      before += keep;
+    }
+    kept_seen += keep_tot;
+    eq_seen += eq_tot;
+    __syncthreads();
+  }
+  // this chunk's movers: kept slots in [max(k0, K), k1); their ranks among all movers
+  const int base_k = int(keys[K] & 0x7fffffffu);           // kept slots before K (K < n)
+  const int s0 = max(k0, K), s1 = max(k1, K);
+  const int r_lo = (s0 < n ? int(keys[s0] & 0x7fffffffu) : K) - base_k;
+  const int r_hi = (s1 < n ? int(keys[s1] & 0x7fffffffu) : K) - base_k;
+  const int cnt = r_hi - r_lo;
+  if (cnt > 0) {
+    for (int j = s0 + tid; j < s1; j += 256) {
+      const uint32_t e = keys[j];
+      if (e >> 31) mover_at[int(e & 0x7fffffffu) - base_k - r_lo] = j;
+    }
+    for (int h = tid; h < K; h += 256) {                      // holes: evicted slots below K
+      const uint32_t e = keys[h];
+      const int rank = h - int(e & 0x7fffffffu);
+      if (!(e >> 31) && rank >= r_lo && rank < r_hi) hole_at[rank - r_lo] = h;
+    }
+  }
+  __syncthreads();
+  gather_rows<CPR>([&](int r) { return mover_at[r]; }, [&](int r) { return off + hole_at[r]; }, cnt, a.k, a.v,
+                   a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid);
+  return K;
 }
 
 template <int D, int RT, int MODE>
@@ -586,18 +711,16 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) {
-    if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
+    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
     return;
   }
   const int k0 = ch * a.chunk;
   if (k0 >= n) {
-    if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
+    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
     return;
   }
   const int k1 = min(n, k0 + a.chunk);
   const int nch = (n + a.chunk - 1) / a.chunk;
-  // the segment counts as failed until its last work-group has gathered its rows
-  if (MODE == kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
   const int b = s / a.n_kv, g = s % a.n_kv;
   const float c = kLog2e / sqrtf(float(D));
   const bool mean = a.aggregate != 0;
@@ -651,7 +774,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
         const float sc =
             mean ? (red[bi][0][tid] + red[bi][1][tid] + red[bi][2][tid] + red[bi][3][tid]) * inv_live
                  : fast_exp2(fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid])));
-        if (MODE == kModeStep)   // read back by the segment's other work-groups: coherent store
+        if (MODE >= kModeStep)   // read back by the segment's other work-groups: coherent store
           __hip_atomic_store(&a.scores[off + j], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
           a.scores[off + j] = sc;
@@ -727,8 +850,12 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   __syncthreads();
   if (tid == 0) sh_item = segment_barrier(ctl + kQueues + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
+  // Every work-group of the segment has read the segment's length by now (the
+  // output length may be the input length array): the segment counts as failed
+  // until its last work-group has moved its rows.
+  if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
   if (sh_item < 0) {                       // the segment's work-groups did not meet: it stays failed
-    if (MODE != kModeStep)
+    if (MODE < kModeStep)
       for (int j = k0 + tid; j < k1; j += 256) a.scores[off + j] = __builtin_nanf("");
     return;
   }
@@ -759,7 +886,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
   sweep(std::integral_constant<bool, true>{});
-  if (MODE != kModeStep) return;
+  if (MODE < kModeStep) return;
 
   // second segment barrier: every chunk's scores are stored
   __builtin_amdgcn_s_waitcnt(0);
@@ -767,7 +894,9 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
   if (sh_item < 0) return;
-  const int keep_n = step_select_compact<D>(a, s, off, n, k0, k1, reinterpret_cast<uint32_t*>(&kt[0][0]), tid);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(&kt[0][0]);
+  const int keep_n = MODE == kModeFill ? step_select_fill<D>(a, s, off, n, k0, k1, keys, tid)
+                                       : step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
   if (keep_n < 0) return;
   // every work-group of the segment has gathered its rows: the last one to
   // finish publishes the segment's length (a work-group that gave up at a
@@ -798,6 +927,11 @@ template <int D, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_step_kernel(ScoreArgs a,
                                                                                                    int* ctl) {
   score_mfma_body<D, RT, kModeStep>(a, ctl);
+}
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_fill_kernel(ScoreArgs a,
+                                                                                                   int* ctl) {
+  score_mfma_body<D, RT, kModeFill>(a, ctl);
 }
 
 // Zero a small int array (queue tickets and arrival counters) with a kernel, so
@@ -900,7 +1034,10 @@ hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
   const int n_ctl = kQueues + 3 * a.n_seg;       // tickets, two arrival counters and a finish counter per segment
   hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
-  hipLaunchKernelGGL((score_step_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
+  if (a.inplace)
+    hipLaunchKernelGGL((score_fill_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
+  else
+    hipLaunchKernelGGL((score_step_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
   return hipGetLastError();
 }
 

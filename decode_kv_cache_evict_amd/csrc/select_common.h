@@ -69,19 +69,19 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
   return t;
 }
 
-// Row gather of a 256-thread work-group: output rows dst0 + r <- input rows
+// Row gather of a 256-thread work-group: output rows dst_at(r) <- input rows
 // in_off + src_at(r) for r in [0, cnt), K and V (CPR 16-byte chunks per row)
-// and the position; kept_out[dst0 + r] = src_at(r) when kept_out is set.
-// src_at reads LDS (it must not issue a memory load).  GU rows per thread and
+// and the position; kept_out[dst_at(r)] = src_at(r) when kept_out is set.
+// src_at and dst_at read LDS or registers (they must not issue memory loads).  GU rows per thread and
 // batch, four batches in registers: the memory counter retires loads and
 // stores in issue order and a batch's registers may only be reloaded once its
 // stores are done, so the loads run two batches ahead of the stores and a
 // batch is reloaded two batches after its stores, which leaves two batches in
 // flight at every wait.  Loads past the last row repeat it (no branch).
-template <int CPR, int GU = 2, typename SrcAt>
-__device__ __forceinline__ void gather_rows(const SrcAt& src_at, int cnt, const void* k, const void* v,
-                                            const int32_t* pos, int64_t in_off, void* k_out, void* v_out,
-                                            int32_t* pos_out, int32_t* kept_out, int64_t dst0, int tid) {
+template <int CPR, int GU = 2, typename SrcAt, typename DstAt>
+__device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& dst_at, int cnt, const void* k,
+                                            const void* v, const int32_t* pos, int64_t in_off, void* k_out,
+                                            void* v_out, int32_t* pos_out, int32_t* kept_out, int tid) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int RPP = 256 / CPR;             // rows per thread-row
   constexpr int STEP = RPP * GU;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, int cnt, const 
     for (int u = 0; u < GU; ++u) {
       const int r = r0 + u * RPP + rsub;
       if (r < cnt) {
-        const int64_t dst = dst0 + r;
+        const int64_t dst = dst_at(r);
         __builtin_nontemporal_store(bt.k[u], &kout[dst * CPR + part]);
         __builtin_nontemporal_store(bt.v[u], &vout[dst * CPR + part]);
         if (part == 0) {

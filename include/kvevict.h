@@ -231,6 +231,32 @@ kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, 
                                          int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
                                          size_t ws_bytes, void* stream);
 
+/* Workspace bytes kv_evict_score_select_compact_inplace needs. */
+size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const kve_obs* o);
+
+/*
+ * kv_evict_score_select_compact_inplace — one eviction trigger of BeaconKV
+ * ("打分时的 RoPE 对齐" for the score; "📊 实验": eviction is permanent) compacted
+ * within the cache itself: the result of kv_evict_score(c, o, scores, NULL)
+ * followed by kv_evict_select_compact_inplace(c, scores, NULL, c->n_rows, budget,
+ * uniform_budget, n_prefix, n_recent, new_len), with the same meaning of every
+ * argument (hole filling: the survivors in [K, n), in ascending slot order,
+ * move into the evicted slots of [0, K), in ascending slot order).  For bf16
+ * caches whose max_seg_len fits the on-chip selection (8704 rows at head_dim
+ * 128, 4608 at 64) it runs as one kernel (each segment's work-groups score
+ * their chunk, wait for the segment's other chunks, select, and move the
+ * survivors of their own chunk); otherwise it makes the two calls.  The kept
+ * sets may differ from the two-call form's only where scores tie to fp32
+ * rounding (the softmax normaliser is summed in another order).  new_len may
+ * be c->seg_len itself; a segment whose work-groups could not meet within the
+ * barrier's poll bound gets -1.
+ * Errors: the union of kv_evict_score's and kv_evict_select_compact_inplace's;
+ * scores and the workspace must not overlap the cache or any input (EALIAS).
+ */
+kve_status kv_evict_score_select_compact_inplace(kve_cache* c, const kve_obs* o, float* scores, const int32_t* budget,
+                                                 int32_t uniform_budget, int32_t n_prefix, int32_t n_recent,
+                                                 int32_t* new_len, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * beacon_fps_update — BeaconKV "Continual FPS": for each of n_buf buffers of
  * pre-RoPE queries ([n_buf, cap, head_dim], dtype) whose count_in equals cap, run

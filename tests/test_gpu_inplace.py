@@ -1,14 +1,17 @@
-"""In-place hole-filling compaction (kv_evict_select_compact_inplace) against
-the oracle: the survivors are the oracle's kept set (ties within tolerance),
-their layout is exactly oracle.hole_fill of that set, the moved rows are
-byte-exact copies, and rows beyond the new length are untouched."""
+"""In-place hole-filling compaction against the oracle, both as the
+select/compact call after kv_evict_score (kv_evict_select_compact_inplace) and
+as the one-call trigger (kv_evict_score_select_compact_inplace, one kernel for
+bf16 segments up to the on-chip selection size, the two calls otherwise): the
+survivors are the oracle's kept set (ties within tolerance), their layout is
+exactly oracle.hole_fill of that set, the moved rows are byte-exact copies,
+and rows beyond the new length are untouched."""
 import numpy as np
 import pytest
 import torch
 
 import decode_kv_cache_evict_amd as kv
 import oracle
-from tests.gpu_side import cache_of, device_layer, score_layer
+from tests.gpu_side import cache_of, device_layer, obs_of, score_layer
 from tests.oracle_side import oracle_cache_keys, oracle_layer_scores
 from tests.parity import kept_matches
 from workloads import get_workload, make_layer
@@ -35,13 +38,19 @@ def _ints(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
 
-def _run(w, L, D, budgets, uniform, alias):
-    """Score, then compact in place on a copy of the cache; returns the copy."""
-    scores, _ = score_layer(D, w)
+def _run(w, L, D, budgets, uniform, alias, one_call=False):
+    """Score, then compact in place on a copy of the cache (or both in one
+    call); returns the copy and the new lengths."""
     C = dict(D, k=D["k"].clone(), v=D["v"].clone(), pos=D["pos"].clone(), seg_len=D["seg_len"].clone())
     new_len = C["seg_len"] if alias else torch.full_like(C["seg_len"], -9)
-    kv.kv_evict_select_compact_inplace(cache_of(C, w), scores, budgets, w.n_prefix, w.n_recent, new_len,
-                                       uniform_budget=uniform)
+    if one_call:
+        scores = torch.empty(C["k"].shape[0], dtype=torch.float32, device="cuda")
+        kv.kv_evict_score_select_compact_inplace(cache_of(C, w), obs_of(C, w), scores, budgets, w.n_prefix,
+                                                 w.n_recent, new_len, uniform_budget=uniform)
+    else:
+        scores, _ = score_layer(D, w)
+        kv.kv_evict_select_compact_inplace(cache_of(C, w), scores, budgets, w.n_prefix, w.n_recent, new_len,
+                                           uniform_budget=uniform)
     torch.cuda.synchronize()
     return C, new_len.cpu().numpy()
 
@@ -69,23 +78,25 @@ def _check(w, L, D, C, new_len, budgets_np, s_orc):
     return moved
 
 
+@pytest.mark.parametrize("one_call", [False, True])
 @pytest.mark.parametrize("alias", [False, True])
 @pytest.mark.parametrize("name", list(CASES))
-def test_inplace_matches_oracle(name, alias):
+def test_inplace_matches_oracle(name, alias, one_call):
     w, budget = CASES[name]
     L = make_layer(w, 0)
     assert all(np.array_equal(L["pos"][int(L["seg_off"][s]):int(L["seg_off"][s]) + int(L["seg_len"][s])].numpy(),
                               np.arange(int(L["seg_len"][s]))) for s in range(len(L["seg_len"])))
     D = device_layer(L, w)
     s_orc = oracle_layer_scores(L, w, oracle_cache_keys(L, w))
-    C, new_len = _run(w, L, D, None, budget, alias)
+    C, new_len = _run(w, L, D, None, budget, alias, one_call)
     moved = _check(w, L, D, C, new_len, np.full(len(L["seg_len"]), budget), s_orc)
     bound = sum(min(budget, int(n) - budget) for n in L["seg_len"] if int(n) > budget)
     assert 0 < moved <= bound
     print(f"{name}: {moved} rows moved of {int(L['seg_len'].sum())} (at most {bound})")
 
 
-def test_inplace_per_segment_budgets_and_degenerate_segments():
+@pytest.mark.parametrize("one_call", [False, True])
+def test_inplace_per_segment_budgets_and_degenerate_segments(one_call):
     w, _ = CASES["llama-ragged"]
     L = make_layer(w, 0)
     D = device_layer(L, w)
@@ -100,7 +111,7 @@ def test_inplace_per_segment_budgets_and_degenerate_segments():
     bud[3] = w.n_prefix + w.n_recent       # only the protected slots survive
     bud[4] = lens[4] - 1                   # one eviction
     budget = torch.tensor(bud, dtype=torch.int32, device="cuda")
-    C, new_len = _run(w, L, D, budget, 0, False)
+    C, new_len = _run(w, L, D, budget, 0, False, one_call)
     _check(w, L, D, C, new_len, bud, s_orc)
 
 
@@ -117,3 +128,29 @@ def test_inplace_rejects_overlaps():
         kv.kv_evict_select_compact_inplace(cache_of(D, w), torch.zeros(D["k"].shape[0], device="cuda"), None, 4, 16,
                                            nl, uniform_budget=19)
     assert ei.value.name == "KVE_EBUDGET"
+
+
+def test_one_call_inplace_rejects_bad_arguments():
+    w, budget = CASES["llama-ragged"]
+    L = make_layer(w, 0)
+    D = device_layer(L, w)
+    cache, obs = cache_of(D, w), obs_of(D, w)
+    nl = torch.full_like(D["seg_len"], -9)
+    bad = D["k"].view(torch.float32).view(-1)[:D["k"].shape[0]]      # scores inside the key rows
+    with pytest.raises(kv.KveError) as ei:
+        kv.kv_evict_score_select_compact_inplace(cache, obs, bad, None, 4, 16, nl, uniform_budget=budget)
+    assert ei.value.name == "KVE_EALIAS"
+    scores = torch.empty(D["k"].shape[0], dtype=torch.float32, device="cuda")
+    with pytest.raises(kv.KveError) as ei:
+        kv.kv_evict_score_select_compact_inplace(cache, obs, scores, None, 4, 16, nl, uniform_budget=19)
+    assert ei.value.name == "KVE_EBUDGET"
+    with pytest.raises(kv.KveError) as ei:
+        kv.kv_evict_score_select_compact_inplace(cache, obs, scores, None, 4, 16, nl, uniform_budget=budget,
+                                                 ws=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert ei.value.name == "KVE_EWORKSPACE"
+    with pytest.raises(kv.KveError) as ei:                            # new_len over the scores
+        kv.kv_evict_score_select_compact_inplace(cache, obs, scores, None, 4, 16, scores[:nl.numel()].view(torch.int32),
+                                                 uniform_budget=budget)
+    assert ei.value.name == "KVE_EALIAS"
+    torch.cuda.synchronize()
+    assert torch.all(nl == -9)                                        # nothing ran
