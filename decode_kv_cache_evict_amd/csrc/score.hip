@@ -852,8 +852,12 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   __syncthreads();
   // Every work-group of the segment has read the segment's length by now (the
   // output length may be the input length array): the segment counts as failed
-  // until its last work-group has moved its rows.
-  if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
+  // until its last work-group has moved its rows.  Both this store and the
+  // final one are device-coherent: the segment's work-groups may run on
+  // different XCDs, whose L2 caches would otherwise write their copies of the
+  // line back in any order at the end of the kernel.
+  if (MODE >= kModeStep && ch == 0 && tid == 0)
+    __hip_atomic_store(&a.out_len[s], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (sh_item < 0) {                       // the segment's work-groups did not meet: it stays failed
     if (MODE < kModeStep)
       for (int j = k0 + tid; j < k1; j += 256) a.scores[off + j] = __builtin_nanf("");

@@ -3,7 +3,8 @@
 // budget goes to the highest scores; "📊 实验": evicted entries are dropped for
 // good).
 //
-// select: one work-group per segment.  The K-th largest candidate score is found
+// select: one work-group per segment (segments longer than the LDS holds: a
+// 1024-thread work-group re-reading the scores).  The K-th largest candidate score is found
 // by an MSB-first radix select over order-preserving 32-bit keys (at most 8-bit
 // digits over LDS histograms, starting below the leading bits that the
 // candidates' minimum and maximum share); ties at the threshold go to the lower
@@ -142,6 +143,120 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
     const int n_keep = n_sure + min(n_eq, max(0, int(kk) - eq_before));
     int keep_tot;
     int at = base + block_scan<kSelBlock>(n_keep, wtot, keep_tot);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      const bool eq = cand && kv[u] == T;
+      const bool keep = j < n && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
+      eq_rank += eq;
+      if (keep) {
+        if (at < K) a.kept[oo + at] = j;
+        ++at;
+      }
+    }
+    base += keep_tot;
+    eq_seen += eq_tot;
+  }
+  if (tid == 0) a.out_len[s] = K;
+}
+
+// Long segments (more keys than the LDS holds): one 1024-thread work-group per
+// segment that re-reads the scores on each radix pass with sixteen loads in
+// flight per thread (a 65,536-key segment is four rounds per pass), and emits
+// the kept slots 8 consecutive slots per thread and round.
+constexpr int kLongBlock = 1024;
+constexpr int kLongUnr = 16;
+
+__global__ __launch_bounds__(kLongBlock) void select_long_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int wtot[kLongBlock / kWave];
+  __shared__ uint32_t mm[2 * (kLongBlock / kWave)];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t oo = a.out_off[s];
+  const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
+  const int64_t io = a.in_off[s];
+  const int n = a.in_len[s];
+  const bool in_ok = n >= 0 && n <= a.in_max && io >= 0 && io + n <= a.in_rows;
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  const int64_t so = a.score_off ? a.score_off[s] : io;
+  const bool sc_ok = so >= 0 && so + n <= a.n_scores;
+  const int keep_n = K >= n ? n : K;
+  const bool bud_ok = K >= n || (K >= P + R && K >= 0);
+  if (!(out_ok && in_ok && sc_ok && bud_ok) || keep_n > a.out_cap) {
+    if (tid == 0) a.out_len[s] = -1;
+    return;
+  }
+  if (K >= n) {
+    for (int j = tid; j < n; j += kLongBlock) a.kept[oo + j] = j;
+    if (tid == 0) a.out_len[s] = n;
+    return;
+  }
+  const float* sc = a.scores + so;
+  const int c0 = P, c1 = n - R;              // candidate slots [c0, c1)
+  // visit the candidates' keys, kLongUnr loads in flight per thread (clamped addresses)
+  auto visit_all = [&](const auto& f) {
+    for (int b0 = c0; b0 < c1; b0 += kLongUnr * kLongBlock) {
+      float raw[kLongUnr];
+#pragma unroll
+      for (int u = 0; u < kLongUnr; ++u) raw[u] = sc[min(b0 + u * kLongBlock + tid, c1 - 1)];
+#pragma unroll
+      for (int u = 0; u < kLongUnr; ++u)
+        if (b0 + u * kLongBlock + tid < c1) f(float_order_key(raw[u]));
+    }
+  };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  visit_all([&](uint32_t key) {
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+  }
+  constexpr int NW = kLongBlock / kWave;
+  if ((tid & 63) == 0) {
+    mm[tid >> 6] = kmin;
+    mm[NW + (tid >> 6)] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    kmin = min(kmin, mm[q]);
+    kmax = max(kmax, mm[NW + q]);
+  }
+  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  uint32_t T, kk;
+  radix_threshold_v<kLongBlock>(visit_all, K - P - R, hist, sh, T, kk, kmin, known);
+  // kept = protected, keys above T, and the first kk candidates equal to T, in
+  // slot order; each thread takes 8 consecutive slots per round
+  int base = 0, eq_seen = 0;
+  for (int r0 = 0; r0 < n; r0 += 8 * kLongBlock) {
+    const int jt = r0 + 8 * tid;
+    float raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = sc[min(jt + u, n - 1)];
+    uint32_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kv[u] = float_order_key(raw[u]);
+    int n_eq = 0, n_sure = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      n_eq += cand && kv[u] == T;
+      n_sure += j < n && (!cand || kv[u] > T);
+    }
+    int eq_tot;
+    const int eq_before = eq_seen + block_scan<kLongBlock>(n_eq, wtot, eq_tot);
+    const int n_keep = n_sure + min(n_eq, max(0, int(kk) - eq_before));
+    int keep_tot;
+    int at = base + block_scan<kLongBlock>(n_keep, wtot, keep_tot);
     int eq_rank = eq_before;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -372,7 +487,10 @@ hipError_t launch_select_inplace(const SelectArgs& a, hipStream_t st) {
 
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st) {
   if (a.n_seg == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(a.n_seg)), dim3(kSelBlock), 0, st, a);
+  if (a.in_max > kSelLdsKeys)
+    hipLaunchKernelGGL(select_long_kernel, dim3(unsigned(a.n_seg)), dim3(kLongBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel, dim3(unsigned(a.n_seg)), dim3(kSelBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.out_cap == 0) return e;
   const int cpr = a.head_dim * a.elem_bytes / 16;

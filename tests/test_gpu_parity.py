@@ -156,6 +156,28 @@ def test_select_ties_signs_and_edges():
             assert np.array_equal(pos[i][:lens[i]], i * n + want)
 
 
+@pytest.mark.parametrize("n", [12289, 40000])
+def test_select_long_segments_ties_and_edges(n):
+    """Segments longer than the selection's LDS key store (12,288) take the
+    1024-thread kernel that re-reads the scores per radix pass: the same kept
+    sets as the oracle, ties and signed values included."""
+    rng = np.random.default_rng(n)
+    cases = [
+        np.full(n, 0.25),
+        rng.integers(0, 5, n).astype(np.float64),
+        rng.standard_normal(n),
+        np.exp(-30 * rng.random(n)),                                # scores over many binades
+    ]
+    for budget in (20, 21, n // 3, n - 1):
+        sc = np.stack(cases)
+        kept, lens, pos = _select_scores(len(cases), n, sc.reshape(-1), budget)
+        for i, s in enumerate(cases):
+            want = oracle.select_kept(s.astype(np.float32).astype(np.float64), n, budget, 4, 16)
+            assert lens[i] == len(want)
+            assert np.array_equal(kept[i][:lens[i]], want), (i, budget)
+            assert np.array_equal(pos[i][:lens[i]], i * n + want)
+
+
 def test_select_rejects_budget_below_protected():
     with pytest.raises(kv.KveError) as ei:
         _select_scores(1, 100, np.zeros(100), 19)
