@@ -573,7 +573,7 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int wtot[4];
-  __shared__ int hole_at[kMfmaChunk], mover_at[kMfmaChunk];
+  __shared__ uint16_t hole_at[kMfmaChunk], mover_at[kMfmaChunk];   // slots < step_max_seg fit in 16 bits
   const int K = a.budget ? a.budget[s] : a.uniform_budget;
   const int P = a.n_prefix, R = a.n_recent;
   if (K >= n) return n;                      // every row stays where it is
@@ -666,16 +666,16 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
   if (cnt > 0) {
     for (int j = s0 + tid; j < s1; j += 256) {
       const uint32_t e = keys[j];
-      if (e >> 31) mover_at[int(e & 0x7fffffffu) - base_k - r_lo] = j;
+      if (e >> 31) mover_at[int(e & 0x7fffffffu) - base_k - r_lo] = uint16_t(j);
     }
     for (int h = tid; h < K; h += 256) {                      // holes: evicted slots below K
       const uint32_t e = keys[h];
       const int rank = h - int(e & 0x7fffffffu);
-      if (!(e >> 31) && rank >= r_lo && rank < r_hi) hole_at[rank - r_lo] = h;
+      if (!(e >> 31) && rank >= r_lo && rank < r_hi) hole_at[rank - r_lo] = uint16_t(h);
     }
   }
   __syncthreads();
-  gather_rows<CPR>([&](int r) { return mover_at[r]; }, [&](int r) { return off + hole_at[r]; }, cnt, a.k, a.v,
+  gather_rows<CPR>([&](int r) { return int(mover_at[r]); }, [&](int r) { return off + hole_at[r]; }, cnt, a.k, a.v,
                    a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid);
   return K;
 }
@@ -899,8 +899,9 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   __syncthreads();
   if (sh_item < 0) return;
   uint32_t* keys = reinterpret_cast<uint32_t*>(&kt[0][0]);
-  const int keep_n = MODE == kModeFill ? step_select_fill<D>(a, s, off, n, k0, k1, keys, tid)
-                                       : step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
+  int keep_n;
+  if constexpr (MODE == kModeFill) keep_n = step_select_fill<D>(a, s, off, n, k0, k1, keys, tid);
+  else keep_n = step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
   if (keep_n < 0) return;
   // every work-group of the segment has gathered its rows: the last one to
   // finish publishes the segment's length (a work-group that gave up at a
