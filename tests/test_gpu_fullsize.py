@@ -84,6 +84,43 @@ def test_qwen3_4b_36_layers_trigger_sampled():
                 assert torch.equal(fbuf[p, :w.fps_keep], st.buf[p, np.sort(P).tolist()])
 
 
+def test_qwen3_4b_36_layers_inplace_trigger_sampled():
+    """The one-call in-place trigger over all 36 layers (the benchmark's
+    --call inplace launch): sampled segments hold exactly the oracle's kept
+    rows in hole-filling order (moved rows byte-exact), the rest untouched."""
+    import bench
+    w = get_workload("qwen3-4b-36l").scaled(triggers=1)
+    st = bench.build_states(w, "cuda")[0]
+    k0, v0, p0 = st.k.clone(), st.v.clone(), st.pos.clone()
+    scores = torch.empty(st.k.shape[0], dtype=torch.float32, device="cuda")
+    new_len = torch.full_like(st.seg_len, -9)
+    cache = kv.make_cache(st.k, st.v, st.pos, st.seg_off, st.seg_len, w.n_kv_heads, st.cap)
+    obs = kv.make_obs(st.q, st.q_pos, st.n_obs, w.rope_theta)
+    kv.kv_evict_score_select_compact_inplace(cache, obs, scores, None, w.n_prefix, w.n_recent, new_len,
+                                             uniform_budget=w.budget)
+    torch.cuda.synchronize()
+    assert torch.all(new_len == w.budget)
+    rng = np.random.default_rng(11)
+    n, K = w.len_hi, w.budget
+    for layer in (0, 20, 35):
+        for b, g in {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}:
+            s_orc, _, _ = _oracle_segment(w, layer, b, g)
+            seg = (layer * w.batch + b) * w.n_kv_heads + g
+            o = seg * n
+            assert_scores_close(scores[o:o + n].cpu().numpy(), s_orc, what=f"layer {layer} request {b} head {g}")
+            src = st.pos[o:o + K].cpu().numpy() - p0[o].item()          # positions are the slots here
+            kept = np.sort(src)
+            ok, _, msg = kept_matches(kept, s_orc, n, K, w.n_prefix, w.n_recent)
+            assert ok, msg
+            assert np.array_equal(src, oracle.hole_fill(kept, n))
+            k_in = k0[o:o + n].view(torch.int16).cpu().numpy()
+            k_now = st.k[o:o + n].view(torch.int16).cpu().numpy()
+            v_in = v0[o:o + n].view(torch.int16).cpu().numpy()
+            v_now = st.v[o:o + n].view(torch.int16).cpu().numpy()
+            assert np.array_equal(k_now[:K], k_in[src]) and np.array_equal(v_now[:K], v_in[src])
+            assert np.array_equal(k_now[K:], k_in[K:]) and np.array_equal(v_now[K:], v_in[K:])
+
+
 def test_long_65k_attention_and_hidden_state_scores_sampled():
     w = get_workload("long-65k")
     L = make_layer(w, 0, device="cuda")
