@@ -1057,11 +1057,23 @@ hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Keys per MFMA work-group: 1024, halved (down to 256) while the launch would
-// have fewer than 2048 work-groups, so that small batches still fill the chip.
+// Keys per MFMA work-group of the two scoring passes: 1024, halved (down to
+// 256) while the launch would have fewer than 2048 work-groups, so that small
+// batches still fill the chip.
 int mfma_chunk(int n_seg, int max_seg_len) {
   int c = kMfmaChunk;
   while (c > 256 && int64_t(n_seg) * ((max_seg_len + c - 1) / c) < 2048) c >>= 1;
+  return c;
+}
+
+// The one-kernel trigger: every work-group of a segment also selects over the
+// whole segment and waits at two barriers, so more, shorter work-groups only
+// pay off while they still fit in one round of resident work-groups (three
+// per CU): 1024 keys, halved (down to 256) while the halved launch still fits.
+int step_chunk(int n_seg, int max_seg_len) {
+  constexpr int64_t kResident = 3 * 256;
+  int c = kMfmaChunk;
+  while (c > 256 && int64_t(n_seg) * ((max_seg_len + c / 2 - 1) / (c / 2)) <= kResident) c >>= 1;
   return c;
 }
 
@@ -1157,7 +1169,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
-  a.chunk = mfma_chunk(a.n_seg, a.max_seg_len);
+  a.chunk = step_chunk(a.n_seg, a.max_seg_len);
   hipError_t e;
   int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;
