@@ -446,13 +446,69 @@ __device__ __forceinline__ int take_ticket(const ScoreArgs& a, int* ctl) {
   return -1;
 }
 
-// One-kernel trigger (kv_evict_score_select_compact): each work-group scores
-// its chunk with the single-read scheme above, stores the chunk's scores with
-// coherent stores and meets the segment's other work-groups at a second arrival
-// counter.  Every work-group of the segment then finds the same protected top-K
-// threshold (radix select over the segment's scores, copied to LDS) and gathers
-// its own chunk's kept rows to their places in the output segment.
-// keys: LDS scratch of step_max_seg(D) words.
+// One-kernel trigger (kv_evict_score_select_compact and its in-place form):
+// each work-group scores its chunk with the single-read scheme above, stores
+// the chunk's scores with coherent stores and counts itself in at a second
+// per-segment arrival counter.  The copying form gathers most of the segment,
+// so every work-group waits there, finds the protected top-K threshold over the
+// segment's scores (copied to LDS) and gathers its own chunk's kept rows.  The
+// in-place form moves at most min(K, n - K) rows, so the last work-group to
+// arrive selects and moves them all and the others are done, which frees
+// their slots for new chunks.  keys: LDS scratch of step_max_seg(D) words.
+
+// The segment's scores into LDS as order keys (eight loads in flight per
+// thread, clamped addresses so that no load waits on a branch), then T, the
+// kc-th largest candidate key, and kk, the number of candidates equal to T
+// that are kept.  hist: 256 words of LDS; sh: 2 words.
+__device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t off, int n, int kc, uint32_t* keys,
+                                                  uint32_t* hist, uint32_t* sh, int tid, uint32_t& T, uint32_t& kk) {
+  const int P = a.n_prefix, R = a.n_recent;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j0 = 0; j0 < n; j0 += 8 * 256) {
+    float raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      raw[u] = __hip_atomic_load(&a.scores[off + min(j0 + u * 256 + tid, n - 1)], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * 256 + tid;
+      if (j < n) {
+        const uint32_t key = float_order_key(raw[u]);
+        keys[j] = key;
+        if (j >= P && j < n - R) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+  }
+  if ((tid & 63) == 0) {
+    hist[tid >> 6] = kmin;
+    hist[4 + (tid >> 6)] = kmax;
+  }
+  __syncthreads();
+  kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
+  kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+  __syncthreads();
+  // every candidate shares the leading bits of its min and max: the radix digits start below them
+  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  radix_threshold_v<256>(
+      [&](const auto& f) {
+        for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
+      },
+      kc, hist, sh, T, kk, kmin, known);
+}
+
+// Copying form: every work-group of the segment finds the threshold and
+// gathers its own chunk's kept rows to their places in the output segment, in
+// ascending slot order (the kept slots and threshold ties before the chunk
+// give its first output row).  Returns keep_n (-1 for a rejected segment).
 template <int D>
 __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
                                                    uint32_t* keys, int tid) {
@@ -467,60 +523,16 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
   const bool bud_ok = K >= n || (K >= P + R && K >= 0);
   const int keep_n = K >= n ? n : K;
-  const bool first = k0 == 0;
-  if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D)) {
-    if (first && tid == 0) a.out_len[s] = -1;
-    return -1;
-  }
+  if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D))
+    return -1;                               // the segment keeps the failure mark stored after the first barrier
   int base = 0, cnt = 0;                     // output row of this chunk's first kept slot; kept count
   if (K >= n) {
     for (int j = k0 + tid; j < k1; j += 256) mine[j - k0] = j;
     base = k0;
     cnt = k1 - k0;
   } else {
-    // the segment's scores into LDS, eight loads in flight per thread (clamped
-    // addresses, so no load waits on a branch), with the candidates' min and max
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int j0 = 0; j0 < n; j0 += 8 * 256) {
-      float raw[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        raw[u] = __hip_atomic_load(&a.scores[off + min(j0 + u * 256 + tid, n - 1)], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u * 256 + tid;
-        if (j < n) {
-          const uint32_t key = float_order_key(raw[u]);
-          keys[j] = key;
-          if (j >= P && j < n - R) {
-            kmin = min(kmin, key);
-            kmax = max(kmax, key);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-      kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-    }
-    if ((tid & 63) == 0) {
-      hist[tid >> 6] = kmin;
-      hist[4 + (tid >> 6)] = kmax;
-    }
-    __syncthreads();
-    kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
-    kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
-    __syncthreads();
-    // every candidate shares the leading bits of its min and max: the radix digits start below them
-    const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
     uint32_t T, kk;
-    radix_threshold_v<256>(
-        [&](const auto& f) {
-          for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
-        },
-        K - P - R, hist, sh, T, kk, kmin, known);
+    segment_threshold(a, off, n, K - P - R, keys, hist, sh, tid, T, kk);
     // kept slots and threshold ties before this chunk
     int eq_b = 0, gt_b = 0;
     for (int j = P + tid; j < min(k0, n - R); j += 256) {
@@ -556,72 +568,32 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   return keep_n;
 }
 
-// In-place form of the one-kernel trigger (kv_evict_score_select_compact_inplace):
-// the same threshold over the segment's scores in LDS, then hole filling
-// within the cache: the survivors in [K, n), in ascending slot order, move
-// into the evicted slots of [0, K), in ascending slot order.  One pass over
-// the slots (8 consecutive per thread and round, two block scans) replaces
-// each key in LDS by (kept << 31) | (kept slots before it); a mover's rank is
-// then its kept-before count minus that of slot K, and a hole's rank its slot
-// minus its kept-before count, so this work-group finds the holes that pair
-// with the movers of its own chunk by a plain sweep and copies them.
-// Returns the segment's new length (-1 for a rejected segment).
+// In-place form (kv_evict_score_select_compact_inplace): the same threshold,
+// then hole filling within the cache: the survivors in [K, n), in ascending
+// slot order, move into the evicted slots of [0, K), in ascending slot order.
+// One pass over the slots (8 consecutive per thread and round, two block
+// scans) replaces each key in LDS by (kept << 31) | (kept slots before it); a
+// mover's rank is then its kept-before count minus that of slot K, and a
+// hole's rank its slot minus its kept-before count, so each piece of at most
+// 1024 slots of [K, n) finds the holes that pair with its movers by a plain
+// sweep.  Sources lie in [K, n) and destinations in [0, K), so no row is
+// overwritten before it is read.  Returns the segment's new length (-1 for a
+// rejected segment).
 template <int D>
-__device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
-                                                uint32_t* keys, int tid) {
+__device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64_t off, int n, uint32_t* keys,
+                                                int tid) {
   constexpr int CPR = D / 8;
+  constexpr int kPiece = 1024;
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int wtot[4];
-  __shared__ uint16_t hole_at[kMfmaChunk], mover_at[kMfmaChunk];   // slots < step_max_seg fit in 16 bits
+  __shared__ uint16_t hole_at[kPiece], mover_at[kPiece];   // slots < step_max_seg fit in 16 bits
   const int K = a.budget ? a.budget[s] : a.uniform_budget;
   const int P = a.n_prefix, R = a.n_recent;
   if (K >= n) return n;                      // every row stays where it is
-  if (K < P + R || K < 0) {
-    if (k0 == 0 && tid == 0) a.out_len[s] = -1;
-    return -1;
-  }
-  // the segment's scores into LDS with the candidates' min and max (as in the copying form)
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int j0 = 0; j0 < n; j0 += 8 * 256) {
-    float raw[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      raw[u] = __hip_atomic_load(&a.scores[off + min(j0 + u * 256 + tid, n - 1)], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u * 256 + tid;
-      if (j < n) {
-        const uint32_t key = float_order_key(raw[u]);
-        keys[j] = key;
-        if (j >= P && j < n - R) {
-          kmin = min(kmin, key);
-          kmax = max(kmax, key);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-  }
-  if ((tid & 63) == 0) {
-    hist[tid >> 6] = kmin;
-    hist[4 + (tid >> 6)] = kmax;
-  }
-  __syncthreads();
-  kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
-  kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
-  __syncthreads();
-  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  if (K < P + R || K < 0 || n > step_max_seg(D)) return -1;
   uint32_t T, kk;
-  radix_threshold_v<256>(
-      [&](const auto& f) {
-        for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
-      },
-      K - P - R, hist, sh, T, kk, kmin, known);
+  segment_threshold(a, off, n, K - P - R, keys, hist, sh, tid, T, kk);
   // keys -> (kept << 31) | kept slots before
   int kept_seen = 0, eq_seen = 0;
   for (int j0 = 0; j0 < n; j0 += 8 * 256) {
@@ -657,26 +629,27 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
     eq_seen += eq_tot;
     __syncthreads();
   }
-  // this chunk's movers: kept slots in [max(k0, K), k1); their ranks among all movers
   const int base_k = int(keys[K] & 0x7fffffffu);           // kept slots before K (K < n)
-  const int s0 = max(k0, K), s1 = max(k1, K);
-  const int r_lo = (s0 < n ? int(keys[s0] & 0x7fffffffu) : K) - base_k;
-  const int r_hi = (s1 < n ? int(keys[s1] & 0x7fffffffu) : K) - base_k;
-  const int cnt = r_hi - r_lo;
-  if (cnt > 0) {
-    for (int j = s0 + tid; j < s1; j += 256) {
+  for (int p0 = K; p0 < n; p0 += kPiece) {
+    const int p1 = min(n, p0 + kPiece);
+    const int r_lo = int(keys[p0] & 0x7fffffffu) - base_k;  // ranks of this piece's movers among all movers
+    const int r_hi = (p1 < n ? int(keys[p1] & 0x7fffffffu) : K) - base_k;
+    const int cnt = r_hi - r_lo;
+    if (cnt <= 0) continue;                                // the same decision in every thread
+    for (int j = p0 + tid; j < p1; j += 256) {
       const uint32_t e = keys[j];
       if (e >> 31) mover_at[int(e & 0x7fffffffu) - base_k - r_lo] = uint16_t(j);
     }
-    for (int h = tid; h < K; h += 256) {                      // holes: evicted slots below K
+    for (int h = tid; h < K; h += 256) {                   // holes: evicted slots below K
       const uint32_t e = keys[h];
       const int rank = h - int(e & 0x7fffffffu);
       if (!(e >> 31) && rank >= r_lo && rank < r_hi) hole_at[rank - r_lo] = uint16_t(h);
     }
+    __syncthreads();
+    gather_rows<CPR>([&](int r) { return int(mover_at[r]); }, [&](int r) { return off + hole_at[r]; }, cnt, a.k,
+                     a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid);
+    __syncthreads();                         // the next piece rebuilds the lists
   }
-  __syncthreads();
-  gather_rows<CPR>([&](int r) { return int(mover_at[r]); }, [&](int r) { return off + hole_at[r]; }, cnt, a.k, a.v,
-                   a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid);
   return K;
 }
 
@@ -892,24 +865,38 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   sweep(std::integral_constant<bool, true>{});
   if (MODE < kModeStep) return;
 
-  // second segment barrier: every chunk's scores are stored
+  // Every chunk's scores are stored (acknowledged before the arrival count).
+  // A work-group that gave up at the first barrier never arrives, so a failed
+  // segment is never selected and keeps -1.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
-  __syncthreads();
-  if (sh_item < 0) return;
   uint32_t* keys = reinterpret_cast<uint32_t*>(&kt[0][0]);
   int keep_n;
-  if constexpr (MODE == kModeFill) keep_n = step_select_fill<D>(a, s, off, n, k0, k1, keys, tid);
-  else keep_n = step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
-  if (keep_n < 0) return;
-  // every work-group of the segment has gathered its rows: the last one to
-  // finish publishes the segment's length (a work-group that gave up at a
-  // barrier never counts in, so a failed segment keeps -1)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
-    __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (MODE == kModeFill) {
+    // in place: the last work-group to arrive selects and moves the segment's
+    // few survivors past K; the others are done
+    if (tid == 0) sh_item = atomicAdd(ctl + kQueues + a.n_seg + s, 1) == nch - 1 ? 0 : -1;
+    __syncthreads();
+    if (sh_item < 0) return;
+    keep_n = step_select_fill<D>(a, s, off, n, keys, tid);
+    if (keep_n < 0) return;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // copying: the kept rows are most of the segment, so every work-group
+    // waits for the others, selects and gathers its own chunk's kept rows
+    if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
+    __syncthreads();
+    if (sh_item < 0) return;
+    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
+    if (keep_n < 0) return;
+    // the last work-group to finish its gather publishes the segment's length
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
+      __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Pass 1 and the single-read kernel carry the row statistics in registers; all
