@@ -1064,6 +1064,20 @@ int step_chunk(int n_seg, int max_seg_len) {
   return c;
 }
 
+// The in-place trigger: only the segment's last work-group selects, so a
+// whole segment per work-group (no barrier waits, no exchange of row
+// statistics) is best while the launch still fills the chip: the smallest
+// power of two covering the longest segment (at most 8192), halved (down to
+// 256) while the halved launch still fits in one round of resident
+// work-groups.
+int fill_chunk(int n_seg, int max_seg_len) {
+  constexpr int64_t kResident = 3 * 256;
+  int c = 256;
+  while (c < 8192 && c < max_seg_len) c <<= 1;
+  while (c > 256 && int64_t(n_seg) * ((max_seg_len + c / 2 - 1) / (c / 2)) <= kResident) c >>= 1;
+  return c;
+}
+
 }  // namespace
 
 size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
@@ -1156,7 +1170,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
-  a.chunk = step_chunk(a.n_seg, a.max_seg_len);
+  a.chunk = a.inplace ? fill_chunk(a.n_seg, a.max_seg_len) : step_chunk(a.n_seg, a.max_seg_len);
   hipError_t e;
   int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;
