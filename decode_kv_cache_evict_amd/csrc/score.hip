@@ -394,11 +394,17 @@ __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float 
 // Work assignment in that mode: eight ticket queues, queue q holding the chunks
 // of the segments s = q (mod 8).  A work-group takes a ticket from the queue of
 // the XCD it runs on (a segment's chunks then share one L2) and steals from the
-// other queues when its own is empty.  Deadlock-free: a ticket is only taken by
-// a running work-group, so every chunk of a segment but those of the newest
-// segment in a queue is held by a running or finished work-group, and missing
-// chunks are taken as soon as any older work-group finishes.  The wait is
-// bounded (ScoreArgs::spin_limit polls).
+// other queues when its own is empty.  A ticket is only taken by a running
+// work-group and each queue hands its tickets out in order, so only the newest
+// segment of each queue can miss chunks: at most 8 (nch - 1) work-groups wait
+// on work-groups not yet started.  Work-groups start in launch order, spread
+// round-robin over the XCDs, and a later one waits while the XCD of the next
+// has no free slot; with at most 12 chunks per segment the waiting
+// work-groups (at most 88) cannot fill the 96 slots of an XCD (32 CUs, three
+// work-groups each), so a full XCD always holds a work-group that will finish,
+// and the launches keep to that (or to one round of resident work-groups).
+// The wait is bounded all the same (ScoreArgs::spin_limit polls).
+constexpr int kMaxWaitChunks = 12;
 constexpr int kQueues = 8;
 constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3, kModeFill = 4;
 
@@ -1053,11 +1059,20 @@ int mfma_chunk(int n_seg, int max_seg_len) {
   return c;
 }
 
+// The single-read scoring kernel: the two-pass chunk, lengthened (in 64-key
+// steps) where a segment would otherwise span more than kMaxWaitChunks chunks.
+int fused_chunk(int n_seg, int max_seg_len) {
+  const int c = mfma_chunk(n_seg, max_seg_len);
+  const int lo = (max_seg_len + kMaxWaitChunks - 1) / kMaxWaitChunks;
+  return c >= lo ? c : (lo + kBK - 1) / kBK * kBK;
+}
+
 // The one-kernel trigger: every work-group of a segment also selects over the
 // whole segment and waits at two barriers, so more, shorter work-groups only
 // pay off while they still fit in one round of resident work-groups (three
 // per CU): 1024 keys, halved (down to 256) while the halved launch still fits.
 int step_chunk(int n_seg, int max_seg_len) {
+  static_assert((step_max_seg(128) + kMfmaChunk - 1) / kMfmaChunk <= kMaxWaitChunks, "segment spans too many chunks");
   constexpr int64_t kResident = 3 * 256;
   int c = kMfmaChunk;
   while (c > 256 && int64_t(n_seg) * ((max_seg_len + c / 2 - 1) / (c / 2)) <= kResident) c >>= 1;
@@ -1146,7 +1161,7 @@ hipError_t launch_step(const ScoreArgs& a, int* ctl, hipStream_t st) {
 hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const bool mfma = a.dtype == 0 && a.impl == 0;
   const bool fused = a.dtype == 0 && a.impl == 2;
-  a.chunk = (fused || mfma) ? mfma_chunk(a.n_seg, a.max_seg_len) : kScoreChunk;
+  a.chunk = fused ? fused_chunk(a.n_seg, a.max_seg_len) : mfma ? mfma_chunk(a.n_seg, a.max_seg_len) : kScoreChunk;
   hipError_t e;
   int* ctl = prepare(a, ws, st, e);
   if (e != hipSuccess) return e;

@@ -76,6 +76,27 @@ def test_scores_match_oracle(name, impl, monkeypatch):
         assert abs(e[s] - want) <= 2e-3 * max(abs(want), 1e-3), (s, e[s], want)
 
 
+def test_single_read_scoring_long_segments(monkeypatch):
+    """The single-read scoring kernel on segments of 32,768 keys: its
+    work-groups meet at a per-segment barrier, so each segment is cut into at
+    most 12 chunks (with the two-pass chunk it would span 128, enough waiting
+    work-groups to fill an XCD while the next work-group in launch order waits
+    for a slot there).  Every segment completes (no failure marks) and matches
+    the oracle."""
+    w = get_workload("long-65k").scaled(batch=1, len_lo=32768, len_hi=32768)
+    L = make_layer(w, 0)
+    D = device_layer(L, w)
+    k_orc = oracle_cache_keys(L, w)
+    s_orc = oracle_layer_scores(L, w, k_orc)
+    monkeypatch.setenv("KVE_SCORE_IMPL", "fused")
+    scores, _ = score_layer(D, w, entropy=False)
+    torch.cuda.synchronize()
+    g = scores.cpu().numpy()
+    assert np.isfinite(g).all(), f"{int((~np.isfinite(g)).sum())} scores not finite"
+    worst = assert_scores_close(g, s_orc)
+    print(f"long-32k/fused: worst relative score error {worst:.2e}")
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_select_compact_match_oracle(name):
     w, L, D, k_orc, s_orc = _case(name)
