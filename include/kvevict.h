@@ -243,9 +243,9 @@ size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const
  * argument (hole filling: the survivors in [K, n), in ascending slot order,
  * move into the evicted slots of [0, K), in ascending slot order).  For bf16
  * caches whose max_seg_len fits the on-chip selection (8704 rows at head_dim
- * 128, 4608 at 64) it runs as one kernel (each segment's work-groups score
- * their chunk, wait for the segment's other chunks, select, and move the
- * survivors of their own chunk); otherwise it makes the two calls.  The kept
+ * 128, 4608 at 64) it runs as one kernel (a segment's work-groups score their
+ * chunks, usually the whole segment in one; the last of them to finish selects
+ * and moves the segment's survivors); otherwise it makes the two calls.  The kept
  * sets may differ from the two-call form's only where scores tie to fp32
  * rounding (the softmax normaliser is summed in another order).  new_len may
  * be c->seg_len itself; a segment whose work-groups could not meet within the
