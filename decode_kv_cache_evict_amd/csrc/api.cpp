@@ -220,8 +220,11 @@ kve_status kv_evict_wave_budgets(int32_t n_layers, double center, double sigma, 
 }
 
 size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx) {
-  if (!out || have_kept_idx || out->n_rows < 0) return 0;
-  return size_t(out->n_rows) * sizeof(int32_t);
+  if (!out || out->n_rows < 0 || out->n_seg < 0) return 0;
+  // the kept-index list (when the caller passes none), then the control ints
+  // of the several-work-groups-per-segment selection of few long segments
+  const size_t kept = have_kept_idx ? 0 : round256(size_t(out->n_rows) * sizeof(int32_t));
+  return kept + kve::split_ctl_ints(out->n_seg) * sizeof(int32_t);
 }
 
 kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, const int64_t* score_off,
@@ -246,6 +249,13 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   const size_t need = kept_idx ? 0 : size_t(out->n_rows) * sizeof(int32_t);
   if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   int32_t* kept = kept_idx ? kept_idx : static_cast<int32_t*>(ws);
+  // control ints of the split selection when the workspace holds them (a
+  // smaller workspace only costs the one-work-group-per-segment form)
+  const size_t ctl_at = kept_idx ? 0 : round256(need);
+  const size_t ctl_b = kve::split_ctl_ints(in->n_seg) * sizeof(int32_t);
+  int32_t* ctl = ws && ctl_b > 0 && ws_bytes >= ctl_at + ctl_b && (reinterpret_cast<uintptr_t>(ws) & 3u) == 0
+                     ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ctl_at)
+                     : nullptr;
   const size_t ib = rows_bytes(in), ob = rows_bytes(out);
   const size_t ipb = size_t(in->n_rows) * 4, opb = size_t(out->n_rows) * 4;
   const size_t kb = size_t(out->n_rows) * 4;
@@ -253,12 +263,12 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   const void* ins[] = {in->k, in->v, in->pos, scores, in->seg_off, in->seg_len, budget, score_off};
   const size_t insz[] = {ib, ib, ipb, sb, size_t(in->n_seg) * 8, size_t(in->n_seg) * 4,
                          budget ? size_t(in->n_seg) * 4 : 0, score_off ? size_t(in->n_seg) * 8 : 0};
-  const void* outs[] = {out->k, out->v, out->pos, out->seg_len, kept};
-  const size_t outsz[] = {ob, ob, opb, size_t(out->n_seg) * 4, kb};
-  for (int i = 0; i < 5; ++i) {
+  const void* outs[] = {out->k, out->v, out->pos, out->seg_len, kept, ctl};
+  const size_t outsz[] = {ob, ob, opb, size_t(out->n_seg) * 4, kb, ctl ? ctl_b : 0};
+  for (int i = 0; i < 6; ++i) {
     for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
-    for (int j = i + 1; j < 5; ++j)
+    for (int j = i + 1; j < 6; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
   }
   if (in->n_seg == 0) return KVE_OK;
@@ -288,6 +298,8 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   a.n_seg = in->n_seg;
   a.head_dim = in->head_dim;
   a.elem_bytes = int32_t(elem_bytes(in->dtype));
+  a.split_ctl = ctl;
+  a.spin_limit = spin_limit();
   return device_status(kve::launch_select_compact(a, static_cast<hipStream_t>(stream)), "kv_evict_select_compact");
 }
 
@@ -402,8 +414,9 @@ kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, 
   if (in->n_seg == 0) return KVE_OK;
   if (!fused) {
     if ((st = kv_evict_score(in, o, scores, nullptr, ws, sw, stream)) != KVE_OK) return st;
+    // the scoring workspace is free again (stream order): the selection's control ints
     return kv_evict_select_compact(in, scores, nullptr, in->n_rows, budget, uniform_budget, n_prefix, n_recent, kept,
-                                   out, nullptr, 0, stream);
+                                   out, ws, sw, stream);
   }
   kve::ScoreArgs a = score_args(in, o, rows, scores);
   a.v = in->v;

@@ -68,7 +68,12 @@ struct SelectArgs {
   const int64_t* out_off; int32_t* out_len; int64_t out_rows; int32_t out_cap;
   int32_t* kept;          // [out_rows]
   int32_t n_seg, head_dim, elem_bytes;
+  int32_t* split_ctl;     // split_ctl_ints(n_seg) ints of workspace, or null (long segments, one work-group each)
+  int32_t spin_limit;     // polls at a segment barrier before giving up
 };
+// Control ints the selection of few long segments over several work-groups
+// per segment needs (0: that form is not used for n_seg segments).
+size_t split_ctl_ints(int32_t n_seg);
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st);
 // In place: k_out/v_out/pos_out are the input cache; out_len receives the new lengths.
 hipError_t launch_select_inplace(const SelectArgs& a, hipStream_t st);

@@ -276,6 +276,226 @@ __global__ __launch_bounds__(kLongBlock) void select_long_kernel(SelectArgs a) {
   if (tid == 0) a.out_len[s] = K;
 }
 
+// Few long segments (the 65k workload has 32): one work-group per segment
+// would leave most CUs idle, so G work-groups share each segment, each
+// holding 1/G of its candidates.  Every digit pass's histogram is summed over
+// the segment's work-groups in a per-segment control block with device-scope
+// atomics, and the work-groups meet at a per-segment arrival counter after
+// each sum (bounded polling).  Work-groups take their (segment, slice) from
+// one ticket counter in launch order, so a waiting work-group only ever waits
+// for slices of its own segment, all of them taken by running work-groups but
+// at most G - 1 of the newest segment; on an idle device the whole launch (at
+// most kSplitMaxWg work-groups, one per CU) is resident at once.  A last exchange of each work-group's
+// kept and tied counts gives every work-group the kept rows before its slice
+// of slots, which it then lists like the one-work-group form.  The segment's
+// length is published by its last work-group to finish, so a segment whose
+// work-groups did not all meet keeps -1.
+// Control block of a segment (kSplitCtl ints): [0] arrivals, [1] finished
+// work-groups, [2] / [3] the candidates' smallest / largest key, [8 + 2g] /
+// [9 + 2g] work-group g's kept-for-sure / tied slot counts, [64 + 256p + d]
+// the pass-p histogram.  One more int after the last block: the ticket counter.
+constexpr int kSplitMaxWg = 256;
+constexpr int kSplitMaxG = 16;
+constexpr int kSplitHist = 64;
+constexpr int kSplitCtl = kSplitHist + 4 * 256;
+
+__device__ __forceinline__ int load_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 only: count this work-group in and poll until `target` arrivals,
+// for at most `limit` polls; on a timeout push the counter far below any
+// target, so that no work-group of the segment passes a later meeting.
+__device__ __forceinline__ bool split_meet(int* arrive, int target, int limit) {
+  atomicAdd(arrive, 1);
+  int spins = 0;
+  while (load_agent(arrive) < target && ++spins < limit) __builtin_amdgcn_s_sleep(1);
+  if (spins < limit) return true;
+  atomicAdd(arrive, -(1 << 24));
+  return false;
+}
+
+__global__ void split_ctl_init_kernel(int* ctl, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) ctl[i] = i % kSplitCtl == 2 ? -1 : 0;    // [2] holds a minimum: all bits set
+}
+
+__global__ __launch_bounds__(kLongBlock) void select_split_kernel(SelectArgs a, int G) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int wtot[kLongBlock / kWave];
+  __shared__ uint32_t mm[2 * (kLongBlock / kWave)];
+  __shared__ int met;
+  const int tid = threadIdx.x;
+  if (tid == 0) met = atomicAdd(&a.split_ctl[int64_t(a.n_seg) * kSplitCtl], 1);
+  __syncthreads();
+  const int item = met;
+  __syncthreads();
+  const int s = item / G, g = item % G;
+  int* ctl = a.split_ctl + int64_t(s) * kSplitCtl;
+  const int64_t oo = a.out_off[s];
+  const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
+  const int64_t io = a.in_off[s];
+  const int n = a.in_len[s];
+  const bool in_ok = n >= 0 && n <= a.in_max && io >= 0 && io + n <= a.in_rows;
+  const int K = a.budget ? a.budget[s] : a.uniform_budget;
+  const int P = a.n_prefix, R = a.n_recent;
+  const int64_t so = a.score_off ? a.score_off[s] : io;
+  const bool sc_ok = so >= 0 && so + n <= a.n_scores;
+  const int keep_n = K >= n ? n : K;
+  const bool bud_ok = K >= n || (K >= P + R && K >= 0);
+  // every work-group of the segment takes the same branch below
+  if (!(out_ok && in_ok && sc_ok && bud_ok) || keep_n > a.out_cap) {
+    if (g == 0 && tid == 0) __hip_atomic_store(&a.out_len[s], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int ls = (n + G - 1) / G;                      // this work-group's slots [s0, s1)
+  const int s0 = min(n, g * ls), s1 = min(n, s0 + ls);
+  if (K >= n) {
+    for (int j = s0 + tid; j < s1; j += kLongBlock) a.kept[oo + j] = j;
+    if (g == 0 && tid == 0) __hip_atomic_store(&a.out_len[s], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (g == 0 && tid == 0) __hip_atomic_store(&a.out_len[s], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float* sc = a.scores + so;
+  const int c0 = P, c1 = n - R;                      // candidate slots; this work-group's [b0, b1)
+  const int lc = (c1 - c0 + G - 1) / G;
+  const int b0 = min(c1, c0 + g * lc), b1 = min(c1, b0 + lc);
+  auto visit = [&](const auto& f) {
+    for (int j0 = b0; j0 < b1; j0 += kLongUnr * kLongBlock) {
+      float raw[kLongUnr];
+#pragma unroll
+      for (int u = 0; u < kLongUnr; ++u) raw[u] = sc[min(j0 + u * kLongBlock + tid, b1 - 1)];
+#pragma unroll
+      for (int u = 0; u < kLongUnr; ++u)
+        if (j0 + u * kLongBlock + tid < b1) f(float_order_key(raw[u]));
+    }
+  };
+  int meetings = 0;
+  // every thread; true when all G work-groups are in.  The device-scope
+  // atomics and coherent stores before it are acknowledged first (a fence
+  // would also write back and invalidate the whole L2).
+  auto meet = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    ++meetings;
+    if (tid == 0) met = split_meet(&ctl[0], meetings * G, a.spin_limit);
+    __syncthreads();
+    return met != 0;
+  };
+  // the candidates' key range over the whole segment
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  visit([&](uint32_t key) {
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
+  }
+  constexpr int NW = kLongBlock / kWave;
+  if ((tid & 63) == 0) {
+    mm[tid >> 6] = kmin;
+    mm[NW + (tid >> 6)] = kmax;
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      kmin = min(kmin, mm[q]);
+      kmax = max(kmax, mm[NW + q]);
+    }
+    atomicMin(reinterpret_cast<unsigned*>(&ctl[2]), kmin);
+    atomicMax(reinterpret_cast<unsigned*>(&ctl[3]), kmax);
+  }
+  if (!meet()) return;
+  kmin = uint32_t(load_agent(&ctl[2]));
+  kmax = uint32_t(load_agent(&ctl[3]));
+  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  int pass = 0;
+  auto merge = [&](uint32_t* h) {
+    int* gh = &ctl[kSplitHist + 256 * pass++];
+    if (tid < 256 && h[tid] != 0) atomicAdd(&gh[tid], int(h[tid]));
+    if (!meet()) return false;
+    if (tid < 256) h[tid] = uint32_t(load_agent(&gh[tid]));
+    __syncthreads();
+    return true;
+  };
+  uint32_t T, kk;
+  if (!radix_threshold_v<kLongBlock>(visit, K - P - R, hist, sh, T, kk, kmin, known, merge)) return;
+  // this work-group's slots kept for sure (protected, or above T) and tied at T
+  int n_sure = 0, n_eq = 0;
+  for (int j0 = s0; j0 < s1; j0 += kLongUnr * kLongBlock) {
+    float raw[kLongUnr];
+#pragma unroll
+    for (int u = 0; u < kLongUnr; ++u) raw[u] = sc[min(j0 + u * kLongBlock + tid, s1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kLongUnr; ++u) {
+      const int j = j0 + u * kLongBlock + tid;
+      const bool cand = j >= c0 && j < c1;
+      const uint32_t key = float_order_key(raw[u]);
+      n_sure += j < s1 && (!cand || key > T);
+      n_eq += j < s1 && cand && key == T;
+    }
+  }
+  n_sure = block_sum<kLongBlock>(n_sure, wtot);
+  n_eq = block_sum<kLongBlock>(n_eq, wtot);
+  if (tid == 0) {
+    __hip_atomic_store(&ctl[8 + 2 * g], n_sure, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctl[9 + 2 * g], n_eq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!meet()) return;
+  int base = 0, eq_seen = 0;                         // kept and tied slots before this work-group's
+  for (int q = 0; q < g; ++q) {
+    const int eq_q = load_agent(&ctl[9 + 2 * q]);
+    base += load_agent(&ctl[8 + 2 * q]) + min(eq_q, max(0, int(kk) - eq_seen));
+    eq_seen += eq_q;
+  }
+  // list this work-group's kept slots, 8 consecutive per thread and round
+  for (int r0 = s0; r0 < s1; r0 += 8 * kLongBlock) {
+    const int jt = r0 + 8 * tid;
+    float raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = sc[min(jt + u, s1 - 1)];
+    uint32_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kv[u] = float_order_key(raw[u]);
+    int r_eq = 0, r_sure = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      r_eq += j < s1 && cand && kv[u] == T;
+      r_sure += j < s1 && (!cand || kv[u] > T);
+    }
+    int eq_tot;
+    const int eq_before = eq_seen + block_scan<kLongBlock>(r_eq, wtot, eq_tot);
+    const int r_keep = r_sure + min(r_eq, max(0, int(kk) - eq_before));
+    int keep_tot;
+    int at = base + block_scan<kLongBlock>(r_keep, wtot, keep_tot);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jt + u;
+      const bool cand = j >= c0 && j < c1;
+      const bool eq = j < s1 && cand && kv[u] == T;
+      const bool keep = j < s1 && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
+      eq_rank += eq;
+      if (keep) {
+        if (at < K) a.kept[oo + at] = j;
+        ++at;
+      }
+    }
+    base += keep_tot;
+    eq_seen += eq_tot;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0 && atomicAdd(&ctl[1], 1) == G - 1)
+    __hip_atomic_store(&a.out_len[s], K, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Gather kept rows.  CPR 16-byte chunks per row; each thread moves UNR rows of
 // K and V per pass (all loads issued before the stores), a tile is PASSES
 // passes, and a work-group takes every gridDim.x-th tile of its segment.  Loads
@@ -485,9 +705,18 @@ hipError_t launch_select_inplace(const SelectArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+size_t split_ctl_ints(int32_t n_seg) {
+  return n_seg > 0 && 2 * n_seg <= kSplitMaxWg ? size_t(n_seg) * kSplitCtl + 1 : 0;
+}
+
 hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st) {
   if (a.n_seg == 0) return hipSuccess;
-  if (a.in_max > kSelLdsKeys)
+  const int G = min(kSplitMaxG, kSplitMaxWg / a.n_seg);
+  if (a.in_max > kSelLdsKeys && a.split_ctl && G >= 2) {
+    const int64_t nc = int64_t(a.n_seg) * kSplitCtl + 1;
+    hipLaunchKernelGGL(split_ctl_init_kernel, dim3(unsigned((nc + 255) / 256)), dim3(256), 0, st, a.split_ctl, nc);
+    hipLaunchKernelGGL(select_split_kernel, dim3(unsigned(a.n_seg * G)), dim3(kLongBlock), 0, st, a, G);
+  } else if (a.in_max > kSelLdsKeys)
     hipLaunchKernelGGL(select_long_kernel, dim3(unsigned(a.n_seg)), dim3(kLongBlock), 0, st, a);
   else
     hipLaunchKernelGGL(select_kernel, dim3(unsigned(a.n_seg)), dim3(kSelBlock), 0, st, a);

@@ -144,11 +144,18 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& ds
 // pass the number of leading bits `known` (0..32) that every candidate shares
 // with `prefix` (e.g. the common prefix of the candidates' minimum and
 // maximum); the digits then start below them.  kc == 0 gives T = 0xFFFFFFFF,
-// kk = 0.  hist: 256 uints of LDS; sh: 2 uints of LDS.
-template <int BLOCK, typename Visit>
-__device__ __forceinline__ void radix_threshold_v(const Visit& visit, int kc, uint32_t* hist, uint32_t* sh,
+// kk = 0.  hist: 256 uints of LDS; sh: 2 uints of LDS.  When the candidates
+// are spread over several work-groups, merge(hist) replaces each digit pass's
+// local histogram by the sum over all of them (every work-group then takes the
+// same digits) and returns false if they could not meet, which ends the
+// selection with false.
+struct LocalHist {
+  __device__ bool operator()(uint32_t*) const { return true; }
+};
+template <int BLOCK, typename Visit, typename Merge = LocalHist>
+__device__ __forceinline__ bool radix_threshold_v(const Visit& visit, int kc, uint32_t* hist, uint32_t* sh,
                                                   uint32_t& T, uint32_t& kk_out, uint32_t prefix = 0,
-                                                  int known = 0) {
+                                                  int known = 0, const Merge& merge = Merge()) {
   const int tid = threadIdx.x;
   uint32_t mask = known == 0 ? 0u : ~0u << (32 - known);
   prefix &= mask;
@@ -156,7 +163,7 @@ __device__ __forceinline__ void radix_threshold_v(const Visit& visit, int kc, ui
   if (kc == 0) {
     T = 0xFFFFFFFFu;
     kk_out = 0;
-    return;
+    return true;
   }
   for (int hi = 32 - known; hi > 0;) {
     const int shift = hi > 8 ? hi - 8 : 0;
@@ -167,6 +174,7 @@ __device__ __forceinline__ void radix_threshold_v(const Visit& visit, int kc, ui
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & wmask], 1u);
     });
     __syncthreads();
+    if (!merge(hist)) return false;
     if (tid < 64) {
       // lane l owns digits 255-4l .. 252-4l (descending)
       uint32_t h[4], loc = 0;
@@ -210,6 +218,7 @@ __device__ __forceinline__ void radix_threshold_v(const Visit& visit, int kc, ui
   }
   T = prefix;
   kk_out = kk;
+  return true;
 }
 
 // Protected form over one segment: candidates are the slots j in [P, n-R),

@@ -134,8 +134,9 @@ def test_select_compact_match_oracle(name):
     print(f"{name}: {swaps} tie-band swaps")
 
 
-def _select_scores(n_seg, n, scores_np, budget, P=4, R=16):
-    """Run select/compact on given per-row scores over a synthetic bf16 cache."""
+def _select_scores(n_seg, n, scores_np, budget, P=4, R=16, ws=None):
+    """Run select/compact on given per-row scores over a synthetic bf16 cache
+    (ws None: the workspace the library asks for)."""
     dev = "cuda"
     rows = n_seg * n
     k = torch.arange(rows * 128, dtype=torch.float32, device=dev).view(rows, 128).to(torch.bfloat16)
@@ -152,7 +153,7 @@ def _select_scores(n_seg, n, scores_np, budget, P=4, R=16):
     kept = torch.zeros(n_seg * cap, dtype=torch.int32, device=dev)
     cout = kv.make_cache(ok_, ov_, op, oo, ol, 1, cap)
     sc = torch.from_numpy(np.asarray(scores_np, dtype=np.float32)).to(dev)
-    kv.kv_evict_select_compact(cin, sc, None, P, R, cout, kept_idx=kept, uniform_budget=budget)
+    kv.kv_evict_select_compact(cin, sc, None, P, R, cout, kept_idx=kept, uniform_budget=budget, ws=ws)
     torch.cuda.synchronize()
     return kept.cpu().numpy().reshape(n_seg, cap), ol.cpu().numpy(), op.cpu().numpy().reshape(n_seg, cap)
 
@@ -177,11 +178,16 @@ def test_select_ties_signs_and_edges():
             assert np.array_equal(pos[i][:lens[i]], i * n + want)
 
 
+@pytest.mark.parametrize("form", ["split", "one"])
 @pytest.mark.parametrize("n", [12289, 40000])
-def test_select_long_segments_ties_and_edges(n):
+def test_select_long_segments_ties_and_edges(n, form):
     """Segments longer than the selection's LDS key store (12,288) take the
-    1024-thread kernel that re-reads the scores per radix pass: the same kept
-    sets as the oracle, ties and signed values included."""
+    1024-thread kernels that re-read the scores per radix pass: with the
+    workspace the library asks for, few segments are split over several
+    work-groups each ("split"); without it, one work-group per segment
+    ("one").  The same kept sets as the oracle, ties and signed values
+    included."""
+    ws = torch.empty(0, dtype=torch.uint8, device="cuda") if form == "one" else None
     rng = np.random.default_rng(n)
     cases = [
         np.full(n, 0.25),
@@ -191,12 +197,81 @@ def test_select_long_segments_ties_and_edges(n):
     ]
     for budget in (20, 21, n // 3, n - 1):
         sc = np.stack(cases)
-        kept, lens, pos = _select_scores(len(cases), n, sc.reshape(-1), budget)
+        kept, lens, pos = _select_scores(len(cases), n, sc.reshape(-1), budget, ws=ws)
         for i, s in enumerate(cases):
             want = oracle.select_kept(s.astype(np.float32).astype(np.float64), n, budget, 4, 16)
             assert lens[i] == len(want)
             assert np.array_equal(kept[i][:lens[i]], want), (i, budget)
             assert np.array_equal(pos[i][:lens[i]], i * n + want)
+
+
+def _split_case(seed=5):
+    """Ragged long and short segments with per-segment budgets (some keeping
+    every row, one rejected) over a synthetic bf16 cache."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([30000, 12289, 500, 20000, 17, 25000, 14000, 9000], dtype=np.int64)
+    budgets = np.array([7000, 12289, 600, 19999, 17, 10, 300, 20], dtype=np.int32)   # [5] below P + R: rejected
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = int(lens.sum())
+    scores = np.concatenate([
+        np.exp(-25 * rng.random(n)) if i % 2 else rng.integers(0, 50, n).astype(np.float64)
+        for i, n in enumerate(lens)])
+    dev = "cuda"
+    k = torch.arange(rows * 128, dtype=torch.float32, device=dev).view(rows, 128).to(torch.bfloat16)
+    pos = torch.arange(rows, dtype=torch.int32, device=dev)
+    cin = kv.make_cache(k, -k, pos, torch.from_numpy(offs).to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev),
+                        1, int(lens.max()))
+    cap = int(lens.max())
+    n_seg = len(lens)
+    out = {"k": torch.zeros(n_seg * cap, 128, dtype=torch.bfloat16, device=dev),
+           "v": torch.zeros(n_seg * cap, 128, dtype=torch.bfloat16, device=dev),
+           "pos": torch.zeros(n_seg * cap, dtype=torch.int32, device=dev),
+           "off": torch.arange(n_seg, dtype=torch.int64, device=dev) * cap,
+           "len": torch.full((n_seg,), -9, dtype=torch.int32, device=dev),
+           "kept": torch.full((n_seg * cap,), -5, dtype=torch.int32, device=dev)}
+    cout = kv.make_cache(out["k"], out["v"], out["pos"], out["off"], out["len"], 1, cap)
+    sc = torch.from_numpy(scores.astype(np.float32)).to(dev)
+    bud = torch.from_numpy(budgets).to(dev)
+    return lens, offs, budgets, scores, cin, cout, sc, bud, out, cap
+
+
+def _check_split(lens, offs, budgets, scores, out, cap, allow_failed):
+    got_len = out["len"].cpu().numpy()
+    kept = out["kept"].cpu().numpy()
+    pos = out["pos"].cpu().numpy()
+    for s, (n, o, b) in enumerate(zip(lens, offs, budgets)):
+        if b < n and b < 20:                       # below prefix + recent: rejected
+            assert got_len[s] == -1, (s, got_len[s])
+            continue
+        if allow_failed and got_len[s] == -1:
+            continue
+        want = oracle.select_kept(scores[o:o + n].astype(np.float32).astype(np.float64), int(n), int(b), 4, 16)
+        assert got_len[s] == len(want), (s, got_len[s], len(want))
+        assert np.array_equal(kept[s * cap:s * cap + len(want)], want), s
+        assert np.array_equal(pos[s * cap:s * cap + len(want)], o + want), s
+
+
+def test_select_split_budgets_and_failed_meetings(monkeypatch):
+    """The several-work-groups-per-segment selection with per-segment budgets
+    over ragged segments (long and short, budgets keeping everything, a
+    rejected one) matches the oracle; with the meeting poll bound forced to
+    one poll from the host, segments whose work-groups did not meet report -1
+    and every other one is exact; a later call with the default bound is
+    whole again."""
+    lens, offs, budgets, scores, cin, cout, sc, bud, out, cap = _split_case()
+    kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
+    torch.cuda.synchronize()
+    _check_split(lens, offs, budgets, scores, out, cap, allow_failed=False)
+    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    out["len"].fill_(-9)
+    kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
+    torch.cuda.synchronize()
+    _check_split(lens, offs, budgets, scores, out, cap, allow_failed=True)
+    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    out["len"].fill_(-9)
+    kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
+    torch.cuda.synchronize()
+    _check_split(lens, offs, budgets, scores, out, cap, allow_failed=False)
 
 
 def test_select_rejects_budget_below_protected():
