@@ -152,7 +152,11 @@ kve_status kv_evict_entropy_budgets(const float* head_entropy, int32_t inverse, 
                                     const int32_t* cap, int32_t batch, int32_t n_heads, int32_t min_per_head,
                                     int32_t* budget_out, void* stream);
 
-/* Workspace bytes kv_evict_select_compact needs (0 when kept_idx is supplied). */
+/* Workspace bytes kv_evict_select_compact asks for: the kept-index list when
+ * kept_idx is not supplied (the part it requires), then, for at most 128
+ * segments, a control area of about 4.3 KB per segment that lets segments too
+ * long for one work-group's on-chip keys be selected by several work-groups
+ * each (with less, those run one work-group per segment). */
 size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx);
 
 /*
@@ -172,7 +176,10 @@ size_t kv_evict_select_workspace(const kve_cache* out, int32_t have_kept_idx);
  * The output must not overlap the input (EALIAS); out->max_seg_len is each output
  * segment's capacity.  A segment whose budget is below n_prefix+n_recent (and
  * below n), or larger than the output capacity, or whose metadata is out of
- * range, gets out->seg_len[s] = -1 and no rows.
+ * range, gets out->seg_len[s] = -1 and no rows.  Work-groups that share a long
+ * segment meet with bounded polling; a segment whose work-groups could not all
+ * run within that bound (only on a device busy with other work for that long)
+ * also gets -1.
  * Errors: EINVAL, ESHAPE (dtype/head_dim/n_seg mismatch), EALIAS,
  * EBUDGET (uniform_budget < n_prefix+n_recent, or > out->max_seg_len), EWORKSPACE, EDEVICE.
  */
