@@ -78,6 +78,8 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
 // stores are done, so the loads run two batches ahead of the stores and a
 // batch is reloaded two batches after its stores, which leaves two batches in
 // flight at every wait.  Loads past the last row repeat it (no branch).
+// Every access is non-temporal: the rows are not touched again here, and
+// keeping them out of L2 leaves it to the scoring passes of other work-groups.
 template <int CPR, int GU = 2, typename SrcAt, typename DstAt>
 __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& dst_at, int cnt, const void* k,
                                             const void* v, const int32_t* pos, int64_t in_off, void* k_out,
@@ -100,7 +102,7 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& ds
     for (int u = 0; u < GU; ++u) bt.src[u] = src_at(min(r0 + u * RPP + rsub, cnt - 1));
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
-      bt.k[u] = kin[(in_off + bt.src[u]) * CPR + part];
+      bt.k[u] = __builtin_nontemporal_load(&kin[(in_off + bt.src[u]) * CPR + part]);
       bt.v[u] = __builtin_nontemporal_load(&vin[(in_off + bt.src[u]) * CPR + part]);
       bt.pos[u] = pos[in_off + bt.src[u]];
     }
