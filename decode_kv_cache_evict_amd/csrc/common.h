@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "kvevict.h"
 
 namespace kve {
@@ -48,7 +50,17 @@ template <> struct Elem<float> {
 
 // ---------------------------------------------------------------- RoPE
 // Rotate the pair (a, b) of frequency index i (of head_dim d) to position p:
-// (a cos - b sin, b cos + a sin), angle p * theta^(-2i/d) in double.
+// (a cos - b sin, b cos + a sin), angle p * theta^(-2i/d) in double.  The
+// inverse frequencies theta^(-2i/d), i < d/2, are formed once on the host
+// (double-precision pow) and passed to the kernels by value.
+struct InvFreq {
+  double v[64];
+};
+inline InvFreq inv_freq(double theta, int d) {
+  InvFreq f{};
+  for (int i = 0; i < d / 2 && i < 64; ++i) f.v[i] = std::pow(theta, -2.0 * double(i) / double(d));
+  return f;
+}
 struct RotPair { double a, b; };
 __device__ __forceinline__ RotPair rotate_pair(double a, double b, double c, double s) {
 #pragma clang fp contract(off)
@@ -57,8 +69,8 @@ __device__ __forceinline__ RotPair rotate_pair(double a, double b, double c, dou
   r.b = b * c + a * s;
   return r;
 }
-__device__ __forceinline__ RotPair rope_pair(double a, double b, int i, int d, int p, double theta) {
-  const double ang = double(p) * pow(theta, -2.0 * double(i) / double(d));
+__device__ __forceinline__ RotPair rope_pair(double a, double b, double inv, int p) {
+  const double ang = double(p) * inv;
   double s, c;
   sincos(ang, &s, &c);
   return rotate_pair(a, b, c, s);

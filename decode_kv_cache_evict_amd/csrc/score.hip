@@ -64,7 +64,7 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 template <typename T>
 __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
                                   const int32_t* __restrict__ n_obs, T* __restrict__ qr,
-                                  int64_t n_work, int n_q, int max_obs, int D, double theta, int hsplit) {
+                                  int64_t n_work, int n_q, int max_obs, int D, InvFreq inv, int hsplit) {
   constexpr int V = 16 / int(sizeof(T));          // frequencies per thread
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n_work) return;
@@ -83,7 +83,7 @@ __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __rest
     sn[v] = 0.0;
     cs[v] = 1.0;
     if (live) {
-      const double ang = double(q_pos[bo]) * pow(theta, -2.0 * double(i0 + v) / double(D));
+      const double ang = double(q_pos[bo]) * inv.v[i0 + v];
       sincos(ang, &sn[v], &cs[v]);
     }
   }
@@ -1132,14 +1132,15 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   while (a.n_q >= 8 * hsplit && base_work * hsplit < 65536) hsplit *= 2;
   const int64_t n_work = base_work * hsplit;
   const dim3 rg(unsigned((n_work + 255) / 256));
+  const InvFreq inv = inv_freq(a.theta, a.head_dim);
   if (n_work > 0) {
     if (a.dtype == 0)
       hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
                          a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim,
-                         a.theta, hsplit);
+                         inv, hsplit);
     else
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
-                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, a.theta, hsplit);
+                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, inv, hsplit);
   }
   e = hipGetLastError();
   return ctl;
