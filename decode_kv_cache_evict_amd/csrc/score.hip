@@ -61,12 +61,17 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 // the angles are shared by all query heads, so their sines and cosines are
 // formed once per group and applied to each of its heads, with 16-byte loads
 // and stores of both halves.  Small batches split the heads over more groups.
+// The same launch clears the n_zero control ints of the scoring kernel that
+// follows (queue tickets and arrival counters): one launch fewer, and no
+// memset node when the call is captured in a graph.
 template <typename T>
 __global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
                                   const int32_t* __restrict__ n_obs, T* __restrict__ qr,
-                                  int64_t n_work, int n_q, int max_obs, int D, InvFreq inv, int hsplit) {
+                                  int64_t n_work, int n_q, int max_obs, int D, InvFreq inv, int hsplit,
+                                  int* __restrict__ zero, int n_zero) {
   constexpr int V = 16 / int(sizeof(T));          // frequencies per thread
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < n_zero) zero[idx] = 0;
   if (idx >= n_work) return;
   const int half = D / 2;
   const int runs = half / V;
@@ -932,13 +937,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   score_mfma_body<D, RT, kModeFill>(a, ctl);
 }
 
-// Zero a small int array (queue tickets and arrival counters) with a kernel, so
-// a captured graph holds no memset node.
-__global__ void zero_ints_kernel(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
 // ------------------------------------------------------------ entropy
 // E = (ln S - sum(s ln s) / S) / ln n over one segment's scores: each term
 // s log2 s in fp32 (the hardware log2, about one ulp; scores under 1e-30 are
@@ -1007,10 +1005,9 @@ hipError_t launch_mfma_rt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   }
 }
 
+// The control ints (tickets, arrival counters) were cleared by the query rotation.
 template <int D, int RT>
 hipError_t launch_fused_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
-  const int n_ctl = kQueues + a.n_seg;
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
   hipLaunchKernelGGL((score_fused_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
   return hipGetLastError();
@@ -1029,8 +1026,6 @@ hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
 
 template <int D, int RT>
 hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
-  const int n_ctl = kQueues + 3 * a.n_seg;       // tickets, two arrival counters and a finish counter per segment
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((n_ctl + 255) / 256)), dim3(256), 0, st, ctl, n_ctl);
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
   if (a.inplace)
     hipLaunchKernelGGL((score_fill_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
@@ -1114,7 +1109,7 @@ namespace {
 
 // Carve the workspace and rotate the observation queries; returns the control
 // counters' address.
-int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
+int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e, int n_zero) {
   const int batch = a.n_seg / a.n_kv;
   const size_t elem = a.dtype == 0 ? 2 : 4;
   const size_t nch256 = (size_t(a.max_seg_len) + kScoreChunk - 1) / kScoreChunk;
@@ -1131,16 +1126,17 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e) {
   int hsplit = 1;                              // head groups of at least 4 heads: about 64K threads in all
   while (a.n_q >= 8 * hsplit && base_work * hsplit < 65536) hsplit *= 2;
   const int64_t n_work = base_work * hsplit;
-  const dim3 rg(unsigned((n_work + 255) / 256));
+  const dim3 rg(unsigned((std::max<int64_t>(n_work, n_zero) + 255) / 256));
   const InvFreq inv = inv_freq(a.theta, a.head_dim);
-  if (n_work > 0) {
+  if (n_work > 0 || n_zero > 0) {
     if (a.dtype == 0)
       hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
                          a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim,
-                         inv, hsplit);
+                         inv, hsplit, ctl, n_zero);
     else
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
-                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, inv, hsplit);
+                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, inv, hsplit, ctl,
+                         n_zero);
   }
   e = hipGetLastError();
   return ctl;
@@ -1164,7 +1160,7 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
   const bool fused = a.dtype == 0 && a.impl == 2;
   a.chunk = fused ? fused_chunk(a.n_seg, a.max_seg_len) : mfma ? mfma_chunk(a.n_seg, a.max_seg_len) : kScoreChunk;
   hipError_t e;
-  int* ctl = prepare(a, ws, st, e);
+  int* ctl = prepare(a, ws, st, e, fused ? kQueues + a.n_seg : 0);   // tickets and an arrival counter per segment
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_chunks), unsigned(a.n_seg));
@@ -1188,7 +1184,8 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
   a.chunk = a.inplace ? fill_chunk(a.n_seg, a.max_seg_len) : step_chunk(a.n_seg, a.max_seg_len);
   hipError_t e;
-  int* ctl = prepare(a, ws, st, e);
+  // tickets, two arrival counters and a finish counter per segment
+  int* ctl = prepare(a, ws, st, e, kQueues + 3 * a.n_seg);
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   return a.head_dim == 128 ? launch_step<128>(a, ctl, st) : launch_step<64>(a, ctl, st);
