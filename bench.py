@@ -627,6 +627,17 @@ def config_bench(args, w):
         nbytes["score"] = score_bytes + S * 4
         nbytes["budgets"] = S * 4 * 4 + L * B * 4
         nbytes["select_compact"] = rows * 4 + 4 * kept_rows * row + 2 * kept_rows * 4
+        if args.call == "fused":
+            # the same trigger in one call: scores, entropies, head budgets,
+            # select and gather in one kernel (K read once; the kept V rows read
+            # and the kept K/V/pos written once)
+            ws_b = torch.empty(kv.kv_evict_score_budget_select_compact_workspace(cache, obs, cout, False, True) + 256,
+                               dtype=torch.uint8, device=dev)
+            name = "score_budget_select_compact"
+            calls = [(name, lambda: kv.kv_evict_score_budget_select_compact(
+                cache, obs, scores, ent, layer_total, w.min_per_head, w.n_prefix, w.n_recent, cout,
+                budget_out=budget, ws=ws_b))]
+            nbytes = {name: score_bytes + 3 * S * 4 + 3 * kept_rows * row + kept_rows * 4}
         what = f"U[{w.len_lo}, {w.len_hi}] -> entropy-driven per-head budgets ({kept_rows} rows kept in all)"
     if w.fps_cap:
         fb, fc = torch.empty_like(c["buf"]), torch.empty_like(c["count"])

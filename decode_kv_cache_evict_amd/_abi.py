@@ -24,7 +24,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
            "kv_evict_score_select_compact_workspace",
            "kv_evict_score_select_compact", "kv_evict_score_select_compact_inplace_workspace",
-           "kv_evict_score_select_compact_inplace", "beacon_fps_update",
+           "kv_evict_score_select_compact_inplace", "kv_evict_score_budget_select_compact_workspace",
+           "kv_evict_score_budget_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
            "kv_decode_attention_workspace", "kv_decode_attention",
            "kv_rope_apply", "kve_last_error", "kve_abi_version"]
@@ -76,6 +77,8 @@ def lib():
             "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
             "kv_evict_score_select_compact_inplace_workspace": (SZ, [CP, OP]),
             "kv_evict_score_select_compact_inplace": (I32, [CP, OP, P, P, I32, I32, I32, P, P, SZ, P]),
+            "kv_evict_score_budget_select_compact_workspace": (SZ, [CP, OP, CP, I32, I32]),
+            "kv_evict_score_budget_select_compact": (I32, [CP, OP, P, P, I32, P, I32, P, I32, I32, P, CP, P, SZ, P]),
             "beacon_fps_update": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P, P]),
             "epikv_workspace_size": (SZ, [I32, I32]),
             "epikv_score": (I32, [P, P, I32, I32, I32, I32, F, I32, P, P, P, SZ, P]),
@@ -245,6 +248,28 @@ def kv_evict_score_select_compact_inplace(cache, obs, scores, budget, n_prefix, 
     _check(lib().kv_evict_score_select_compact_inplace(ctypes.byref(cache), ctypes.byref(obs), _ptr(scores),
                                                        _ptr(budget), int(uniform_budget), int(n_prefix),
                                                        int(n_recent), _ptr(new_len), wp, wn, _stream(stream)))
+
+
+def kv_evict_score_budget_select_compact_workspace(cache_in, obs, cache_out, have_kept_idx, have_budget_out):
+    return int(lib().kv_evict_score_budget_select_compact_workspace(
+        ctypes.byref(cache_in), ctypes.byref(obs), ctypes.byref(cache_out), int(bool(have_kept_idx)),
+        int(bool(have_budget_out))))
+
+
+def kv_evict_score_budget_select_compact(cache_in, obs, scores, head_entropy, layer_total, min_per_head, n_prefix,
+                                         n_recent, cache_out, inverse=0, budget_out=None, kept_idx=None, ws=None,
+                                         stream=None):
+    """One trigger with entropy-driven head budgets: scores, head_entropy (fp32 [n_seg], written), the
+    request-layer totals layer_total (int32 [n_seg / n_kv_heads]), budgets (budget_out, optional) and the
+    compacted output cache."""
+    if ws is None:
+        ws = _ws(kv_evict_score_budget_select_compact_workspace(cache_in, obs, cache_out, kept_idx is not None,
+                                                                budget_out is not None), scores.device)
+    wp, wn = _aligned(ws)
+    _check(lib().kv_evict_score_budget_select_compact(
+        ctypes.byref(cache_in), ctypes.byref(obs), _ptr(scores), _ptr(head_entropy), int(inverse), _ptr(layer_total),
+        int(min_per_head), _ptr(budget_out), int(n_prefix), int(n_recent), _ptr(kept_idx), ctypes.byref(cache_out),
+        wp, wn, _stream(stream)))
 
 
 def beacon_fps_update(q_in, q_out, count_in, count_out, k_keep, picks=None, stream=None):

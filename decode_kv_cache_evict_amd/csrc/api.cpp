@@ -436,6 +436,98 @@ kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, 
                        "kv_evict_score_select_compact");
 }
 
+size_t kv_evict_score_budget_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
+                                                      int32_t have_kept_idx, int32_t have_budget_out) {
+  int32_t rows = 0;
+  if (check_cache(in, "in", true) != KVE_OK || check_obs(in, o, &rows) != KVE_OK || !out || out->n_rows < 0)
+    return 0;
+  return step_score_ws(in, o, rows) + (have_kept_idx ? 0 : round256(size_t(out->n_rows) * sizeof(int32_t))) +
+         (have_budget_out ? 0 : round256(size_t(in->n_seg) * sizeof(int32_t)));
+}
+
+kve_status kv_evict_score_budget_select_compact(const kve_cache* in, const kve_obs* o, float* scores,
+                                                float* head_entropy, int32_t inverse, const int32_t* layer_total,
+                                                int32_t min_per_head, int32_t* budget_out, int32_t n_prefix,
+                                                int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  // every check of the three halves runs before anything is launched
+  kve_status st = check_cache(in, "in", true);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(out, "out", true)) != KVE_OK) return st;
+  int32_t rows = 0;
+  if ((st = check_obs(in, o, &rows)) != KVE_OK) return st;
+  if (in->dtype != out->dtype || in->head_dim != out->head_dim || in->n_seg != out->n_seg ||
+      in->n_kv_heads != out->n_kv_heads)
+    return fail(KVE_ESHAPE, "in/out cache shapes differ");
+  if (inverse != 0 && inverse != 1) return fail(KVE_EINVAL, "inverse must be 0 or 1");
+  if (n_prefix < 0 || n_recent < 0 || min_per_head < 0) return fail(KVE_EINVAL, "negative prefix/recent/floor");
+  if (in->n_kv_heads > 64) return fail(KVE_ESHAPE, "n_kv_heads %d > 64", in->n_kv_heads);
+  if (in->n_seg > 0 && (!scores || !head_entropy || !layer_total))
+    return fail(KVE_EINVAL, "null scores, head_entropy or layer_total");
+  if (in->max_seg_len > out->max_seg_len)
+    return fail(KVE_EBUDGET, "output capacity %d below max_seg_len %d (a head may keep every row)",
+                out->max_seg_len, in->max_seg_len);
+  const bool fused = in->dtype == KVE_BF16 && score_impl() == 0 && in->max_seg_len > 0 &&
+                     kve::budget_step_fits(in->n_seg, in->n_kv_heads, in->max_seg_len, in->head_dim);
+  const int impl = in->dtype == KVE_BF16 ? score_impl() : 1;
+  if (!fused && impl == 1 && valu_lds(rows, in->head_dim, in->dtype) > 65536)
+    return fail(KVE_ESHAPE, "rows*head_dim too large for the fp32 scoring path");
+  const size_t sw = step_score_ws(in, o, rows);
+  const size_t kb = kept_idx ? 0 : round256(size_t(out->n_rows) * sizeof(int32_t));
+  const size_t bb = budget_out ? 0 : round256(size_t(in->n_seg) * sizeof(int32_t));
+  const size_t need = sw + kb + bb;
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
+  char* wsc = static_cast<char*>(ws);
+  int32_t* kept = kept_idx ? kept_idx : reinterpret_cast<int32_t*>(wsc + sw);
+  int32_t* budget = budget_out ? budget_out : reinterpret_cast<int32_t*>(wsc + sw + kb);
+  const int32_t batch = in->n_seg / in->n_kv_heads;
+  const size_t ns = size_t(in->n_seg);
+  const void* ins[] = {in->k, in->v, in->pos, in->seg_off, in->seg_len, o->q, o->q_pos, o->n_obs, layer_total,
+                       out->seg_off};
+  const size_t insz[] = {rows_bytes(in), rows_bytes(in), size_t(in->n_rows) * 4, ns * 8, ns * 4,
+                         size_t(batch) * o->n_q_heads * o->max_obs * in->head_dim * elem_bytes(in->dtype),
+                         size_t(batch) * o->max_obs * 4, size_t(batch) * 4, size_t(batch) * 4, ns * 8};
+  const void* outs[] = {scores, head_entropy, budget, out->k, out->v, out->pos, out->seg_len, kept, ws};
+  const size_t outsz[] = {size_t(in->n_rows) * 4, ns * 4, ns * 4, rows_bytes(out), rows_bytes(out),
+                          size_t(out->n_rows) * 4, ns * 4, size_t(out->n_rows) * 4, sw};
+  for (int i = 0; i < 9; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 9; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
+  if (in->n_seg == 0) return KVE_OK;
+  if (!fused) {
+    if ((st = kv_evict_score(in, o, scores, head_entropy, ws, sw, stream)) != KVE_OK) return st;
+    if ((st = kv_evict_entropy_budgets(head_entropy, inverse, layer_total, in->seg_len, batch, in->n_kv_heads,
+                                       min_per_head, budget, stream)) != KVE_OK)
+      return st;
+    // the scoring workspace is free again (stream order): the selection's control ints
+    return kv_evict_select_compact(in, scores, nullptr, in->n_rows, budget, 0, n_prefix, n_recent, kept, out, ws, sw,
+                                   stream);
+  }
+  kve::ScoreArgs a = score_args(in, o, rows, scores);
+  a.entropy = head_entropy;
+  a.v = in->v;
+  a.k_out = out->k;
+  a.v_out = out->v;
+  a.pos_out = out->pos;
+  a.out_off = out->seg_off;
+  a.out_len = out->seg_len;
+  a.out_rows = out->n_rows;
+  a.out_cap = out->max_seg_len;
+  a.kept = kept_idx;
+  a.n_prefix = n_prefix;
+  a.n_recent = n_recent;
+  a.layer_total = layer_total;
+  a.min_per_head = min_per_head;
+  a.ent_form = inverse;
+  a.budget_out = budget_out;
+  return device_status(kve::launch_score_budget_select_compact(a, ws, static_cast<hipStream_t>(stream)),
+                       "kv_evict_score_budget_select_compact");
+}
+
 size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const kve_obs* o) {
   int32_t rows = 0;
   if (check_cache(c, "cache", true) != KVE_OK || check_obs(c, o, &rows) != KVE_OK) return 0;

@@ -8,14 +8,13 @@
 // exactly on the breakpoints of the piecewise-linear sum, then rounded by the
 // largest-remainder rule (ties to the lower index).  Double precision; the
 // layer table is one thread's work, the per-request head budgets one wave's.
+#include "budget_common.h"
 #include "common.h"
 #include "internal.h"
 
 namespace kve {
 
 namespace {
-
-constexpr int kMaxHeads = 64;
 
 __device__ double clamp_sum(const double* w, const double* lo, const double* hi, int H, double lam) {
   double f = 0.0;
@@ -146,112 +145,16 @@ __device__ void allocate(const double* w_in, double lo_all, const double* hi, in
   round_shares(x, H, (long long)(total + 0.5), out);
 }
 
-// One wave per request, lane g = head g: the same shares as allocate() (every
-// sum over heads is taken in head order by a plain loop, so the rounding is
-// the serial solver's), with the breakpoint search and the largest-remainder
-// ranking spread over the lanes.
-__device__ __forceinline__ double wave_min_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmin(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 __global__ __launch_bounds__(64) void head_budget_kernel(const float* __restrict__ wts, const int32_t* __restrict__ tot,
                                                          const int32_t* __restrict__ cap, int batch, int H, int lo_all,
                                                          int form, int32_t* __restrict__ out) {
-  __shared__ double sw[kMaxHeads], slo[kMaxHeads], shi[kMaxHeads], sfr[kMaxHeads];
-  __shared__ int spart[kMaxHeads];
+  __shared__ HeadBudgetLds L;
   const int b = blockIdx.x, g = threadIdx.x;
   if (b >= batch) return;
   const bool act = g < H;
-  double w = 0.0, hi = 0.0;
-  if (act) {
-    const double e = double(wts[b * H + g]);
-    w = form == 1 ? 1.0 - e : e;              // inverse entropy: focused heads gain budget
-    hi = double(cap[b * H + g] > 0 ? cap[b * H + g] : 0);
-    w = w > 0.0 ? w : 0.0;
-  }
-  const double lo = act ? fmin(double(lo_all), hi) : 0.0;
-  // sums of integers: exact in any order
-  const double sum_hi = wave_sum_f64(hi), sum_lo = wave_sum_f64(lo);
-  const double total = fmin(double(tot[b]), sum_hi);
-  int32_t* o = out + b * H;
-  if (total >= sum_hi) {
-    if (act) o[g] = int32_t(hi);
-    return;
-  }
-  if (total < sum_lo - 1e-9) {
-    if (act) o[g] = -1;
-    return;
-  }
-  if (!__any(act && w > 0.0) && act) w = 1.0;
-  const bool pos = act && w > 0.0;
-  const double cap_pos = wave_sum_f64(pos ? hi : 0.0), lo_zero = wave_sum_f64(act && !pos ? lo : 0.0);
-  const bool any_zero = __any(act && !pos);
-  // weightless heads cannot grow with lam: when the weighted heads' caps and the
-  // weightless floors cannot absorb the total, the weighted heads sit at their
-  // caps and the weightless ones split the rest equally
-  const bool zero_split = any_zero && total > cap_pos + lo_zero;
-  const bool part = zero_split ? act && !pos : act;
-  const double pw = zero_split ? 1.0 : w;
-  const double ptot = zero_split ? total - cap_pos : total;
-  sw[g] = pw;
-  slo[g] = lo;
-  shi[g] = hi;
-  spart[g] = part;
-  __syncthreads();
-  auto f = [&](double lam) {                  // sum of the clamped shares, in head order
-    double v = 0.0;
-    for (int q = 0; q < H; ++q)
-      if (spart[q]) v += fmin(fmax(lam * sw[q], slo[q]), shi[q]);
-    return v;
-  };
-  // breakpoints: 0 and, per participating head with weight, lo/w and hi/w
-  const bool owns = part && pw > 0.0;
-  const double p1 = owns ? lo / pw : 0.0, p2 = owns ? hi / pw : 0.0;
-  const double f1 = owns ? f(p1) : 0.0, f2 = owns ? f(p2) : 0.0;
-  const double f0 = f(0.0);
-  double lam;
-  const double kBigD = 1.0e300;
-  if (ptot <= f0) {
-    lam = 0.0;
-  } else {
-    double cand = kBigD;                        // smallest breakpoint whose sum reaches the total
-    if (owns && f1 >= ptot) cand = fmin(cand, p1);
-    if (owns && f2 >= ptot) cand = fmin(cand, p2);
-    const double bb = wave_min_f64(cand);
-    if (bb == kBigD) {
-      lam = wave_max_f64(owns ? fmax(p1, p2) : 0.0);   // the largest breakpoint
-    } else {
-      double below = 0.0;                       // largest breakpoint below it (0 is one)
-      if (owns && p1 < bb) below = fmax(below, p1);
-      if (owns && p2 < bb) below = fmax(below, p2);
-      const double aa = wave_max_f64(below);
-      const double fa = f(aa);
-      const double mid = 0.5 * (aa + bb);
-      double wf = 0.0;
-      for (int q = 0; q < H; ++q) {
-        const double v = mid * sw[q];
-        if (spart[q] && sw[q] > 0.0 && v > slo[q] && v < shi[q]) wf += sw[q];
-      }
-      lam = wf == 0.0 ? bb : aa + (ptot - fa) / wf;
-    }
-  }
-  const double x = !act ? 0.0 : part ? fmin(fmax(lam * pw, lo), hi) : hi;
-  // largest remainder: +1 to the r heads with the largest fractional parts (ties to the lower head)
-  const double fl = floor(x);
-  const double fr = x - fl;
-  const long long r = (long long)(total + 0.5) - (long long)wave_sum_f64(fl);
-  sfr[g] = fr;
-  __syncthreads();
-  long long rank = 0;
-  for (int q = 0; q < H; ++q) rank += (sfr[q] > fr || (sfr[q] == fr && q < g)) ? 1 : 0;
-  if (act) o[g] = int32_t(fl) + (rank < r ? 1 : 0);
+  const int32_t v = head_budget_wave(act ? double(wts[b * H + g]) : 0.0, form, act ? cap[b * H + g] : 0,
+                                     double(tot[b]), lo_all, H, L);
+  if (act) out[b * H + g] = v;
 }
 
 __global__ void wave_budget_kernel(int L, double center, double sigma, int total, int lo, int32_t* out) {

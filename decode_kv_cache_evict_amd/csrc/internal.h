@@ -44,12 +44,20 @@ struct ScoreArgs {
   const int32_t* budget;  // [n_seg] or null
   int32_t uniform_budget, n_prefix, n_recent;
   int32_t inplace;        // 1: hole filling within the input cache (k_out = k, out_len = new lengths)
+  // entropy budgets in the one-kernel trigger (kv_evict_score_budget_select_compact) only
+  const int32_t* layer_total;  // [n_seg / n_kv] request-layer totals
+  int32_t min_per_head, ent_form;  // ent_form 1: weights 1 - entropy
+  int32_t* budget_out;    // [n_seg] or null
 };
 
 // Largest segment the one-kernel step can select on chip: its order keys reuse the
 // two 64-key tiles of padded bf16 rows (64 * (D + 8) 32-bit words).
 constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 8); }
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
+// The one-kernel trigger with entropy budgets applies when every
+// request-layer's work-groups fit the dispatch bound of its barrier.
+bool budget_step_fits(int32_t n_seg, int32_t n_kv, int32_t max_seg_len, int32_t head_dim);
+hipError_t launch_score_budget_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
 
 size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_t head_dim, int32_t dtype,
                              int32_t n_seg, int32_t max_seg_len, int32_t rows);

@@ -11,6 +11,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "budget_common.h"
 #include "common.h"
 #include "internal.h"
 #include "select_common.h"
@@ -411,7 +412,7 @@ __device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float 
 // The wait is bounded all the same (ScoreArgs::spin_limit polls).
 constexpr int kMaxWaitChunks = 12;
 constexpr int kQueues = 8;
-constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3, kModeFill = 4;
+constexpr int kModePass1 = 0, kModePass2 = 1, kModeFused = 2, kModeStep = 3, kModeFill = 4, kModeBudget = 5;
 
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
@@ -468,13 +469,22 @@ __device__ __forceinline__ int take_ticket(const ScoreArgs& a, int* ctl) {
 // their slots for new chunks.  keys: LDS scratch of step_max_seg(D) words.
 
 // The segment's scores into LDS as order keys (eight loads in flight per
-// thread, clamped addresses so that no load waits on a branch), then T, the
-// kc-th largest candidate key, and kk, the number of candidates equal to T
-// that are kept.  hist: 256 words of LDS; sh: 2 words.
-__device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t off, int n, int kc, uint32_t* keys,
-                                                  uint32_t* hist, uint32_t* sh, int tid, uint32_t& T, uint32_t& kk) {
+// thread, clamped addresses so that no load waits on a branch) and the
+// candidates' smallest and largest key.  With ENT, also the segment's
+// normalised score entropy (ReasonAlloc, "Key Concepts"), with the arithmetic
+// of entropy_kernel: per score, fp32 s * log2(s) for s > 1e-30, double sums.
+// hist: 256 words of LDS.
+struct SegKeys {
+  uint32_t kmin, kmax;
+  float entropy;
+};
+template <bool ENT>
+__device__ __forceinline__ SegKeys segment_keys(const ScoreArgs& a, int64_t off, int n, uint32_t* keys,
+                                                uint32_t* hist, int tid) {
+  __shared__ double esum[2][4];
   const int P = a.n_prefix, R = a.n_recent;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  double S = 0.0, Q2 = 0.0;
   for (int j0 = 0; j0 < n; j0 += 8 * 256) {
     float raw[8];
 #pragma unroll
@@ -491,6 +501,10 @@ __device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t of
           kmin = min(kmin, key);
           kmax = max(kmax, key);
         }
+        if (ENT) {
+          S += double(raw[u]);
+          if (raw[u] > 1e-30f) Q2 += double(raw[u] * __builtin_amdgcn_logf(raw[u]));
+        }
       }
     }
   }
@@ -499,37 +513,68 @@ __device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t of
     kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
     kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
   }
+  if (ENT) {
+    S = wave_sum_f64(S);
+    Q2 = wave_sum_f64(Q2 * 0.69314718055994530942);   // log2 -> ln
+  }
   if ((tid & 63) == 0) {
     hist[tid >> 6] = kmin;
     hist[4 + (tid >> 6)] = kmax;
+    if (ENT) {
+      esum[0][tid >> 6] = S;
+      esum[1][tid >> 6] = Q2;
+    }
   }
   __syncthreads();
-  kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
-  kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+  SegKeys r;
+  r.kmin = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
+  r.kmax = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+  r.entropy = 0.f;
+  if (ENT) {
+    const double St = esum[0][0] + esum[0][1] + esum[0][2] + esum[0][3];
+    const double Qt = esum[1][0] + esum[1][1] + esum[1][2] + esum[1][3];
+    if (n > 1 && St > 0.0) r.entropy = float((log(St) - Qt / St) / log(double(n)));
+  }
   __syncthreads();
+  return r;
+}
+
+// T, the kc-th largest candidate key among the keys in LDS, and kk, the number
+// of candidates equal to T that are kept.  hist: 256 words of LDS; sh: 2 words.
+__device__ __forceinline__ void segment_radix(const ScoreArgs& a, int n, int kc, const uint32_t* keys,
+                                              const SegKeys& sk, uint32_t* hist, uint32_t* sh, int tid,
+                                              uint32_t& T, uint32_t& kk) {
+  const int P = a.n_prefix, R = a.n_recent;
   // every candidate shares the leading bits of its min and max: the radix digits start below them
-  const int known = kmin == kmax ? 32 : __clz(int(kmin ^ kmax));
+  const int known = sk.kmin == sk.kmax ? 32 : __clz(int(sk.kmin ^ sk.kmax));
   radix_threshold_v<256>(
       [&](const auto& f) {
         for (int j = P + tid; j < n - R; j += 256) f(keys[j]);
       },
-      kc, hist, sh, T, kk, kmin, known);
+      kc, hist, sh, T, kk, sk.kmin, known);
 }
 
-// Copying form: every work-group of the segment finds the threshold and
-// gathers its own chunk's kept rows to their places in the output segment, in
-// ascending slot order (the kept slots and threshold ties before the chunk
-// give its first output row).  Returns keep_n (-1 for a rejected segment).
+__device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t off, int n, int kc, uint32_t* keys,
+                                                  uint32_t* hist, uint32_t* sh, int tid, uint32_t& T, uint32_t& kk) {
+  const SegKeys sk = segment_keys<false>(a, off, n, keys, hist, tid);
+  segment_radix(a, n, kc, keys, sk, hist, sh, tid, T, kk);
+}
+
+// Copying form: every work-group of the segment finds the threshold for
+// budget K and gathers its own chunk's kept rows to their places in the output
+// segment, in ascending slot order (the kept slots and threshold ties before
+// the chunk give its first output row).  `loaded`: the segment's keys are
+// already in LDS (else they are loaded here).  Returns keep_n (-1 for a
+// rejected segment).
 template <int D>
 __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
-                                                   uint32_t* keys, int tid) {
+                                                   int K, uint32_t* keys, const SegKeys* loaded, int tid) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int wtot[4];
   __shared__ int mine[kMfmaChunk];           // this chunk's kept slots, ascending
   const int64_t oo = a.out_off[s];
-  const int K = a.budget ? a.budget[s] : a.uniform_budget;
   const int P = a.n_prefix, R = a.n_recent;
   const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
   const bool bud_ok = K >= n || (K >= P + R && K >= 0);
@@ -543,7 +588,8 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     cnt = k1 - k0;
   } else {
     uint32_t T, kk;
-    segment_threshold(a, off, n, K - P - R, keys, hist, sh, tid, T, kk);
+    if (loaded) segment_radix(a, n, K - P - R, keys, *loaded, hist, sh, tid, T, kk);
+    else segment_threshold(a, off, n, K - P - R, keys, hist, sh, tid, T, kk);
     // kept slots and threshold ties before this chunk
     int eq_b = 0, gt_b = 0;
     for (int j = P + tid; j < min(k0, n - R); j += 256) {
@@ -664,6 +710,63 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
   return K;
 }
 
+// One-kernel trigger with ReasonAlloc's entropy budgets
+// (kv_evict_score_budget_select_compact): the heads of one request-layer
+// (a.n_kv consecutive segments, consecutive tickets of one queue) publish their
+// score entropies, meet at a per-request-layer arrival counter, and each of
+// their work-groups solves the same head budgets (the budget kernel's wave
+// solver) before selecting with its own head's budget.  With one queue, only
+// the newest request-layer can be waiting for work-groups not yet started, so
+// at most n_kv * chunks - 1 <= 95 work-groups wait (the launch keeps to that, or
+// fits in one round of resident work-groups; a segment takes one or two
+// chunks).
+constexpr int kNoBudget = INT_MIN;
+
+// Thread 0 of chunk 0's work-group: publish the segment's entropy and count
+// the head in.
+__device__ __forceinline__ void group_arrive(const ScoreArgs& a, int* ctl, int s, float e) {
+  __hip_atomic_store(&a.entropy[s], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  atomicAdd(ctl + kQueues + 3 * a.n_seg + s / a.n_kv, 1);
+}
+
+// Every thread of every work-group of segment s: the head's budget, or
+// kNoBudget when the heads did not meet within the poll bound or the floors
+// exceed the request-layer's total (the segment then keeps -1).
+__device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s, int ch, float e, int tid) {
+  __shared__ HeadBudgetLds L;
+  __shared__ int kb;
+  const int H = a.n_kv, grp = s / H;
+  int* cnt = ctl + kQueues + 3 * a.n_seg + grp;
+  if (tid == 0) {
+    if (ch == 0) group_arrive(a, ctl, s, e);
+    int spins = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < H && ++spins < a.spin_limit)
+      __builtin_amdgcn_s_sleep(1);
+    kb = spins < a.spin_limit ? 0 : kNoBudget;
+    if (kb == kNoBudget) atomicAdd(cnt, -(1 << 24));
+  }
+  __syncthreads();
+  if (kb == kNoBudget) return kNoBudget;
+  if (tid < kWave) {
+    const bool act = tid < H;
+    const int hs = grp * H + tid;
+    const float eh = act ? __hip_atomic_load(&a.entropy[hs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+    int cap = 0;
+    if (act) {
+      const int nl = a.seg_len[hs];
+      cap = nl >= 0 && nl <= a.max_seg_len ? nl : 0;
+    }
+    const int32_t b = head_budget_wave(double(eh), a.ent_form, cap, double(a.layer_total[grp]), a.min_per_head, H, L);
+    if (tid == s - grp * H) {
+      if (ch == 0 && a.budget_out) a.budget_out[s] = b;   // -1: the floors exceed the total
+      kb = b < 0 ? kNoBudget : b;
+    }
+  }
+  __syncthreads();
+  return kb;
+}
+
 template <int D, int RT, int MODE>
 __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
@@ -683,7 +786,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   const int col = lane & 15, quad = lane >> 4;
   int s, ch;
   if (MODE >= kModeFused) {
-    if (tid == 0) sh_item = take_ticket(a, ctl);
+    if (tid == 0) {
+      if (MODE == kModeBudget) {               // one queue: a request-layer's heads are consecutive tickets
+        const int t = atomicAdd(&ctl[0], 1);
+        sh_item = t < a.n_seg * a.n_chunks ? t : -1;
+      } else {
+        sh_item = take_ticket(a, ctl);
+      }
+    }
     __syncthreads();
     const int item = sh_item;
     if (item < 0) return;
@@ -695,12 +805,18 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   int64_t off;
   int n;
   if (!segment_ok(a, s, off, n)) {
-    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
+    if (MODE >= kModeStep && ch == 0 && tid == 0) {
+      a.out_len[s] = -1;
+      if (MODE == kModeBudget) group_arrive(a, ctl, s, 0.f);
+    }
     return;
   }
   const int k0 = ch * a.chunk;
   if (k0 >= n) {
-    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
+    if (MODE >= kModeStep && ch == 0 && tid == 0) {
+      a.out_len[s] = 0;                        // empty segment
+      if (MODE == kModeBudget) group_arrive(a, ctl, s, 0.f);
+    }
     return;
   }
   const int k1 = min(n, k0 + a.chunk);
@@ -900,7 +1016,20 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
     __syncthreads();
     if (sh_item < 0) return;
-    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, keys, tid);
+    int K;
+    const SegKeys* loaded = nullptr;
+    SegKeys sk;
+    if constexpr (MODE == kModeBudget) {
+      // the segment's scores into LDS and its entropy; the request-layer's
+      // heads meet, then every work-group finds the same head budgets
+      sk = segment_keys<true>(a, off, n, keys, reinterpret_cast<uint32_t*>(&red[0][0][0]), tid);
+      loaded = &sk;
+      K = group_budget(a, ctl, s, ch, sk.entropy, tid);
+      if (K == kNoBudget) return;
+    } else {
+      K = a.budget ? a.budget[s] : a.uniform_budget;
+    }
+    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid);
     if (keep_n < 0) return;
     // the last work-group to finish its gather publishes the segment's length
     __builtin_amdgcn_s_waitcnt(0);
@@ -930,6 +1059,11 @@ template <int D, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_step_kernel(ScoreArgs a,
                                                                                                    int* ctl) {
   score_mfma_body<D, RT, kModeStep>(a, ctl);
+}
+template <int D, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_budget_kernel(ScoreArgs a,
+                                                                                                     int* ctl) {
+  score_mfma_body<D, RT, kModeBudget>(a, ctl);
 }
 template <int D, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_fill_kernel(ScoreArgs a,
@@ -1027,7 +1161,9 @@ hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
 template <int D, int RT>
 hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
-  if (a.inplace)
+  if (a.layer_total)
+    hipLaunchKernelGGL((score_budget_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
+  else if (a.inplace)
     hipLaunchKernelGGL((score_fill_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
   else
     hipLaunchKernelGGL((score_step_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
@@ -1097,7 +1233,7 @@ size_t score_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_obs, int32_
   const size_t nch = (size_t(max_seg_len) + kScoreChunk - 1) / kScoreChunk;
   const size_t st = align_up(size_t(n_seg) * (nch ? nch : 1) * rows * sizeof(float2));
   const size_t ls = align_up(size_t(n_seg) * rows * sizeof(float));
-  const size_t ct = align_up(size_t(3 * n_seg + kQueues) * sizeof(int));
+  const size_t ct = align_up(size_t(4 * n_seg + kQueues) * sizeof(int));
   return qr + st + ls + ct;
 }
 
@@ -1179,6 +1315,28 @@ hipError_t launch_score(ScoreArgs& a, void* ws, hipStream_t st) {
     e = hipGetLastError();
   }
   return e;
+}
+
+// The entropy-budget trigger keeps far fewer rows than it scores, so, as for
+// the in-place form, a whole segment per work-group serves it best (one
+// selection per segment, no segment barrier waits; 32-layer per-head-budget
+// workload: 3.0 ms, against 3.9 ms with 1024-key chunks and 3.2 ms for the
+// three calls).
+bool budget_step_fits(int32_t n_seg, int32_t n_kv, int32_t max_seg_len, int32_t head_dim) {
+  if (n_kv < 1 || n_kv > kMaxHeads || n_seg % n_kv != 0 || max_seg_len > step_max_seg(head_dim)) return false;
+  const int c = fill_chunk(n_seg, max_seg_len);
+  const int64_t items = int64_t(n_seg) * ((max_seg_len + c - 1) / c);
+  return items <= 3 * 256 || int64_t(n_kv) * ((max_seg_len + c - 1) / c) <= 96;
+}
+
+hipError_t launch_score_budget_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {
+  a.chunk = fill_chunk(a.n_seg, a.max_seg_len);
+  hipError_t e;
+  // one ticket queue, three counters per segment, one per request-layer
+  int* ctl = prepare(a, ws, st, e, kQueues + 3 * a.n_seg + a.n_seg / a.n_kv);
+  if (e != hipSuccess) return e;
+  if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
+  return a.head_dim == 128 ? launch_step<128>(a, ctl, st) : launch_step<64>(a, ctl, st);
 }
 
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {

@@ -264,6 +264,46 @@ kve_status kv_evict_score_select_compact_inplace(kve_cache* c, const kve_obs* o,
                                                  int32_t uniform_budget, int32_t n_prefix, int32_t n_recent,
                                                  int32_t* new_len, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes kv_evict_score_budget_select_compact needs. */
+size_t kv_evict_score_budget_select_compact_workspace(const kve_cache* in, const kve_obs* o, const kve_cache* out,
+                                                      int32_t have_kept_idx, int32_t have_budget_out);
+
+/*
+ * kv_evict_score_budget_select_compact — one eviction trigger with ReasonAlloc's
+ * entropy-driven head budgets ("Core Mechanism": online head-wise reallocation;
+ * "Key Concepts": normalised attention entropy): the result of
+ *   kv_evict_score(in, o, scores, head_entropy, ...),
+ *   kv_evict_entropy_budgets(head_entropy, inverse, layer_total, in->seg_len,
+ *                            in->n_seg / in->n_kv_heads, in->n_kv_heads, min_per_head, budget, ...),
+ *   kv_evict_select_compact(in, scores, NULL, in->n_rows, budget, 0, n_prefix, n_recent, kept_idx, out, ...)
+ * with the same meaning of every argument.  The segments of one request-layer
+ * are the in->n_kv_heads consecutive segments b*n_kv_heads .. b*n_kv_heads +
+ * n_kv_heads - 1, and layer_total[b] is their total ([n_seg / n_kv_heads] device
+ * int32, e.g. n_kv_heads times the layer's kv_evict_wave_budgets entry).
+ * head_entropy ([n_seg] fp32) is required and written; budget_out ([n_seg] int32)
+ * is optional and receives the head budgets.  out->max_seg_len must be at least
+ * in->max_seg_len (a head may keep every row).  For bf16 caches whose segments fit
+ * the on-chip selection (8704 rows at head_dim 128, 4608 at 64) and whose heads'
+ * work-groups fit its dispatch bound (about 96 per request-layer, so at most 10
+ * heads of up to 8704 rows) it runs as one kernel: each request-layer's heads score their
+ * chunks, publish their entropies, meet, and every work-group solves the same
+ * head budgets with the budget kernel's solver before selecting and gathering
+ * its own chunk's kept rows; otherwise it makes the three calls.  The entropies
+ * are summed in another order than the stand-alone scoring's (equal to fp32
+ * rounding), so budgets can differ from the three-call form's only where
+ * largest-remainder fractions tie to that rounding.  A request-layer whose
+ * heads could not meet within the poll bound (only on a device stalled that
+ * long), or whose floors exceed its total, gets out->seg_len = -1 in every head.
+ * Errors: the union of the three calls' (EINVAL for inverse not 0/1 or a null
+ * head_entropy/layer_total, ESHAPE, EALIAS, EBUDGET when out->max_seg_len <
+ * in->max_seg_len, EWORKSPACE, EDEVICE).
+ */
+kve_status kv_evict_score_budget_select_compact(const kve_cache* in, const kve_obs* o, float* scores,
+                                                float* head_entropy, int32_t inverse, const int32_t* layer_total,
+                                                int32_t min_per_head, int32_t* budget_out, int32_t n_prefix,
+                                                int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
+                                                size_t ws_bytes, void* stream);
+
 /*
  * beacon_fps_update — BeaconKV "Continual FPS": for each of n_buf buffers of
  * pre-RoPE queries ([n_buf, cap, head_dim], dtype) whose count_in equals cap, run

@@ -79,3 +79,15 @@ def test_host_validation_without_gpu():
     assert _fail(L.kv_evict_entropy_budgets, 0x1000, 2, 0x2000, 0x3000, 4, 8, 64, 0x4000, None)[0] == 1
     assert _fail(L.kv_evict_entropy_budgets, 0x1000, 1, 0x2000, 0x3000, 4, 65, 64, 0x4000, None)[0] == 2
     assert _fail(L.kv_rope_apply, 0x1000, 0x1000, 0x2000, 4, 128, 1e4, 0, None)[0] == 3
+    # one-call entropy-budget trigger: direction flag, missing entropies, output capacity
+    outb = kv.KveCache(**{f: getattr(out, f) for f, _ in kv.KveCache._fields_})
+    outb.k, outb.max_seg_len = 0x10000, 64
+    bw = L.kv_evict_score_budget_select_compact_workspace(ctypes.byref(c), ctypes.byref(o), ctypes.byref(outb), 1, 1)
+    assert bw > 0
+    args = lambda inv, ent, ob: (ctypes.byref(c), ctypes.byref(o), 0x8000, ent, inv, 0x9000, 64, None, 4, 16,  # noqa: E731
+                                 0xA000, ctypes.byref(ob), 0x100000, bw, None)
+    assert _fail(L.kv_evict_score_budget_select_compact, *args(2, 0x8800, outb))[0] == 1
+    assert _fail(L.kv_evict_score_budget_select_compact, *args(0, None, outb))[0] == 1
+    outs = kv.KveCache(**{f: getattr(outb, f) for f, _ in kv.KveCache._fields_})
+    outs.max_seg_len = 63
+    assert _fail(L.kv_evict_score_budget_select_compact, *args(0, 0x8800, outs))[0] == 4

@@ -1,0 +1,172 @@
+"""The one-kernel trigger with ReasonAlloc's entropy-driven head budgets
+(kv_evict_score_budget_select_compact) against the oracle (scores, head
+entropies, head budgets, kept sets and moved bytes) and against the three calls
+it stands for (kv_evict_score with entropies, kv_evict_entropy_budgets,
+kv_evict_select_compact); failure reporting driven from the host."""
+import numpy as np
+import pytest
+import torch
+
+import decode_kv_cache_evict_amd as kv
+import oracle
+from tests.gpu_side import alloc_out, cache_of, device_layer, obs_of, score_layer, select_compact
+from tests.oracle_side import oracle_cache_keys, oracle_layer_scores
+from tests.parity import assert_scores_close, kept_matches
+from workloads import get_workload, make_layer
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # 4 requests x 8 heads, ragged lengths: four request-layers of eight heads
+    "llama-ragged": get_workload("r1-llama-8b").scaled(batch=4, len_lo=700, len_hi=3300, n_layers=1),
+    # d = 64, fewer heads per request-layer
+    "d64": get_workload("tiny-f32").scaled(dtype="bf16", batch=5, len_lo=900, len_hi=2500),
+}
+FLOOR = 24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.lib()
+
+
+_cache = {}
+
+
+def _case(name):
+    if name not in _cache:
+        w = CASES[name]
+        L = make_layer(w, 0)
+        D = device_layer(L, w)
+        k = oracle_cache_keys(L, w)
+        _cache[name] = (w, L, D, oracle_layer_scores(L, w, k))
+    return _cache[name]
+
+
+def _totals(w, L, frac):
+    """Request-layer totals: a fraction of each request's cached rows over its heads."""
+    n = np.asarray(L["lengths"], dtype=np.int64)
+    return (np.maximum(FLOOR * w.n_kv_heads, (frac * n).astype(np.int64) * w.n_kv_heads)).astype(np.int32)
+
+
+def _one_call(D, w, L, totals, inverse):
+    S = D["seg_off"].numel()
+    scores = torch.zeros(D["k"].shape[0], dtype=torch.float32, device="cuda")
+    ent = torch.zeros(S, dtype=torch.float32, device="cuda")
+    bud = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    out = alloc_out(D, w, D["max_len"])
+    cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, out["cap"])
+    tot = torch.from_numpy(totals).to("cuda")
+    kv.kv_evict_score_budget_select_compact(cache_of(D, w), obs_of(D, w), scores, ent, tot, FLOOR, w.n_prefix,
+                                            w.n_recent, cout, inverse=inverse, budget_out=bud, kept_idx=out["kept"])
+    torch.cuda.synchronize()
+    return scores, ent, bud, out
+
+
+def _ints(t):
+    return t.contiguous().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("inverse", [0, 1])
+@pytest.mark.parametrize("name", list(CASES))
+def test_entropy_budget_trigger_matches_oracle(name, inverse):
+    w, L, D, s_orc = _case(name)
+    totals = _totals(w, L, 0.3)
+    scores, ent, bud, out = _one_call(D, w, L, totals, inverse)
+    assert_scores_close(scores.cpu().numpy(), s_orc)
+    g_ent, g_bud = ent.cpu().numpy(), bud.cpu().numpy()
+    lens, kept, cap = out["seg_len"].cpu().numpy(), out["kept"].cpu().numpy(), out["cap"]
+    k_in, v_in, p_in = _ints(D["k"]), _ints(D["v"]), D["pos"].cpu().numpy()
+    k_out, v_out, p_out = _ints(out["k"]), _ints(out["v"]), out["pos"].cpu().numpy()
+    H = w.n_kv_heads
+    for b in range(w.batch):
+        segs = list(range(b * H, (b + 1) * H))
+        n = np.array([int(L["seg_len"][s]) for s in segs])
+        E = np.array([oracle.normalized_entropy(s_orc[int(L["seg_off"][s]):int(L["seg_off"][s]) + n[i]])
+                      for i, s in enumerate(segs)])
+        assert np.all(np.abs(g_ent[segs] - E) <= 2e-3 * np.maximum(np.abs(E), 1e-3)), (g_ent[segs], E)
+        want = oracle.head_budgets(oracle.head_weights(E, bool(inverse)), n, int(totals[b]), FLOOR)
+        got = g_bud[segs]
+        assert got.sum() == want.sum() and np.all(got >= np.minimum(FLOOR, n)) and np.all(got <= n)
+        assert np.abs(got - want).max() <= 1, (got, want)   # a near-tie of remainders may move one token
+        for i, s in enumerate(segs):
+            K = int(got[i])
+            assert lens[s] == min(K, n[i]), (s, lens[s], K)
+            o = int(L["seg_off"][s])
+            ks = kept[s * cap:s * cap + lens[s]]
+            ok, _, msg = kept_matches(ks, s_orc[o:o + n[i]], int(n[i]), K, w.n_prefix, w.n_recent)
+            assert ok, f"segment {s}: {msg}"
+            rows = slice(s * cap, s * cap + lens[s])
+            assert np.array_equal(k_out[rows], k_in[o + ks]) and np.array_equal(v_out[rows], v_in[o + ks])
+            assert np.array_equal(p_out[rows], p_in[o + ks])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_entropy_budget_trigger_agrees_with_three_calls(name):
+    w, L, D, _ = _case(name)
+    totals = _totals(w, L, 0.2)
+    scores, ent, bud, out = _one_call(D, w, L, totals, 0)
+    s3, e3 = score_layer(D, w, entropy=True)
+    b3 = torch.zeros_like(bud)
+    kv.kv_evict_entropy_budgets(e3, 0, torch.from_numpy(totals).to("cuda"), D["seg_len"], w.batch, w.n_kv_heads,
+                                FLOOR, b3)
+    out3 = alloc_out(D, w, D["max_len"])
+    select_compact(D, w, s3, out3, budget=b3)
+    torch.cuda.synchronize()
+    e1, e2 = ent.cpu().numpy(), e3.cpu().numpy()
+    assert np.all(np.abs(e1 - e2) <= 1e-5 * np.maximum(np.abs(e2), 1e-3))
+    g1, g2 = bud.cpu().numpy(), b3.cpu().numpy()
+    H = w.n_kv_heads
+    for b in range(w.batch):
+        segs = slice(b * H, (b + 1) * H)
+        assert g1[segs].sum() == g2[segs].sum() and np.abs(g1[segs] - g2[segs]).max() <= 1
+    same = np.flatnonzero(g1 == g2)
+    assert len(same) >= len(g1) - 2 * w.batch
+    a, c = scores.cpu().numpy(), s3.cpu().numpy()
+    assert_scores_close(a, c, rtol=2e-5, what="one-call vs three-call scores")
+    cap = out["cap"]
+    k1, k2 = out["kept"].cpu().numpy(), out3["kept"].cpu().numpy()
+    l1, l2 = out["seg_len"].cpu().numpy(), out3["seg_len"].cpu().numpy()
+    for s in same:
+        assert l1[s] == l2[s]
+        if not np.array_equal(k1[s * cap:s * cap + l1[s]], k2[s * cap:s * cap + l2[s]]):
+            # only candidates tied within rounding may swap
+            o, n = int(L["seg_off"][s]), int(L["seg_len"][s])
+            ok, _, msg = kept_matches(k1[s * cap:s * cap + l1[s]], c[o:o + n].astype(np.float64), n, int(g1[s]),
+                                      w.n_prefix, w.n_recent, rtol=2e-5)
+            assert ok, msg
+
+
+def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(monkeypatch):
+    """A request-layer whose floors exceed its total gets -1 in every head
+    (as kv_evict_entropy_budgets); with the meeting poll bound forced to one
+    poll from the host, request-layers whose work-groups did not meet report
+    -1 and the others are exact; the default bound is whole again."""
+    w, L, D, s_orc = _case("llama-ragged")
+    totals = _totals(w, L, 0.3)
+    totals[1] = FLOOR * w.n_kv_heads - 5                      # below the floors
+    H = w.n_kv_heads
+
+    def check(allow_failed):
+        scores, ent, bud, out = _one_call(D, w, L, totals, 0)
+        lens, kept, cap = out["seg_len"].cpu().numpy(), out["kept"].cpu().numpy(), out["cap"]
+        g_bud = bud.cpu().numpy()
+        assert np.all(lens[H:2 * H] == -1)
+        if not allow_failed:
+            assert np.all(g_bud[H:2 * H] == -1)
+        for s in range(len(lens)):
+            if s // H == 1 or (allow_failed and lens[s] == -1):
+                continue
+            n, o = int(L["seg_len"][s]), int(L["seg_off"][s])
+            K = int(g_bud[s])
+            assert lens[s] == min(K, n)
+            ok, _, msg = kept_matches(kept[s * cap:s * cap + lens[s]], s_orc[o:o + n], n, K, w.n_prefix, w.n_recent)
+            assert ok, f"segment {s}: {msg}"
+
+    check(False)
+    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    check(True)
+    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    check(False)
