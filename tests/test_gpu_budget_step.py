@@ -69,9 +69,15 @@ def _ints(t):
     return t.contiguous().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
 
+@pytest.mark.parametrize("form", ["one-kernel", "three-call"])
 @pytest.mark.parametrize("inverse", [0, 1])
 @pytest.mark.parametrize("name", list(CASES))
-def test_entropy_budget_trigger_matches_oracle(name, inverse):
+def test_entropy_budget_trigger_matches_oracle(name, inverse, form, monkeypatch):
+    """form three-call: the entry point's own fallback (taken for fp32 caches,
+    long segments or many heads), forced here by selecting the single-read
+    scoring kernel."""
+    if form == "three-call":
+        monkeypatch.setenv("KVE_SCORE_IMPL", "fused")
     w, L, D, s_orc = _case(name)
     totals = _totals(w, L, 0.3)
     scores, ent, bud, out = _one_call(D, w, L, totals, inverse)
