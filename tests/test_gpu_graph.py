@@ -87,3 +87,80 @@ def test_captured_step_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager step"
         _step(layers, w, outs, scores, ws, side, fps_out)        # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("form", ["copy", "inplace", "budget"])
+def test_captured_one_call_triggers_replay_match_eager(form):
+    """The one-kernel triggers (work tickets and meeting counters cleared by a
+    kernel inside each call, so a graph holds no memset node) captured once and
+    replayed several times, with eager calls between the replays: every replay
+    reproduces the eager outputs bit for bit.  The in-place form rewrites the
+    cache, which is restored eagerly before every call."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = get_workload("r1-llama-8b").scaled(batch=3, len_lo=900, len_hi=1500, n_layers=1)
+    D = device_layer(make_layer(w, 0), w)
+    S = w.batch * w.n_kv_heads
+    cap = D["max_len"]
+    c = kv.make_cache(D["k"], D["v"], D["pos"], D["seg_off"], D["seg_len"], w.n_kv_heads, D["max_len"])
+    o = kv.make_obs(D["q_obs"], D["q_pos"], D["n_obs"], w.rope_theta)
+    pristine = [D[k].clone() for k in ("k", "v", "pos")]
+    scores = torch.zeros(D["k"].shape[0], device="cuda")
+    out = {"k": torch.zeros(S * cap, w.head_dim, dtype=torch.bfloat16, device="cuda"),
+           "v": torch.zeros(S * cap, w.head_dim, dtype=torch.bfloat16, device="cuda"),
+           "pos": torch.zeros(S * cap, dtype=torch.int32, device="cuda"),
+           "seg_off": torch.arange(S, dtype=torch.int64, device="cuda") * cap,
+           "seg_len": torch.zeros(S, dtype=torch.int32, device="cuda"),
+           "kept": torch.zeros(S * cap, dtype=torch.int32, device="cuda")}
+    co = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], w.n_kv_heads, cap)
+    ent = torch.zeros(S, device="cuda")
+    bud = torch.zeros(S, dtype=torch.int32, device="cuda")
+    new_len = torch.zeros(S, dtype=torch.int32, device="cuda")
+    totals = torch.full((w.batch,), 300 * w.n_kv_heads, dtype=torch.int32, device="cuda")
+    budget = 700
+    if form == "copy":
+        ws = torch.empty(kv.kv_evict_score_select_compact_workspace(c, o, co, True) + 256, dtype=torch.uint8,
+                         device="cuda")
+        call = lambda: kv.kv_evict_score_select_compact(c, o, scores, None, w.n_prefix, w.n_recent, co,  # noqa: E731
+                                                        kept_idx=out["kept"], uniform_budget=budget, ws=ws)
+        outputs = lambda: [scores, out["k"], out["v"], out["pos"], out["seg_len"], out["kept"]]  # noqa: E731
+    elif form == "inplace":
+        ws = torch.empty(kv.kv_evict_score_select_compact_inplace_workspace(c, o) + 256, dtype=torch.uint8,
+                         device="cuda")
+        call = lambda: kv.kv_evict_score_select_compact_inplace(c, o, scores, None, w.n_prefix, w.n_recent,  # noqa: E731
+                                                                new_len, uniform_budget=budget, ws=ws)
+        outputs = lambda: [scores, D["k"], D["v"], D["pos"], new_len]  # noqa: E731
+    else:
+        ws = torch.empty(kv.kv_evict_score_budget_select_compact_workspace(c, o, co, True, True) + 256,
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: kv.kv_evict_score_budget_select_compact(c, o, scores, ent, totals, 24, w.n_prefix,  # noqa: E731
+                                                               w.n_recent, co, budget_out=bud, kept_idx=out["kept"],
+                                                               ws=ws)
+        outputs = lambda: [scores, ent, bud, out["k"], out["v"], out["pos"], out["seg_len"], out["kept"]]  # noqa: E731
+
+    def reset():
+        for t, p in zip((D["k"], D["v"], D["pos"]), pristine):
+            t.copy_(p)
+        for t in (scores, ent, bud, new_len, *out.values()):
+            if t is not out["seg_off"]:
+                t.zero_()
+
+    reset()
+    call()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs()]
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outputs(), want)):
+            assert torch.equal(a, b), f"{form} replay {rep}: output {i} differs from the eager call"
+        reset()
+        call()                                                  # eager work between replays
+        torch.cuda.synchronize()
