@@ -735,7 +735,7 @@ __device__ __forceinline__ void group_arrive(const ScoreArgs& a, int* ctl, int s
 // exceed the request-layer's total (the segment then keeps -1).
 __device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s, int ch, float e, int tid) {
   __shared__ HeadBudgetLds L;
-  __shared__ int kb;
+  __shared__ int met, kb;                      // two words: kb is written while others may still read met
   const int H = a.n_kv, grp = s / H;
   int* cnt = ctl + kQueues + 3 * a.n_seg + grp;
   if (tid == 0) {
@@ -743,11 +743,11 @@ __device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s,
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < H && ++spins < a.spin_limit)
       __builtin_amdgcn_s_sleep(1);
-    kb = spins < a.spin_limit ? 0 : kNoBudget;
-    if (kb == kNoBudget) atomicAdd(cnt, -(1 << 24));
+    met = spins < a.spin_limit;
+    if (!met) atomicAdd(cnt, -(1 << 24));
   }
   __syncthreads();
-  if (kb == kNoBudget) return kNoBudget;
+  if (!met) return kNoBudget;
   if (tid < kWave) {
     const bool act = tid < H;
     const int hs = grp * H + tid;
