@@ -804,19 +804,17 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   }
   int64_t off;
   int n;
+  // a segment with nothing to score still takes part in its request-layer's
+  // budgets (entropy 0, its cap is its length) and gets its budget written
   if (!segment_ok(a, s, off, n)) {
-    if (MODE >= kModeStep && ch == 0 && tid == 0) {
-      a.out_len[s] = -1;
-      if (MODE == kModeBudget) group_arrive(a, ctl, s, 0.f);
-    }
+    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
+    if (MODE == kModeBudget && ch == 0) group_budget(a, ctl, s, 0, 0.f, tid);
     return;
   }
   const int k0 = ch * a.chunk;
   if (k0 >= n) {
-    if (MODE >= kModeStep && ch == 0 && tid == 0) {
-      a.out_len[s] = 0;                        // empty segment
-      if (MODE == kModeBudget) group_arrive(a, ctl, s, 0.f);
-    }
+    if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
+    if (MODE == kModeBudget && ch == 0) group_budget(a, ctl, s, 0, 0.f, tid);
     return;
   }
   const int k1 = min(n, k0 + a.chunk);

@@ -10,7 +10,7 @@ import torch
 import decode_kv_cache_evict_amd as kv
 import oracle
 from tests.gpu_side import alloc_out, cache_of, device_layer, obs_of, score_layer, select_compact
-from tests.oracle_side import oracle_cache_keys, oracle_layer_scores
+from tests.oracle_side import np64, oracle_cache_keys, oracle_layer_scores
 from tests.parity import assert_scores_close, kept_matches
 from workloads import get_workload, make_layer
 
@@ -176,3 +176,43 @@ def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(monkeypa
     check(True)
     monkeypatch.delenv("KVE_SPIN_LIMIT")
     check(False)
+
+
+def test_entropy_budget_trigger_degenerate_heads():
+    """A request-layer with an empty head and a head shorter than the
+    protected rows: the empty head gets budget 0 and length 0, the short one
+    keeps every row, and the other heads share the total as the oracle's
+    budgets (computed with the same lengths) say."""
+    w, L, D, s_full = _case("llama-ragged")
+    H = w.n_kv_heads
+    D2 = dict(D)
+    D2["seg_len"] = D["seg_len"].clone()
+    D2["seg_len"][1] = 0
+    D2["seg_len"][2] = 10
+    # the oracle's scores of the ten-row head (its own softmax over those rows)
+    k_orc = oracle_cache_keys(L, w)
+    o2 = int(L["seg_off"][2])
+    qp = L["q_pos"][0].cpu().numpy()
+    q = np64(L["q_obs"][0])
+    rows = [oracle.to_storage(oracle.rope(q[hh], qp, w.rope_theta), w.dtype)
+            for hh in range(2 * w.group, 3 * w.group)]
+    s2 = oracle.segment_scores(k_orc[o2:o2 + 10], L["pos"][o2:o2 + 10].cpu().numpy(), np.concatenate(rows),
+                               np.tile(qp, w.group))
+    totals = _totals(w, L, 0.3)
+    scores, ent, bud, out = _one_call(D2, w, L, totals, 0)
+    g_ent, g_bud = ent.cpu().numpy(), bud.cpu().numpy()
+    lens, kept, cap = out["seg_len"].cpu().numpy(), out["kept"].cpu().numpy(), out["cap"]
+    n = np.array([int(D2["seg_len"][s]) for s in range(H)])
+    seg_scores = [s_full[int(L["seg_off"][s]):int(L["seg_off"][s]) + n[s]] for s in range(H)]
+    seg_scores[2] = s2
+    E = np.array([oracle.normalized_entropy(x) if len(x) else 0.0 for x in seg_scores])
+    assert np.all(np.abs(g_ent[:H] - E) <= 2e-3 * np.maximum(np.abs(E), 1e-3)), (g_ent[:H], E)
+    want = oracle.head_budgets(oracle.head_weights(E, False), n, int(totals[0]), FLOOR)
+    assert g_bud[1] == 0 and g_bud[2] == 10 and want[1] == 0 and want[2] == 10
+    assert g_bud[:H].sum() == want.sum() and np.abs(g_bud[:H] - want).max() <= 1, (g_bud[:H], want)
+    assert lens[1] == 0 and lens[2] == 10
+    assert np.array_equal(kept[2 * cap:2 * cap + 10], np.arange(10))
+    for s in [0] + list(range(3, H)):
+        ok, _, msg = kept_matches(kept[s * cap:s * cap + lens[s]], seg_scores[s], int(n[s]), int(g_bud[s]),
+                                  w.n_prefix, w.n_recent)
+        assert ok, f"segment {s}: {msg}"
