@@ -806,21 +806,24 @@ def main():
         for i in range(args.warmup):
             graphs[i % len(states)].replay()
         torch.cuda.synchronize()
+    # HIP events on the launching stream bracket every launch of the dominant
+    # call inside the timed steps (a replayed graph cannot hold them: its
+    # launches are timed in eager steps of the same schedule afterwards)
+    timing_steps = args.steps if not graphs else min(args.steps, 8)
+    tev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runner.cgroups] for _ in range(timing_steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         if graphs:
             graphs[i % len(states)].replay()
         else:
-            runner.run(i)
+            runner.run(i, timing=tev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
-    # per-call durations of the dominant call (select + gather), live, same schedule, eager launches
-    timing_steps = min(args.steps, 8)
-    tev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runner.cgroups] for _ in range(timing_steps)]
-    for i in range(timing_steps):
-        runner.run(i, timing=tev[i])
-    torch.cuda.synchronize()
+    if graphs:
+        for i in range(timing_steps):
+            runner.run(i, timing=tev[i])
+        torch.cuda.synchronize()
     sc_ms = sum(t[0].elapsed_time(t[1]) for step in tev for t in step) / (timing_steps * len(runner.cgroups))
     tokens = w.n_layers * w.batch * w.len_hi
     nb = step_bytes(w, args.call)
