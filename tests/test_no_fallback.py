@@ -1,6 +1,7 @@
-"""The product path has no fallback: the package never imports the oracle,
-and with its HIP library missing every call fails loudly instead of
-computing anything on the CPU (no GPU needed)."""
+"""The product path has no fallback and shares no code with the oracle: the
+package never imports the oracle, the oracle imports nothing but numpy and
+the standard library, and with its HIP library missing every call fails
+loudly instead of computing anything on the CPU (no GPU needed)."""
 import ast
 import os
 import subprocess
@@ -20,6 +21,20 @@ def test_package_sources_do_not_reference_the_oracle():
                 assert not any(a.name.split(".")[0] == "oracle" for a in node.names), name
             if isinstance(node, ast.ImportFrom):
                 assert (node.module or "").split(".")[0] != "oracle", name
+
+
+def test_oracle_does_not_reference_the_package():
+    odir = os.path.join(ROOT, "oracle")
+    for name in sorted(os.listdir(odir)):
+        if not name.endswith(".py"):
+            continue
+        src = open(os.path.join(odir, name)).read()
+        tree = ast.parse(src)
+        mods = [a.name for n in ast.walk(tree) if isinstance(n, ast.Import) for a in n.names]
+        mods += [n.module or "" for n in ast.walk(tree) if isinstance(n, ast.ImportFrom)]
+        assert all(m.split(".")[0] in ("math", "numpy", "oracle", "") or m.startswith("kvevict_oracle")
+                   for m in mods), (name, mods)
+        assert "decode_kv_cache_evict_amd" not in src and "csrc" not in src, name
 
 
 def test_missing_library_raises():
