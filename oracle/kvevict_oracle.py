@@ -186,7 +186,11 @@ def waterfill(total, w, lo, hi):
     Mechanism": budget moves between heads, the layer total is kept).
     lo_g = min(lo, hi_g).  total >= sum(hi) gives hi; all-zero weights split
     equally.  Raises if total < sum(lo_g).  Solved exactly on the breakpoints
-    of the piecewise-linear sum."""
+    of the piecewise-linear sum.
+    READING (weightless heads, not on the page): a head of weight 0 keeps its
+    floor while some lam meets the total; once every weighted head is at its
+    cap, the rest of the total is split equally over the weightless heads
+    under their caps (the limit of equal tiny weights)."""
     w = np.asarray(w, dtype=np.float64)
     hi = np.asarray(hi, dtype=np.float64)
     lo_g = np.minimum(np.asarray(lo, dtype=np.float64) * np.ones_like(hi), hi)

@@ -42,6 +42,56 @@ def test_waterfill_hand_examples():
         waterfill(100, [1, 1], 64, [1000, 1000])
 
 
+def test_waterfill_weightless_heads_hand_examples():
+    """Heads of weight 0 stay at their floor while a common factor can still
+    meet the total; once every weighted head is at its cap, the rest of the
+    total is split equally over the weightless heads (the limit of equal tiny
+    weights).  ReasonAlloc, Core Mechanism: the layer total is kept."""
+    # weighted heads below their caps: the weightless head keeps its floor
+    assert np.allclose(waterfill(600, [0, 1, 1], 64, [1000, 1000, 1000]), [64, 268, 268])
+    assert np.allclose(waterfill(300, [0, 2, 1], 50, [1000, 1000, 1000]), [50, 500 / 3, 250 / 3])
+    # weighted heads capped: the weightless head takes what is left
+    assert np.allclose(waterfill(600, [0, 0.5, 0.5], 64, [1000, 100, 100]), [400, 100, 100])
+    # two weightless heads share the rest equally, one of them then capped
+    assert np.allclose(waterfill(700, [0, 0, 1], 64, [500, 300, 100]), [300, 300, 100])
+    assert np.allclose(waterfill(850, [0, 0, 1], 64, [500, 300, 100]), [450, 300, 100])
+    # the boundary between the two regimes: weighted heads exactly at their caps
+    assert np.allclose(waterfill(264, [0, 1, 1], 64, [1000, 100, 100]), [64, 100, 100])
+
+
+def test_waterfill_weightless_heads_match_bisection():
+    """Independent check of both regimes: bisection on the unmodified weights
+    where a common factor meets the total (total <= sum of the weighted heads'
+    caps + the weightless heads' floors), else bisection with every zero weight
+    replaced by the same tiny weight (the limit the oracle's equal split of the
+    rest stands for)."""
+    rng = np.random.default_rng(5)
+    n_split = 0
+    for _ in range(300):
+        G = int(rng.integers(2, 10))
+        w = rng.random(G) ** 2 + 0.05
+        zero = rng.random(G) < 0.4
+        zero[int(rng.integers(G))] = True
+        if zero.all():
+            zero[0] = False
+        w[zero] = 0.0
+        hi = rng.integers(80, 3000, G).astype(float)
+        lo = 64.0
+        lo_g = np.minimum(lo, hi)
+        total = float(rng.uniform(lo_g.sum(), hi.sum()))
+        x = waterfill(total, w, lo, hi)
+        assert abs(x.sum() - total) < 1e-6
+        if total <= hi[~zero].sum() + lo_g[zero].sum():
+            assert np.allclose(x, _bisect(total, w, lo, hi), rtol=1e-9, atol=1e-7)
+            assert np.allclose(x[zero], lo_g[zero])
+        else:
+            n_split += 1
+            eps = np.where(zero, 1e-12, w)
+            assert np.allclose(x, _bisect(total, eps, lo, hi), rtol=1e-7, atol=1e-5)
+            assert np.allclose(x[~zero], hi[~zero])
+    assert n_split > 20
+
+
 def test_waterfill_matches_bisection():
     rng = np.random.default_rng(0)
     for _ in range(300):
