@@ -55,3 +55,55 @@ def kept_matches(gpu_kept, orc_scores, n, budget, n_prefix, n_recent, rtol=RTOL,
         j = diff[~band][0]
         return False, len(diff), f"slot {j} (oracle score {s32[j]!r}) differs outside the band around {cut!r}"
     return True, len(diff) // 2, ""
+
+
+FRAC_TOL = 1e-3
+
+
+def _near_cut(x, total, tol):
+    """Heads whose largest-remainder rounding of the real shares x can flip:
+    those whose fractional part lies within tol of the cut, when the last
+    fraction rounded up and the first rounded down are within tol of each
+    other (otherwise no head: the rounding is decided)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = np.floor(x)
+    frac = x - f
+    r = int(round(total - f.sum()))
+    order = sorted(range(len(x)), key=lambda g: (-frac[g], g))
+    a = frac[order[r - 1]] if r > 0 else np.inf          # last rounded up
+    b = frac[order[r]] if r < len(x) else -np.inf        # first rounded down
+    if a - b > tol:
+        return np.zeros(len(x), dtype=bool)
+    return (frac >= b - tol) & (frac <= a + tol)
+
+
+def budgets_match(got, e_gpu, e_orc, seg_len, layer_total, floor, inverse=False, tol=FRAC_TOL):
+    """Check one request-layer's GPU head budgets (ReasonAlloc, Core Mechanism).
+
+    Invariants: the sum is min(total, sum of lengths), every head between
+    min(floor, n) and n.  Against the oracle's budget rule applied to the
+    GPU's own entropies: equal, except by one token at heads whose real
+    share's fractional part lies within tol of the largest-remainder cut.
+    Against the oracle's entropies end to end: the same, with the band widened
+    by the largest shift of any real share between the two entropy vectors.
+    Returns (ok, message)."""
+    got = np.asarray(got, dtype=np.int64)
+    n = np.asarray(seg_len, dtype=np.int64)
+    tot = min(int(layer_total), int(n.sum()))
+    if got.sum() != tot:
+        return False, f"sum {got.sum()} != {tot}"
+    if np.any(got < np.minimum(floor, n)) or np.any(got > n):
+        return False, f"a budget outside [min(floor, n), n]: {got.tolist()} for lengths {n.tolist()}"
+    x_g = oracle.waterfill(float(layer_total), oracle.head_weights(e_gpu, inverse), float(floor), n.astype(float))
+    x_o = oracle.waterfill(float(layer_total), oracle.head_weights(e_orc, inverse), float(floor), n.astype(float))
+    shift = float(np.abs(x_g - x_o).max())
+    for x, band, what in ((x_g, tol, "the GPU's entropies"), (x_o, tol + 2 * shift, "the oracle's entropies")):
+        want = oracle.largest_remainder(x, tot)
+        diff = got != want
+        if not diff.any():
+            continue
+        ok = _near_cut(x, tot, band)
+        if np.any(np.abs(got - want) > 1) or np.any(diff & ~ok):
+            return False, (f"budgets {got.tolist()} != {want.tolist()} from {what} (real shares {x.tolist()}) "
+                           f"outside the remainder band {band:g}")
+    return True, ""
