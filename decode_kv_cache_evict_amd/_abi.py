@@ -28,7 +28,7 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_score_budget_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
            "kv_decode_attention_workspace", "kv_decode_attention",
-           "kv_rope_apply", "kve_last_error", "kve_abi_version"]
+           "kv_rope_apply", "kve_set_test_overrides", "kve_last_error", "kve_abi_version"]
 
 
 class KveError(RuntimeError):
@@ -87,6 +87,7 @@ def lib():
             "kv_decode_attention_workspace": (SZ, [CP, I32]),
             "kv_decode_attention": (I32, [CP, P, I32, P, P, P, SZ, P]),
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
+            "kve_set_test_overrides": (I32, [I32, I32]),
             "kve_last_error": (ctypes.c_char_p, []),
             "kve_abi_version": (I32, []),
         }
@@ -333,3 +334,12 @@ def kv_rope_apply(src, dst, pos, rope_theta, stream=None):
 
 def kve_abi_version():
     return int(lib().kve_abi_version())
+
+
+SCORE_IMPLS = {"default": 0, "valu": 1, "fused": 2}
+
+
+def kve_set_test_overrides(score_impl="default", spin_limit=0):
+    """Test hook (process-wide): the scoring kernels to force ("default",
+    "valu" or "fused") and the meetings' poll bound (0 = the default)."""
+    _check(lib().kve_set_test_overrides(SCORE_IMPLS[score_impl], int(spin_limit)))

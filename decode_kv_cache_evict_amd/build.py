@@ -49,5 +49,49 @@ def build(verbose=False):
     return LIB
 
 
+SAN_LIB = os.path.join(LIBDIR, "libkvevict_san.so")
+# host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI layer
+# (argument checks, workspace carving, launch set-up); device code is built as usual
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized():
+    """libkvevict_san.so: api.cpp built with host ASan/UBSan, linked with the
+    kernel objects of the regular build (build() first).  Load it with the
+    compiler's ASan runtime preloaded (sanitizer_runtime())."""
+    objs = [os.path.join(LIBDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: {missing[0]} is missing")
+    obj = os.path.join(LIBDIR, "api_san.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    cmd = [HIPCC, *flags, *SAN_FLAGS, "-c", os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized api.cpp:\n{r.stderr}")
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libasan", *SAN_FLAGS[:4], obj, *objs,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def sanitizer_runtime():
+    """The compiler's shared ASan runtime (to preload into the Python process)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to hipcc")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())

@@ -2,6 +2,7 @@
 // launches.  Every check runs on the host before anything is launched.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -54,29 +55,21 @@ kve_status check_cache(const kve_cache* c, const char* name, bool need_v) {
   return KVE_OK;
 }
 
+// Process-wide overrides set by kve_set_test_overrides (0: the default).
+std::atomic<int32_t> g_score_impl{0}, g_spin_limit{0};
+
 // Polls a single-read work-group makes at a segment barrier before it reports
-// the segment failed; KVE_SPIN_LIMIT (a positive count) overrides the default
-// so that tests can drive the timeout path on purpose.
+// the segment failed (tests lower it to drive that path on purpose).
 int32_t spin_limit() {
-  const char* e = std::getenv("KVE_SPIN_LIMIT");
-  if (e) {
-    const long v = std::strtol(e, nullptr, 10);
-    if (v > 0 && v <= (1L << 30)) return int32_t(v);
-  }
-  return 1 << 22;
+  const int32_t v = g_spin_limit.load(std::memory_order_relaxed);
+  return v > 0 ? v : (1 << 22);
 }
 
 size_t rows_bytes(const kve_cache* c) { return size_t(c->n_rows) * c->head_dim * elem_bytes(c->dtype); }
 
 // Scoring implementation for bf16 caches: two MFMA passes (default), the
-// single-read MFMA kernel ("fused") or, for cross-checks, the plain VALU
-// kernels ("valu").
-int score_impl() {
-  const char* e = std::getenv("KVE_SCORE_IMPL");
-  if (e && std::strcmp(e, "valu") == 0) return 1;
-  if (e && std::strcmp(e, "fused") == 0) return 2;
-  return 0;
-}
+// single-read MFMA kernel (2) or, for cross-checks, the plain VALU kernels (1).
+int score_impl() { return g_score_impl.load(std::memory_order_relaxed); }
 
 size_t valu_lds(int rows, int D, int dtype) {
   return size_t(rows) * D * elem_bytes(dtype) + size_t(rows) * (4 * sizeof(float2) + sizeof(float) + sizeof(int));
@@ -137,6 +130,14 @@ size_t step_score_ws(const kve_cache* in, const kve_obs* o, int32_t rows) {
 extern "C" {
 
 const char* kve_last_error(void) { return g_err.c_str(); }
+
+kve_status kve_set_test_overrides(int32_t score_impl, int32_t spin_limit) {
+  if (score_impl < 0 || score_impl > 2) return fail(KVE_EINVAL, "score_impl %d not 0, 1 or 2", score_impl);
+  if (spin_limit < 0 || spin_limit > (1 << 30)) return fail(KVE_EINVAL, "spin_limit %d out of range", spin_limit);
+  g_score_impl.store(score_impl, std::memory_order_relaxed);
+  g_spin_limit.store(spin_limit, std::memory_order_relaxed);
+  return KVE_OK;
+}
 
 int32_t kve_abi_version(void) { return KVE_ABI_VERSION; }
 

@@ -14,8 +14,10 @@
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *     keeps no state and allocates no device memory; scratch comes from a
- *     caller-provided workspace whose size the *_workspace_size calls return.
+ *     keeps no state (apart from the test overrides of kve_set_test_overrides
+ *     and the per-thread error message) and allocates no device memory;
+ *     scratch comes from a caller-provided workspace whose size the
+ *     *_workspace_size calls return.
  *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL is the null stream).  No call synchronises.
  *   - Arguments are checked on the host BEFORE any launch; on an error status
@@ -122,7 +124,10 @@ kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, f
  * proportionally to weights[b*n_heads+g] with floor min_per_head and cap
  * cap[b*n_heads+g] (x_g = clamp(lam*w_g, min(floor,cap_g), cap_g), sum =
  * min(total, sum cap)), then round by largest remainder (ties to the lower
- * head).  All-zero weights split equally.  Computed in double precision.
+ * head).  All-zero weights split equally.  A head of weight 0 keeps its floor
+ * while some lam meets the total; once every weighted head is at its cap, the
+ * rest is split equally over the weightless heads (under their caps).
+ * Computed in double precision.
  * budget_out: [batch*n_heads] int32.  A request whose total is below the sum of
  * its floors gets -1 in every head.  Errors: EINVAL, ESHAPE (n_heads > 64), EDEVICE.
  */
@@ -402,6 +407,22 @@ kve_status kv_decode_attention(const kve_cache* c, const void* q, int32_t n_q_he
  */
 kve_status kv_rope_apply(const float* src, void* dst, const int32_t* pos, int64_t n_rows,
                          int32_t head_dim, double rope_theta, int32_t dtype, void* stream);
+
+/*
+ * kve_set_test_overrides — for the library's own tests, not for production
+ * callers: two process-wide overrides of internal choices, both 0 (off) when
+ * the library loads.  Every later call of any entry point, on any thread, sees
+ * the values set last; set them while no other thread is calling the library.
+ *   score_impl  0: default dispatch.  1: the plain VALU scoring kernels for
+ *               bf16 caches as well (a cross-check of the MFMA kernels).  2: the
+ *               single-read MFMA scoring kernel in kv_evict_score.  With 1 or 2
+ *               the one-call entry points run their multi-call forms.
+ *   spin_limit  0: the default poll bound of the work-group meetings (about
+ *               four million polls).  > 0: that many polls, so that a test can
+ *               make the meetings give up and check the failure reporting.
+ * Errors: EINVAL (score_impl not 0..2, spin_limit outside [0, 2^30]).
+ */
+kve_status kve_set_test_overrides(int32_t score_impl, int32_t spin_limit);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* kve_last_error(void);

@@ -91,3 +91,12 @@ def test_host_validation_without_gpu():
     outs = kv.KveCache(**{f: getattr(outb, f) for f, _ in kv.KveCache._fields_})
     outs.max_seg_len = 63
     assert _fail(L.kv_evict_score_budget_select_compact, *args(0, 0x8800, outs))[0] == 4
+
+
+def test_test_overrides_validate_and_reset():
+    L = kv.lib()
+    assert _fail(L.kve_set_test_overrides, 3, 0)[0] == 1
+    assert _fail(L.kve_set_test_overrides, 0, -1)[0] == 1
+    assert _fail(L.kve_set_test_overrides, 0, (1 << 30) + 1)[0] == 1
+    assert L.kve_set_test_overrides(2, 5) == 0
+    assert L.kve_set_test_overrides(0, 0) == 0

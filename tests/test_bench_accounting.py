@@ -26,6 +26,19 @@ def test_benchmark_workload_bytes():
     assert bench.step_bytes(w, "inplace")["total"] < b["total"]
 
 
+def test_benchmark_definition_bytes():
+    """The benchmark definition's accounting of one trigger: K read once for
+    scoring (4.832 GB), queries (0.227 GB), scores written and read (0.151 GB),
+    kept K/V read and written (16.911 GB), kept positions read and written
+    (0.132 GB), FPS buffers (0.227 GB): 22.48 GB, 4.01 ms at 70 % of 8 TB/s."""
+    w = get_workload("qwen3-4b-36l")
+    b = bench.step_bytes(w, "fused")
+    S, n, keep, row = 36 * 16 * 8, 4096, 3584, 256
+    assert b["compact_kv"] == 4 * S * keep * row == 16_911_433_728
+    assert abs(b["survey_step"] - 22.48e9) < 0.01e9
+    assert abs(b["survey_step"] / (0.7 * 8e12) * 1e3 - 4.01) < 0.01
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)

@@ -72,12 +72,12 @@ def _ints(t):
 @pytest.mark.parametrize("form", ["one-kernel", "three-call"])
 @pytest.mark.parametrize("inverse", [0, 1])
 @pytest.mark.parametrize("name", list(CASES))
-def test_entropy_budget_trigger_matches_oracle(name, inverse, form, monkeypatch):
+def test_entropy_budget_trigger_matches_oracle(name, inverse, form, kve_overrides):
     """form three-call: the entry point's own fallback (taken for fp32 caches,
     long segments or many heads), forced here by selecting the single-read
     scoring kernel."""
     if form == "three-call":
-        monkeypatch.setenv("KVE_SCORE_IMPL", "fused")
+        kve_overrides(score_impl="fused")
     w, L, D, s_orc = _case(name)
     totals = _totals(w, L, 0.3)
     scores, ent, bud, out = _one_call(D, w, L, totals, inverse)
@@ -148,7 +148,7 @@ def test_entropy_budget_trigger_agrees_with_three_calls(name):
             assert ok, msg
 
 
-def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(monkeypatch):
+def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(kve_overrides):
     """A request-layer whose floors exceed its total gets -1 in every head
     (as kv_evict_entropy_budgets); with the meeting poll bound forced to one
     poll from the host, request-layers whose work-groups did not meet report
@@ -175,9 +175,9 @@ def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(monkeypa
             assert ok, f"segment {s}: {msg}"
 
     check(False)
-    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    kve_overrides(spin_limit=1)
     check(True)
-    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    kve_overrides(spin_limit=0)
     check(False)
 
 

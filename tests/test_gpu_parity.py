@@ -57,12 +57,12 @@ def test_rope_keys_bit_exact(name):
 
 @pytest.mark.parametrize("impl", ["mfma", "fused", "valu"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_scores_match_oracle(name, impl, monkeypatch):
+def test_scores_match_oracle(name, impl, kve_overrides):
     w, L, D, k_orc, s_orc = _case(name)
     if impl != "mfma":
         if w.dtype != "bf16":
             pytest.skip("fp32 caches always use the VALU path")
-        monkeypatch.setenv("KVE_SCORE_IMPL", impl)
+        kve_overrides(score_impl=impl)
     scores, ent = score_layer(D, w, entropy=True)
     torch.cuda.synchronize()
     g = scores.cpu().numpy()
@@ -76,7 +76,7 @@ def test_scores_match_oracle(name, impl, monkeypatch):
         assert abs(e[s] - want) <= 2e-3 * max(abs(want), 1e-3), (s, e[s], want)
 
 
-def test_single_read_scoring_long_segments(monkeypatch):
+def test_single_read_scoring_long_segments(kve_overrides):
     """The single-read scoring kernel on segments of 32,768 keys: its
     work-groups meet at a per-segment barrier, so each segment is cut into at
     most 12 chunks (with the two-pass chunk it would span 128, enough waiting
@@ -88,7 +88,7 @@ def test_single_read_scoring_long_segments(monkeypatch):
     D = device_layer(L, w)
     k_orc = oracle_cache_keys(L, w)
     s_orc = oracle_layer_scores(L, w, k_orc)
-    monkeypatch.setenv("KVE_SCORE_IMPL", "fused")
+    kve_overrides(score_impl="fused")
     scores, _ = score_layer(D, w, entropy=False)
     torch.cuda.synchronize()
     g = scores.cpu().numpy()
@@ -251,7 +251,7 @@ def _check_split(lens, offs, budgets, scores, out, cap, allow_failed):
         assert np.array_equal(pos[s * cap:s * cap + len(want)], o + want), s
 
 
-def test_select_split_budgets_and_failed_meetings(monkeypatch):
+def test_select_split_budgets_and_failed_meetings(kve_overrides):
     """The several-work-groups-per-segment selection with per-segment budgets
     over ragged segments (long and short, budgets keeping everything, a
     rejected one) matches the oracle; with the meeting poll bound forced to
@@ -262,12 +262,12 @@ def test_select_split_budgets_and_failed_meetings(monkeypatch):
     kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
     torch.cuda.synchronize()
     _check_split(lens, offs, budgets, scores, out, cap, allow_failed=False)
-    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    kve_overrides(spin_limit=1)
     out["len"].fill_(-9)
     kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
     torch.cuda.synchronize()
     _check_split(lens, offs, budgets, scores, out, cap, allow_failed=True)
-    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    kve_overrides(spin_limit=0)
     out["len"].fill_(-9)
     kv.kv_evict_select_compact(cin, sc, bud, 4, 16, cout, kept_idx=out["kept"])
     torch.cuda.synchronize()

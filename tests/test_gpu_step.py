@@ -209,8 +209,8 @@ def test_one_call_rejects_bad_arguments_before_launch():
     assert torch.all(out["seg_len"] == -9)   # nothing ran
 
 
-def test_forced_valu_scorer_takes_the_two_call_path(monkeypatch):
-    monkeypatch.setenv("KVE_SCORE_IMPL", "valu")
+def test_forced_valu_scorer_takes_the_two_call_path(kve_overrides):
+    kve_overrides(score_impl="valu")
     w, budget, L, D, s_orc = _case("qwen-short")
     out = alloc_out(D, w, budget)
     scores = score_select_compact(D, w, out, uniform=budget)
@@ -219,14 +219,14 @@ def test_forced_valu_scorer_takes_the_two_call_path(monkeypatch):
     _check_segments(w, L, D, out, s_orc, [budget] * len(L["seg_len"]))
 
 
-def test_barrier_timeout_reports_failed_segments(monkeypatch):
+def test_barrier_timeout_reports_failed_segments(kve_overrides):
     """With the segment barrier's poll bound forced down to one poll (the
     failure handling path, driven from the host), a segment whose work-groups
     do not all arrive at once is reported failed (seg_len -1) rather than
     selected from partial row statistics; every kernel exits, and a segment
     that did meet is exact.  A later call with the default bound is whole."""
     w, budget, L, D, s_orc = _case("llama-ragged")
-    monkeypatch.setenv("KVE_SPIN_LIMIT", "1")
+    kve_overrides(spin_limit=1)
     out = alloc_out(D, w, budget)
     score_select_compact(D, w, out, uniform=budget)
     torch.cuda.synchronize()
@@ -243,7 +243,7 @@ def test_barrier_timeout_reports_failed_segments(monkeypatch):
         ok, _, msg = kept_matches(ks, s_orc[o:o + n], n, budget, w.n_prefix, w.n_recent)
         assert ok, f"segment {s}: {msg}"
         assert np.array_equal(k_out[s * cap:s * cap + lens[s]], k_in[o + ks])
-    monkeypatch.delenv("KVE_SPIN_LIMIT")
+    kve_overrides(spin_limit=0)
     out2 = alloc_out(D, w, budget)
     score_select_compact(D, w, out2, uniform=budget)
     torch.cuda.synchronize()

@@ -46,12 +46,12 @@ def _case(name):
 
 @pytest.mark.parametrize("impl", ["mfma", "fused", "valu"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_mean_aggregation_scores_and_entropy(name, impl, monkeypatch):
+def test_mean_aggregation_scores_and_entropy(name, impl, kve_overrides):
     w, L, D, _, s_orc = _case(name)
     if impl != "mfma":
         if w.dtype != "bf16":
             pytest.skip("fp32 caches always use the VALU path")
-        monkeypatch.setenv("KVE_SCORE_IMPL", impl)
+        kve_overrides(score_impl=impl)
     scores, ent = score_layer(D, w, entropy=True, aggregate=kv.KVE_AGG_MEAN)
     torch.cuda.synchronize()
     assert_scores_close(scores.cpu().numpy(), s_orc, what=f"{name}/{impl} mean scores")
