@@ -8,7 +8,8 @@ from ._abi import (  # noqa: F401
     kv_evict_score_workspace, kv_evict_score, kv_evict_budgets, kv_evict_entropy_budgets, kv_evict_wave_budgets,
     kv_evict_select_workspace, kv_evict_select_compact, kv_evict_select_compact_inplace,
     kv_evict_score_select_compact_workspace,
-    kv_evict_score_select_compact, kv_evict_score_select_compact_inplace_workspace,
+    kv_evict_score_select_compact, kv_evict_score_select_compact_noalloc,
+    kv_evict_score_select_compact_inplace_workspace,
     kv_evict_score_select_compact_inplace, kv_evict_score_budget_select_compact_workspace,
     kv_evict_score_budget_select_compact, beacon_fps_update,
     epikv_workspace_size, epikv_score, skipkv_workspace_size, skipkv_sentence_scores, kv_decode_attention_workspace, kv_decode_attention, kv_rope_apply,

@@ -23,7 +23,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_wave_budgets",
            "kv_evict_select_workspace", "kv_evict_select_compact", "kv_evict_select_compact_inplace",
            "kv_evict_score_select_compact_workspace",
-           "kv_evict_score_select_compact", "kv_evict_score_select_compact_inplace_workspace",
+           "kv_evict_score_select_compact", "kv_evict_score_select_compact_noalloc",
+           "kv_evict_score_select_compact_inplace_workspace",
            "kv_evict_score_select_compact_inplace", "kv_evict_score_budget_select_compact_workspace",
            "kv_evict_score_budget_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
@@ -75,6 +76,7 @@ def lib():
             "kv_evict_select_compact_inplace": (I32, [CP, P, P, I64, P, I32, I32, I32, P, P]),
             "kv_evict_score_select_compact_workspace": (SZ, [CP, OP, CP, I32]),
             "kv_evict_score_select_compact": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P, SZ, P]),
+            "kv_evict_score_select_compact_noalloc": (I32, [CP, OP, P, P, I32, I32, I32, P, CP, P]),
             "kv_evict_score_select_compact_inplace_workspace": (SZ, [CP, OP]),
             "kv_evict_score_select_compact_inplace": (I32, [CP, OP, P, P, I32, I32, I32, P, P, SZ, P]),
             "kv_evict_score_budget_select_compact_workspace": (SZ, [CP, OP, CP, I32, I32]),
@@ -234,6 +236,15 @@ def kv_evict_score_select_compact(cache_in, obs, scores, budget, n_prefix, n_rec
     _check(lib().kv_evict_score_select_compact(ctypes.byref(cache_in), ctypes.byref(obs), _ptr(scores), _ptr(budget),
                                                int(uniform_budget), int(n_prefix), int(n_recent), _ptr(kept_idx),
                                                ctypes.byref(cache_out), wp, wn, _stream(stream)))
+
+
+def kv_evict_score_select_compact_noalloc(cache_in, obs, scores, budget, n_prefix, n_recent, cache_out, kept_idx=None,
+                                          uniform_budget=0, stream=None):
+    """kv_evict_score_select_compact with the library's static scratch in place of a workspace."""
+    _check(lib().kv_evict_score_select_compact_noalloc(ctypes.byref(cache_in), ctypes.byref(obs), _ptr(scores),
+                                                       _ptr(budget), int(uniform_budget), int(n_prefix),
+                                                       int(n_recent), _ptr(kept_idx), ctypes.byref(cache_out),
+                                                       _stream(stream)))
 
 
 def kv_evict_score_select_compact_inplace_workspace(cache, obs):

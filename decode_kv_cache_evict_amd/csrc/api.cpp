@@ -529,6 +529,25 @@ kve_status kv_evict_score_budget_select_compact(const kve_cache* in, const kve_o
                        "kv_evict_score_budget_select_compact");
 }
 
+kve_status kv_evict_score_select_compact_noalloc(const kve_cache* in, const kve_obs* o, float* scores,
+                                                 const int32_t* budget, int32_t uniform_budget, int32_t n_prefix,
+                                                 int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* stream) {
+  // the scratch size this call needs, from the same checks as the workspace query
+  int32_t rows = 0;
+  kve_status st = check_cache(in, "in", true);
+  if (st != KVE_OK) return st;
+  if ((st = check_obs(in, o, &rows)) != KVE_OK) return st;
+  if (!out) return fail(KVE_EINVAL, "out: null cache");
+  const size_t need = kv_evict_score_select_compact_workspace(in, o, out, kept_idx ? 1 : 0);
+  if (need > kve::kNoAllocScratchBytes)
+    return fail(KVE_EWORKSPACE, "needs %zu bytes of scratch, more than the static %zu", need,
+                kve::kNoAllocScratchBytes);
+  void* p = nullptr;
+  if ((st = device_status(kve::noalloc_scratch(&p), "static scratch address")) != KVE_OK) return st;
+  return kv_evict_score_select_compact(in, o, scores, budget, uniform_budget, n_prefix, n_recent, kept_idx, out, p,
+                                       kve::kNoAllocScratchBytes, stream);
+}
+
 size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const kve_obs* o) {
   int32_t rows = 0;
   if (check_cache(c, "cache", true) != KVE_OK || check_obs(c, o, &rows) != KVE_OK) return 0;

@@ -54,6 +54,10 @@ struct ScoreArgs {
 // two 64-key tiles of padded bf16 rows (64 * (D + 8) 32-bit words).
 constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 8); }
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
+// Static device scratch of kv_evict_score_select_compact_noalloc: its size,
+// and its address on the current device (taken once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // The one-kernel trigger with entropy budgets applies when every
 // request-layer's work-groups fit the dispatch bound of its barrier.
 bool budget_step_fits(int32_t n_seg, int32_t n_kv, int32_t max_seg_len, int32_t head_dim);

@@ -9,6 +9,7 @@
 // key tiles staged through LDS by coalesced 16-byte loads; a plain VALU path
 // serves fp32 caches.
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "budget_common.h"
@@ -1335,6 +1336,35 @@ hipError_t launch_score_budget_select_compact(ScoreArgs& a, void* ws, hipStream_
   if (e != hipSuccess) return e;
   if (a.n_chunks == 0 || a.n_seg == 0) return hipSuccess;
   return a.head_dim == 128 ? launch_step<128>(a, ctl, st) : launch_step<64>(a, ctl, st);
+}
+
+// Scratch of the entry point that allocates nothing: a file-scope device
+// array (each device holds its own copy from the code object's load until the
+// process ends).  Host code must not use the array's name as an address: its
+// device address is taken once per device, with that device current, and
+// kept here.
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return *ptr ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st) {

@@ -243,6 +243,27 @@ kve_status kv_evict_score_select_compact(const kve_cache* in, const kve_obs* o, 
                                          int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* ws,
                                          size_t ws_bytes, void* stream);
 
+/*
+ * kv_evict_score_select_compact_noalloc — for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): kv_evict_score_select_compact with the same
+ * arguments and results, minus the workspace, which comes instead from a
+ * static device array of 32 MiB that every GPU the library runs on holds until
+ * the process ends.  It calls no allocating routine.  Calls on one GPU share
+ * that array: two such calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and give undefined results;
+ * calls ordered on one stream do not.  What must start at zero is cleared by
+ * each call.  A call whose workspace (kv_evict_score_select_compact_workspace
+ * with have_kept_idx = kept_idx != NULL) exceeds 32 MiB is rejected
+ * (EWORKSPACE) before anything is launched: a Qwen3-4B-shaped layer of 16
+ * requests needs about 10 MB, so one call covers up to three such layers.
+ * Errors: those of kv_evict_score_select_compact, EWORKSPACE when the scratch
+ * is too small.
+ */
+kve_status kv_evict_score_select_compact_noalloc(const kve_cache* in, const kve_obs* o, float* scores,
+                                                 const int32_t* budget, int32_t uniform_budget, int32_t n_prefix,
+                                                 int32_t n_recent, int32_t* kept_idx, kve_cache* out, void* stream);
+
 /* Workspace bytes kv_evict_score_select_compact_inplace needs. */
 size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const kve_obs* o);
 
