@@ -203,6 +203,12 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
  * they were.  The survivors are therefore not in slot order; attention does
  * not depend on the order of the cached rows (BeaconKV "📊 实验": eviction is
  * permanent; each row keeps its position, which carries RoPE and causality).
+ * Protection is by slot, as in kv_evict_select_compact: once a segment has been
+ * hole-filled its slot order no longer follows position, so a later call
+ * protects the n_recent most recent tokens only if at least n_recent tokens
+ * were appended at the end of the segment since the hole filling (with fewer,
+ * the protected window also covers the last slots of the hole-filled rows,
+ * whatever their positions).
  * new_len: [n_seg] int32, receives K (n when K >= n, -1 for a segment rejected
  * as in kv_evict_select_compact); it may be c->seg_len itself.  No workspace.
  * Errors: EINVAL, ESHAPE, EALIAS (scores/budget/score_off/seg_off overlapping the

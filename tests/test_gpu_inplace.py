@@ -12,7 +12,7 @@ import torch
 import decode_kv_cache_evict_amd as kv
 import oracle
 from tests.gpu_side import cache_of, device_layer, obs_of, score_layer
-from tests.oracle_side import oracle_cache_keys, oracle_layer_scores
+from tests.oracle_side import np64, oracle_cache_keys, oracle_layer_scores
 from tests.parity import kept_matches
 from workloads import get_workload, make_layer
 
@@ -154,3 +154,88 @@ def test_one_call_inplace_rejects_bad_arguments():
     assert ei.value.name == "KVE_EALIAS"
     torch.cuda.synchronize()
     assert torch.all(nl == -9)                                        # nothing ran
+
+
+def test_chained_inplace_triggers_protect_by_slot():
+    """Two in-place one-call triggers with fewer appended tokens than the
+    protected recent window in between.  After hole filling, slot order no
+    longer follows position, and the next trigger protects its last n_recent
+    slots (BeaconKV's protected recent span, read by slot): with A < n_recent
+    appended tokens that window holds the A new tokens and the last
+    n_recent - A slots of the hole-filled region, whatever their positions.
+    The GPU's second trigger equals the oracle's selection by slot on the
+    oracle's own layout (scores within 2e-3, kept sets up to the tie band), and
+    it keeps exactly those protected slots."""
+    from workloads import make_append
+    w, K = get_workload("qwen3-4b-1l").scaled(batch=2), 1792
+    A = 8
+    assert A < w.n_recent
+    L = make_layer(w, 0)
+    D = device_layer(L, w)
+    n = int(L["lengths"][0])
+    # trigger 1 on the GPU (in place, one call)
+    C = dict(D, k=D["k"].clone(), v=D["v"].clone(), pos=D["pos"].clone(), seg_len=D["seg_len"].clone())
+    sc1 = torch.empty(C["k"].shape[0], dtype=torch.float32, device="cuda")
+    kv.kv_evict_score_select_compact_inplace(cache_of(C, w), obs_of(C, w), sc1, None, w.n_prefix, w.n_recent,
+                                             C["seg_len"], uniform_budget=K)
+    torch.cuda.synchronize()
+    assert torch.all(C["seg_len"] == K)
+    # append A tokens at slots K .. K+A-1 (positions n .. n+A-1), queries moved to step n + A
+    full = make_append(w.scaled(append=w.n_recent_q), 0, 1, [n] * w.batch)   # the first A of its tokens
+    ap = {k: full[k][:, :, :A].contiguous() for k in ("k_pre", "v", "pos")}
+    S = w.batch * w.n_kv_heads
+    new_k = torch.empty(S * A, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    kv.kv_rope_apply(ap["k_pre"].reshape(-1, w.head_dim).contiguous().cuda(), new_k,
+                     ap["pos"].reshape(-1).contiguous().cuda(), w.rope_theta)
+    rows = (torch.arange(S, device="cuda") * n).view(S, 1) + K + torch.arange(A, device="cuda").view(1, A)
+    C["k"][rows.view(-1)] = new_k
+    C["v"][rows.view(-1)] = ap["v"].reshape(-1, w.head_dim).cuda()
+    C["pos"][rows.view(-1)] = ap["pos"].reshape(-1).cuda()
+    C["seg_len"].fill_(K + A)
+    t2 = n + A
+    C["q_pos"] = torch.cat([torch.arange(t2 - w.n_recent_q, t2, dtype=torch.int32).expand(w.batch, -1),
+                            torch.full((w.batch, w.n_beacon), t2, dtype=torch.int32)], 1).contiguous().cuda()
+    k_before = C["k"].clone()
+    pos_before = C["pos"].cpu().numpy()
+    sc2 = torch.empty(C["k"].shape[0], dtype=torch.float32, device="cuda")
+    new_len = torch.full_like(C["seg_len"], -9)
+    kv.kv_evict_score_select_compact_inplace(cache_of(C, w), obs_of(C, w), sc2, None, w.n_prefix, w.n_recent,
+                                             new_len, uniform_budget=K)
+    torch.cuda.synchronize()
+    assert torch.all(new_len == K)
+    # the oracle's own chain for each segment
+    k_orc = oracle_cache_keys(L, w)
+    s1 = oracle_layer_scores(L, w, k_orc)
+    qp2 = C["q_pos"].cpu().numpy()
+    pos_after = C["pos"].cpu().numpy()
+    k_now, k_prev = _ints(C["k"]), _ints(k_before)
+    checked = 0
+    for s in range(S):
+        b, g = divmod(s, w.n_kv_heads)
+        o = int(L["seg_off"][s])
+        kept1 = oracle.select_kept(s1[o:o + n], n, K, w.n_prefix, w.n_recent)
+        src = oracle.hole_fill(kept1, n)
+        lay_pos = np.concatenate([np.arange(n)[src], ap["pos"][b, g].numpy()])   # trigger-1 positions are the slots
+        if not np.array_equal(pos_before[s * n:s * n + K + A], lay_pos):
+            continue                                   # trigger 1 resolved a near-tie the other way
+        kn = oracle.to_storage(oracle.rope(np64(ap["k_pre"][b, g]), ap["pos"][b, g].numpy(), w.rope_theta), w.dtype)
+        lay_k = np.concatenate([k_orc[o:o + n][src], kn])
+        q = np64(L["q_obs"][b])
+        qrows = [oracle.to_storage(oracle.rope(q[h], qp2[b], w.rope_theta), w.dtype)
+                 for h in range(g * w.group, (g + 1) * w.group)]
+        s2 = oracle.segment_scores(lay_k, lay_pos, np.concatenate(qrows), np.tile(qp2[b], w.group))
+        got2 = sc2[s * n:s * n + K + A].cpu().numpy()
+        assert np.all(np.abs(got2 - s2) <= np.maximum(2e-3 * np.abs(s2), 1e-30)), f"segment {s}: scores"
+        # the GPU's kept slots of trigger 2, from where each kept position sat before it
+        at = {int(p): j for j, p in enumerate(pos_before[s * n:s * n + K + A])}
+        kept2 = np.sort([at[int(p)] for p in pos_after[s * n:s * n + K]])
+        ok, _, msg = kept_matches(kept2, s2, K + A, K, w.n_prefix, w.n_recent)
+        assert ok, f"segment {s}: {msg}"
+        prot = np.arange(K + A - w.n_recent, K + A)
+        assert np.all(np.isin(prot, kept2)), f"segment {s}: a protected slot was evicted"
+        # the protected window reaches back into the hole-filled region
+        assert np.any(lay_pos[prot] < n)
+        assert np.array_equal(oracle.hole_fill(kept2, K + A), np.array([at[int(p)] for p in pos_after[s * n:s * n + K]]))
+        assert np.array_equal(k_now[s * n:s * n + K], k_prev[s * n + np.array([at[int(p)] for p in pos_after[s * n:s * n + K]])])
+        checked += 1
+    assert checked >= S - 2, f"only {checked} of {S} segments checked"
