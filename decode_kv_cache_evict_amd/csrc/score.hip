@@ -9,6 +9,7 @@
 // key tiles staged through LDS by coalesced 16-byte loads; a plain VALU path
 // serves fp32 caches.
 #include <climits>
+#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 
@@ -1180,13 +1181,26 @@ hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Keys per MFMA work-group of the two scoring passes: 1024, halved (down to
-// 256) while the launch would have fewer than 2048 work-groups, so that small
-// batches still fill the chip.
+// Keys per MFMA work-group of the two scoring passes: the multiple of 64 in
+// [256, 2048] with the shortest expected launch, counted as rounds of
+// resident work-groups (three per CU) times the keys a work-group scores plus
+// a fixed cost of about 96 keys' worth (query load, statistics); ties go to
+// the length nearest 1024.  This keeps the last round of a launch from
+// running mostly empty (65,536-key segments, 32 of them: 1408 keys, two full
+// rounds, instead of 1024 keys, 2.7 rounds).
 int mfma_chunk(int n_seg, int max_seg_len) {
-  int c = kMfmaChunk;
-  while (c > 256 && int64_t(n_seg) * ((max_seg_len + c - 1) / c) < 2048) c >>= 1;
-  return c;
+  constexpr int64_t kResident = 3 * 256, kOverhead = 96;
+  int best = kMfmaChunk;
+  int64_t best_cost = INT64_MAX;
+  for (int c = 256; c <= 2048; c += 64) {
+    const int64_t wgs = int64_t(n_seg) * ((max_seg_len + c - 1) / c);
+    const int64_t cost = (wgs + kResident - 1) / kResident * (c + kOverhead);
+    if (cost < best_cost || (cost == best_cost && std::abs(c - kMfmaChunk) < std::abs(best - kMfmaChunk))) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // The single-read scoring kernel: the two-pass chunk, lengthened (in 64-key
