@@ -1,10 +1,9 @@
 """Float64 CPU oracle of the eviction step (test infrastructure only).
 
 Every function takes and returns numpy arrays.  Floating point is float64
-throughout; where a floating-point value decides an integer (the top-K cut,
-the FPS argmax) the decision is taken on the value rounded to float32, the
-precision the GPU kernels decide in.  Stored tensors (bf16 / fp32) enter as
-their exact values widened to float64.
+throughout, including where a value decides an integer (the top-K cut, the
+FPS argmax).  Stored tensors (bf16 / fp32) enter as their exact values
+widened to float64.
 
 Readings of points the pages leave open are marked READING and collected in
 the design notes of the repository.
@@ -281,16 +280,16 @@ def select_kept(scores, n, budget, n_prefix, n_recent):
 
     BeaconKV, "打分时的 RoPE 对齐": the prefix and a short recent span are
     always kept, the rest of the budget goes to the highest scores.  Ranking is
-    by (score descending, slot ascending) on the score rounded to float32."""
+    by (score descending, slot ascending)."""
     n = int(n)
     budget = int(budget)
     if budget >= n:
         return np.arange(n)
     if budget < n_prefix + n_recent:
         raise ValueError("budget below the protected prefix + recent window")
-    s32 = np.asarray(scores[:n], dtype=np.float64).astype(np.float32)
+    s = np.asarray(scores[:n], dtype=np.float64)
     cand = np.arange(n_prefix, n - n_recent)
-    order = np.lexsort((cand, -s32[cand].astype(np.float64)))
+    order = np.lexsort((cand, -s[cand]))
     chosen = cand[order[: budget - n_prefix - n_recent]]
     kept = np.concatenate([np.arange(n_prefix), chosen, np.arange(n - n_recent, n)])
     return np.sort(kept)
@@ -349,21 +348,20 @@ def fps(X, k):
     to B_Q^max it is shrunk to B_Q^min by FPS in the cosine geometry of
     pre-RoPE queries.  READING: the first pick is row 0 (oldest); each step
     takes the unpicked row farthest from the picked set, ties to the lower
-    row.  Distances are formed in float64 and compared as float32.
-    Returns the picks in selection order."""
+    row.  Returns the picks in selection order."""
     U = _unit_rows(X)
     m = U.shape[0]
     k = min(int(k), m)
     picks = [0]
-    dist = (1.0 - U @ U[0]).astype(np.float32)
+    dist = 1.0 - U @ U[0]
     taken = np.zeros(m, dtype=bool)
     taken[0] = True
     for _ in range(k - 1):
-        cand = np.where(taken, -np.inf, dist.astype(np.float64))
+        cand = np.where(taken, -np.inf, dist)
         j = int(np.argmax(cand))
         picks.append(j)
         taken[j] = True
-        dist = np.minimum(dist, (1.0 - U @ U[j]).astype(np.float32))
+        dist = np.minimum(dist, 1.0 - U @ U[j])
     return np.array(picks, dtype=np.int64)
 
 

@@ -43,17 +43,17 @@ def kept_matches(gpu_kept, orc_scores, n, budget, n_prefix, n_recent, rtol=RTOL,
         return False, 0, "kept slots not strictly ascending"
     if np.array_equal(gpu_kept, want):
         return True, 0, ""
-    s32 = np.asarray(orc_scores[:n], dtype=np.float64).astype(np.float32).astype(np.float64)
+    s64 = np.asarray(orc_scores[:n], dtype=np.float64)
     cand = np.arange(n_prefix, n - n_recent)
     chosen = np.setdiff1d(want, np.concatenate([np.arange(n_prefix), np.arange(n - n_recent, n)]))
-    cut = s32[chosen].min()
+    cut = s64[chosen].min()
     diff = np.setxor1d(gpu_kept, want)
     if not np.all(np.isin(diff, cand)):
         return False, len(diff), "a protected slot differs"
-    band = np.abs(s32[diff] - cut) <= max(rtol * abs(cut), floor)
+    band = np.abs(s64[diff] - cut) <= max(rtol * abs(cut), floor)
     if not band.all():
         j = diff[~band][0]
-        return False, len(diff), f"slot {j} (oracle score {s32[j]!r}) differs outside the band around {cut!r}"
+        return False, len(diff), f"slot {j} (oracle score {s64[j]!r}) differs outside the band around {cut!r}"
     return True, len(diff) // 2, ""
 
 

@@ -25,12 +25,11 @@ def test_select_brute_force_order():
         assert np.all(np.diff(kept) > 0)
         ks = set(kept.tolist())
         assert set(range(P)) <= ks and set(range(n - R, n)) <= ks
-        s32 = s.astype(np.float32)
         cand = range(P, n - R)
         for a in cand:
             for b in cand:
                 if a in ks and b not in ks:
-                    assert _beats(s32, a, b)
+                    assert _beats(s, a, b)
 
 
 def test_select_hand_example_ties_to_lower_slot():
@@ -77,7 +76,7 @@ def _fps_from_scratch(X, k):
         for r in range(len(X)):
             if r in picks:
                 continue
-            dmin = min(float(np.float32(1.0 - U[r] @ U[p])) for p in picks)
+            dmin = min(float(1.0 - U[r] @ U[p]) for p in picks)
             if dmin > best:
                 best, arg = dmin, r
         picks.append(arg)
