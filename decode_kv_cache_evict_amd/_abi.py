@@ -29,7 +29,7 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_score_budget_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
            "kv_decode_attention_workspace", "kv_decode_attention",
-           "kv_rope_apply", "kve_set_test_overrides", "kve_last_error", "kve_abi_version"]
+           "kv_rope_apply", "kve_set_test_overrides", "kve_debug_flags", "kve_last_error", "kve_abi_version"]
 
 
 class KveError(RuntimeError):
@@ -90,6 +90,7 @@ def lib():
             "kv_decode_attention": (I32, [CP, P, I32, P, P, P, SZ, P]),
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
             "kve_set_test_overrides": (I32, [I32, I32]),
+            "kve_debug_flags": (I32, [ctypes.POINTER(ctypes.c_uint32)]),
             "kve_last_error": (ctypes.c_char_p, []),
             "kve_abi_version": (I32, []),
         }
@@ -345,6 +346,14 @@ def kv_rope_apply(src, dst, pos, rope_theta, stream=None):
 
 def kve_abi_version():
     return int(lib().kve_abi_version())
+
+
+def kve_debug_flags():
+    """Bounds-check flags of a KVE_DEBUG build since the last call (cleared);
+    raises KveError on a regular build."""
+    f = ctypes.c_uint32(0)
+    _check(lib().kve_debug_flags(ctypes.byref(f)))
+    return int(f.value)
 
 
 SCORE_IMPLS = {"default": 0, "valu": 1, "fused": 2}

@@ -21,10 +21,10 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 
-def _compile(src):
-    obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra=(), suffix=""):
+    obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + suffix + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -33,20 +33,31 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=False):
+def build(verbose=False, extra=(), suffix="", lib=LIB):
     os.makedirs(LIBDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, extra, suffix), SOURCES))
     for _, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+DEBUG_LIB = os.path.join(LIBDIR, "libkvevict_debug.so")
+
+
+def build_debug(verbose=False):
+    """libkvevict_debug.so: every source built with -DKVE_DEBUG, which checks
+    the indices of the select, compact, in-place and gather stages against
+    their segment before each access and reports misses through
+    kve_debug_flags() instead of touching memory."""
+    return build(verbose, extra=("-DKVE_DEBUG",), suffix="_debug", lib=DEBUG_LIB)
 
 
 SAN_LIB = os.path.join(LIBDIR, "libkvevict_san.so")
@@ -93,5 +104,7 @@ def sanitizer_runtime():
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--debug" in sys.argv:
+        print(build_debug(verbose=True))
     if "--sanitized" in sys.argv:
         print(build_sanitized())

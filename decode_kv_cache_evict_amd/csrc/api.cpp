@@ -139,6 +139,20 @@ kve_status kve_set_test_overrides(int32_t score_impl, int32_t spin_limit) {
   return KVE_OK;
 }
 
+kve_status kve_debug_flags(uint32_t* flags) {
+  if (!flags) return fail(KVE_EINVAL, "flags is NULL");
+#ifdef KVE_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return fail(KVE_EDEVICE, "kve_debug_flags: device synchronisation failed");
+  const unsigned int a = kve::debug_take_score(), b = kve::debug_take_select();
+  if (a == ~0u || b == ~0u) return fail(KVE_EDEVICE, "kve_debug_flags: flag words could not be read");
+  *flags = a | b;
+  return KVE_OK;
+#else
+  *flags = 0;
+  return fail(KVE_EINVAL, "kve_debug_flags: not a KVE_DEBUG build");
+#endif
+}
+
 int32_t kve_abi_version(void) { return KVE_ABI_VERSION; }
 
 size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o) {

@@ -101,6 +101,23 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// ---------------------------------------------------------------- debug build bounds checks
+// Built with -DKVE_DEBUG, KVE_CHECK(cond, bit) guards a global-memory access
+// whose index comes from device-resident metadata (segment offsets, lengths,
+// kept slots): a failed check sets `bit` in this source file's flag word and
+// the caller skips the access (nothing traps).  kve_debug_flags() on the host
+// reads and clears the words.  In the regular build the checks compile away.
+#ifdef KVE_DEBUG
+static __device__ unsigned int kve_debug_word;
+__device__ __forceinline__ bool kve_debug_check(bool ok, unsigned int bit) {
+  if (!ok) atomicOr(&kve_debug_word, 1u << bit);
+  return ok;
+}
+#define KVE_CHECK(cond, bit) ::kve::kve_debug_check((cond), (bit))
+#else
+#define KVE_CHECK(cond, bit) true
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 

@@ -58,6 +58,10 @@ hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
 // and its address on the current device (taken once per device).
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 hipError_t noalloc_scratch(void** ptr);
+// Debug build (KVE_DEBUG) only: read and clear the bounds-check flag word of
+// the score / select kernel files (0 in the regular build, ~0u when the copy fails).
+unsigned int debug_take_score();
+unsigned int debug_take_select();
 // The one-kernel trigger with entropy budgets applies when every
 // request-layer's work-groups fit the dispatch bound of its barrier.
 bool budget_step_fits(int32_t n_seg, int32_t n_kv, int32_t max_seg_len, int32_t head_dim);

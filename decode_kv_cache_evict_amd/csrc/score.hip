@@ -585,7 +585,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     return -1;                               // the segment keeps the failure mark stored after the first barrier
   int base = 0, cnt = 0;                     // output row of this chunk's first kept slot; kept count
   if (K >= n) {
-    for (int j = k0 + tid; j < k1; j += 256) mine[j - k0] = j;
+    for (int j = k0 + tid; j < k1; j += 256) if (KVE_CHECK(j - k0 < kMfmaChunk, 7)) mine[j - k0] = j;
     base = k0;
     cnt = k1 - k0;
   } else {
@@ -614,7 +614,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
       const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
       int keep_tot;
       const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
-      if (keep) mine[at] = j;
+      if (keep && KVE_CHECK(at < kMfmaChunk, 7)) mine[at] = j;
       cnt += keep_tot;
       eq_seen += eq_tot;
     }
@@ -623,7 +623,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   // gather this chunk's kept rows to output rows base .. base + cnt - 1
   const int64_t dst0 = oo + base;
   gather_rows<CPR>([&](int r) { return mine[r]; }, [&](int r) { return dst0 + r; }, cnt, a.k, a.v, a.pos, off,
-                   a.k_out, a.v_out, a.pos_out, a.kept, tid);
+                   a.k_out, a.v_out, a.pos_out, a.kept, tid, n, oo, oo + a.out_cap);
   return keep_n;
 }
 
@@ -697,16 +697,20 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
     if (cnt <= 0) continue;                                // the same decision in every thread
     for (int j = p0 + tid; j < p1; j += 256) {
       const uint32_t e = keys[j];
-      if (e >> 31) mover_at[int(e & 0x7fffffffu) - base_k - r_lo] = uint16_t(j);
+      if (e >> 31) {
+        const int m = int(e & 0x7fffffffu) - base_k - r_lo;
+        if (KVE_CHECK(m >= 0 && m < cnt, 6)) mover_at[m] = uint16_t(j);
+      }
     }
     for (int h = tid; h < K; h += 256) {                   // holes: evicted slots below K
       const uint32_t e = keys[h];
       const int rank = h - int(e & 0x7fffffffu);
-      if (!(e >> 31) && rank >= r_lo && rank < r_hi) hole_at[rank - r_lo] = uint16_t(h);
+      if (!(e >> 31) && rank >= r_lo && rank < r_hi && KVE_CHECK(rank - r_lo < kPiece, 6))
+        hole_at[rank - r_lo] = uint16_t(h);
     }
     __syncthreads();
     gather_rows<CPR>([&](int r) { return int(mover_at[r]); }, [&](int r) { return off + hole_at[r]; }, cnt, a.k,
-                     a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid);
+                     a.v, a.pos, off, a.k_out, a.v_out, a.pos_out, nullptr, tid, n, off, off + K);
     __syncthreads();                         // the next piece rebuilds the lists
   }
   return K;
@@ -1365,6 +1369,17 @@ void* g_scratch_ptr[kMaxDevices];
 std::once_flag g_scratch_once[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
 }  // namespace
+
+unsigned int debug_take_score() {
+#ifdef KVE_DEBUG
+  unsigned int v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kve_debug_word), sizeof(v)) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(kve_debug_word), &z, sizeof(z)) != hipSuccess) return ~0u;
+  return v;
+#else
+  return 0;
+#endif
+}
 
 hipError_t noalloc_scratch(void** ptr) {
   int dev = -1;

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
     return;
   }
   if (K >= n) {
-    for (int j = tid; j < n; j += kSelBlock) a.kept[oo + j] = j;
+    for (int j = tid; j < n; j += kSelBlock) if (KVE_CHECK(j < a.out_cap, 3)) a.kept[oo + j] = j;
     if (tid == 0) a.out_len[s] = n;
     return;
   }
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
       const bool keep = j < n && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
       eq_rank += eq;
       if (keep) {
-        if (at < K) a.kept[oo + at] = j;
+        if (at < K && KVE_CHECK(at < a.out_cap && j < n, 3)) a.kept[oo + at] = j;
         ++at;
       }
     }
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kLongBlock) void select_long_kernel(SelectArgs a) {
     return;
   }
   if (K >= n) {
-    for (int j = tid; j < n; j += kLongBlock) a.kept[oo + j] = j;
+    for (int j = tid; j < n; j += kLongBlock) if (KVE_CHECK(j < a.out_cap, 3)) a.kept[oo + j] = j;
     if (tid == 0) a.out_len[s] = n;
     return;
   }
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kLongBlock) void select_long_kernel(SelectArgs a) {
       const bool keep = j < n && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
       eq_rank += eq;
       if (keep) {
-        if (at < K) a.kept[oo + at] = j;
+        if (at < K && KVE_CHECK(at < a.out_cap && j < n, 3)) a.kept[oo + at] = j;
         ++at;
       }
     }
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kLongBlock) void select_split_kernel(SelectArgs a, 
   const int ls = (n + G - 1) / G;                      // this work-group's slots [s0, s1)
   const int s0 = min(n, g * ls), s1 = min(n, s0 + ls);
   if (K >= n) {
-    for (int j = s0 + tid; j < s1; j += kLongBlock) a.kept[oo + j] = j;
+    for (int j = s0 + tid; j < s1; j += kLongBlock) if (KVE_CHECK(j < a.out_cap, 3)) a.kept[oo + j] = j;
     if (g == 0 && tid == 0) __hip_atomic_store(&a.out_len[s], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kLongBlock) void select_split_kernel(SelectArgs a, 
       const bool keep = j < s1 && (!cand || kv[u] > T || (eq && eq_rank < int(kk)));
       eq_rank += eq;
       if (keep) {
-        if (at < K) a.kept[oo + at] = j;
+        if (at < K && KVE_CHECK(at < a.out_cap && j < n, 3)) a.kept[oo + at] = j;
         ++at;
       }
     }
@@ -537,6 +537,7 @@ __global__ __launch_bounds__(256) void compact_kernel(SelectArgs a) {
         const int r = r0 + u * RPP + rsub;
         int j = r < out_n ? a.kept[oo + r] : -1;
         if (j >= n_in) j = -1;
+        if (j >= 0 && !KVE_CHECK(io + j < a.in_rows && r < a.out_cap, 4)) j = -1;
         src[u] = j;
       }
 #pragma unroll
@@ -665,6 +666,8 @@ __global__ __launch_bounds__(kSelBlock) void inplace_kernel(SelectArgs a) {
         const int r = r0 + u * RPP + rsub;
         src[u] = r < p ? ml[r] : -1;
         dst[u] = r < p ? hl[r] : -1;
+        if (src[u] >= 0 && !KVE_CHECK(dst[u] >= 0 && dst[u] < K && src[u] >= K && src[u] < n, 5))
+          src[u] = -1;
         if (src[u] >= 0) {
           kb[u] = __builtin_nontemporal_load(&kc[(io + src[u]) * CPR + part]);
           vb[u] = __builtin_nontemporal_load(&vc[(io + src[u]) * CPR + part]);
@@ -729,6 +732,17 @@ hipError_t launch_select_compact(const SelectArgs& a, hipStream_t st) {
     case 32: return launch_compact<32>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+unsigned int debug_take_select() {
+#ifdef KVE_DEBUG
+  unsigned int v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kve_debug_word), sizeof(v)) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(kve_debug_word), &z, sizeof(z)) != hipSuccess) return ~0u;
+  return v;
+#else
+  return 0;
+#endif
 }
 
 }  // namespace kve

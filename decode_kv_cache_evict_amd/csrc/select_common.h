@@ -72,8 +72,9 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
 // Row gather of a 256-thread work-group: output rows dst_at(r) <- input rows
 // in_off + src_at(r) for r in [0, cnt), K and V (CPR 16-byte chunks per row)
 // and the position; kept_out[dst_at(r)] = src_at(r) when kept_out is set.
-// src_at and dst_at read LDS or registers (they must not issue memory loads).  GU rows per thread and
-// batch, four batches in registers: the memory counter retires loads and
+// src_at and dst_at read LDS or registers (they must not issue memory loads).
+// The debug build checks every source slot against [0, src_n) and every
+// output row against [dst_lo, dst_hi).  GU rows per thread and batch, four batches in registers: the memory counter retires loads and
 // stores in issue order and a batch's registers may only be reloaded once its
 // stores are done, so the loads run two batches ahead of the stores and a
 // batch is reloaded two batches after its stores, which leaves two batches in
@@ -83,7 +84,8 @@ __device__ __forceinline__ int block_sum(int v, int* wtot) {
 template <int CPR, int GU = 2, typename SrcAt, typename DstAt>
 __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& dst_at, int cnt, const void* k,
                                             const void* v, const int32_t* pos, int64_t in_off, void* k_out,
-                                            void* v_out, int32_t* pos_out, int32_t* kept_out, int tid) {
+                                            void* v_out, int32_t* pos_out, int32_t* kept_out, int tid,
+                                            int src_n, int64_t dst_lo, int64_t dst_hi) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int RPP = 256 / CPR;             // rows per thread-row
   constexpr int STEP = RPP * GU;
@@ -102,6 +104,7 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& ds
     for (int u = 0; u < GU; ++u) bt.src[u] = src_at(min(r0 + u * RPP + rsub, cnt - 1));
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
+      if (!KVE_CHECK(bt.src[u] >= 0 && bt.src[u] < src_n, 1)) continue;
       bt.k[u] = __builtin_nontemporal_load(&kin[(in_off + bt.src[u]) * CPR + part]);
       bt.v[u] = __builtin_nontemporal_load(&vin[(in_off + bt.src[u]) * CPR + part]);
       bt.pos[u] = pos[in_off + bt.src[u]];
@@ -113,6 +116,7 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& ds
       const int r = r0 + u * RPP + rsub;
       if (r < cnt) {
         const int64_t dst = dst_at(r);
+        if (!KVE_CHECK(dst >= dst_lo && dst < dst_hi, 2)) continue;
         __builtin_nontemporal_store(bt.k[u], &kout[dst * CPR + part]);
         __builtin_nontemporal_store(bt.v[u], &vout[dst * CPR + part]);
         if (part == 0) {

@@ -14,12 +14,15 @@
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *     keeps no state (apart from the test overrides of kve_set_test_overrides
- *     and the per-thread error message) and allocates no device memory;
+ *     keeps no state (apart from the test overrides of kve_set_test_overrides,
+ *     the per-thread error message, the static scratch array of
+ *     kv_evict_score_select_compact_noalloc and, in the bounds-checked build
+ *     only, the flag word of kve_debug_flags) and allocates no device memory;
  *     scratch comes from a caller-provided workspace whose size the
  *     *_workspace_size calls return.
  *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
- *     NULL is the null stream).  No call synchronises.
+ *     NULL is the null stream).  No call synchronises (kve_debug_flags, a test
+ *     call, synchronises the device).
  *   - Arguments are checked on the host BEFORE any launch; on an error status
  *     nothing is launched and nothing is written.  Values that live in device
  *     memory (segment offsets, lengths, budgets) are checked by the kernels,
@@ -450,6 +453,30 @@ kve_status kv_rope_apply(const float* src, void* dst, const int32_t* pos, int64_
  * Errors: EINVAL (score_impl not 0..2, spin_limit outside [0, 2^30]).
  */
 kve_status kve_set_test_overrides(int32_t score_impl, int32_t spin_limit);
+
+/*
+ * kve_debug_flags — bounds-check report of a library built with -DKVE_DEBUG
+ * (libkvevict_debug.so), for the library's own tests.  That build checks every
+ * global or LDS index of the select, compact and in-place kernels and of the
+ * gather / hole-filling stages of the one-call triggers against its segment's
+ * range before the access; an index out of range skips the access (nothing
+ * traps) and sets one bit of a per-device flag word.  This call synchronises
+ * the device, writes the OR of the flags set since the previous call to
+ * *flags and clears them:
+ *   bit 1  one-call trigger gather: a source slot outside [0, seg_len)
+ *   bit 2  one-call trigger gather: an output row outside the segment's rows
+ *          ([out_off, out_off + out_cap) compacting, [seg_off, seg_off + budget)
+ *          hole filling)
+ *   bit 3  select: a kept index at or past out_cap, or a kept slot past seg_len
+ *   bit 4  compact: a kept slot outside the input rows, or a row past out_cap
+ *   bit 5  in-place select: a mover outside [budget, seg_len) or a hole outside
+ *          [0, budget)
+ *   bit 6  one-call in-place trigger: a mover or hole list index outside its piece
+ *   bit 7  one-call trigger: a kept-slot list index outside its chunk
+ * Errors: EINVAL (flags NULL, or the library is not a debug build), EDEVICE
+ * (the device could not be read).
+ */
+kve_status kve_debug_flags(uint32_t* flags);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* kve_last_error(void);

@@ -25,3 +25,21 @@ def kve_overrides():
 
     yield set_
     kv.kve_set_test_overrides("default", 0)
+
+
+@pytest.fixture(autouse=True)
+def _debug_bounds_flags(request):
+    """With the bounds-checked library (KVE_LIB=.../libkvevict_debug.so), every
+    GPU test must end with no kernel index outside its segment: the flags are
+    cleared before the test and must read zero after it."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import decode_kv_cache_evict_amd as kv
+    if os.path.basename(kv.LIB_PATH) != "libkvevict_debug.so":
+        yield
+        return
+    kv.kve_debug_flags()
+    yield
+    flags = kv.kve_debug_flags()
+    assert flags == 0, f"bounds checks fired: flags 0x{flags:x}"

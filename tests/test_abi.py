@@ -100,3 +100,13 @@ def test_test_overrides_validate_and_reset():
     assert _fail(L.kve_set_test_overrides, 0, (1 << 30) + 1)[0] == 1
     assert L.kve_set_test_overrides(2, 5) == 0
     assert L.kve_set_test_overrides(0, 0) == 0
+
+
+def test_debug_flags_call_outside_a_debug_build():
+    if os.path.basename(kv.LIB_PATH) == "libkvevict_debug.so":
+        pytest.skip("run against the bounds-checked library")
+    L = kv.lib()
+    assert _fail(L.kve_debug_flags, None)[0] == 1
+    f = ctypes.c_uint32(7)
+    st, msg = _fail(L.kve_debug_flags, ctypes.byref(f))
+    assert st == 1 and "not a KVE_DEBUG build" in msg and f.value == 0
