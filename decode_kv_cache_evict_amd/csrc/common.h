@@ -77,6 +77,28 @@ __device__ __forceinline__ RotPair rope_pair(double a, double b, double inv, int
 }
 
 // ---------------------------------------------------------------- wave reductions
+// Combine v over lanes l and l ^ 16 (lanes16_*) or l ^ 32 (lanes32_*) with the
+// gfx950 row-swap instructions: v_permlane16_swap with both operands v leaves
+// each lane holding {v[l], v[l ^ 16]} across its two results (v_permlane32_swap
+// likewise for l ^ 32), so the pair's max or sum needs no LDS round trip.
+// Every lane of the wave must be active.
+__device__ __forceinline__ float lanes16_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float lanes32_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float lanes16_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float lanes32_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

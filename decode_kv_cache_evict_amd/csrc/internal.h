@@ -51,8 +51,8 @@ struct ScoreArgs {
 };
 
 // Largest segment the one-kernel step can select on chip: its order keys reuse the
-// two 64-key tiles of padded bf16 rows (64 * (D + 8) 32-bit words).
-constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 8); }
+// two 64-key tiles of padded bf16 rows (64 * (D + 16) 32-bit words).
+constexpr int step_max_seg(int head_dim) { return 64 * (head_dim + 16); }
 hipError_t launch_score_select_compact(ScoreArgs& a, void* ws, hipStream_t st);
 // Static device scratch of kv_evict_score_select_compact_noalloc: its size,
 // and its address on the current device (taken once per device).

@@ -302,9 +302,11 @@ struct WaveRows {
   }
 
   // Logits of key tiles q0, q0+1 of one LDS batch (row stride LS): acc[j][rt] holds
-  // rows 16*(w*RT+rt) + 4*quad + i against key (q0+j)*16 + col.
-  template <int LS>
-  __device__ __forceinline__ void logits2(f32x4 (&acc)[2][RT], const uint16_t* kb, int q0, int col, int quad) const {
+  // rows 16*(w*RT+rt) + 4*quad + i against key (q0+j)*16 + col.  SHIFT: the
+  // accumulation starts from shift[rt] (one value per row) instead of 0.
+  template <int LS, bool SHIFT>
+  __device__ __forceinline__ void logits2(f32x4 (&acc)[2][RT], const uint16_t* kb, int q0, int col, int quad,
+                                          const f32x4 (&shift)[RT]) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       bf16x8 bfr[KS];
@@ -314,7 +316,7 @@ struct WaveRows {
         bfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        f32x4 x = SHIFT ? shift[rt] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], bfr[ks], x, 0, 0, 0);
         acc[j][rt] = x;
@@ -373,23 +375,22 @@ __device__ __forceinline__ void stats_update(float (&mc)[RT][4], float (&l)[RT][
 
 // Pass-2: per key of tiles q0, q0+1, the max over this wave's rows of
 // c*x - lse (MEAN: the sum of exp2(c*x - lse)), combined over the 4 lane
-// groups; written to redw[key].
+// groups; written to redw[key].  The logits arrive shifted, acc = x - lse/c
+// (the MFMA accumulation starts from -lse/c), so c*x - lse = c*acc, and since
+// c > 0 the max over the rows needs one multiply per key instead of one
+// multiply-add per row.
 template <int RT, bool MEAN>
-__device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], const float (&lse)[RT][4], float c, float* redw,
-                                         int q0, int col, int quad) {
+__device__ __forceinline__ void key_max2(const f32x4 (&acc)[2][RT], float c, float* redw, int q0, int col, int quad) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float best = MEAN ? 0.f : -kInf;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float y = fmaf(acc[j][rt][i], c, -lse[rt][i]);
-        best = MEAN ? best + fast_exp2(y) : fmaxf(best, y);
-      }
-    best = MEAN ? best + __shfl_xor(best, 16, kWave) : fmaxf(best, __shfl_xor(best, 16, kWave));
-    best = MEAN ? best + __shfl_xor(best, 32, kWave) : fmaxf(best, __shfl_xor(best, 32, kWave));
-    if (quad == 0) redw[(q0 + j) * 16 + col] = best;
+      for (int i = 0; i < 4; ++i) best = MEAN ? best + fast_exp2(acc[j][rt][i] * c) : fmaxf(best, acc[j][rt][i]);
+    best = MEAN ? lanes16_sum(best) : lanes16_max(best);
+    best = MEAN ? lanes32_sum(best) : lanes32_max(best);
+    if (quad == 0) redw[(q0 + j) * 16 + col] = MEAN ? best : best * c;
   }
 }
 
@@ -775,7 +776,11 @@ __device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s,
 
 template <int D, int RT, int MODE>
 __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
-  constexpr int LS = D + 8;                  // padded LDS row (bf16 elements)
+  // Padded LDS row (bf16 elements).  A 16-byte fragment read of the MFMA B
+  // operand has lane (col, quad) read row col at byte 16 * quad; with rows of
+  // D + 16 elements (288 bytes at D = 128) the reads of a wave hit distinct
+  // banks, while D + 8 (272 bytes) costs four conflict cycles per read on gfx950.
+  constexpr int LS = D + 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int KPU = 256 / CPR;             // keys covered by one 16-byte load per thread
   constexpr int CPT = kBK / KPU;             // loads per thread per batch
@@ -841,6 +846,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   WaveRows<D, RT> rows;
   rows.load(static_cast<const uint16_t*>(a.qr), rpos_s, qoff_s, w, col, quad);
   float st0[RT][4], st1[RT][4];   // pass 1: (m * c, l); pass 2: st0 = lse (log2 units)
+  f32x4 shift[RT];                // pass 2: -lse / c, where the rows' MFMA accumulation starts
+  auto set_shift = [&]() {
+    const float ninv = -1.f / c;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) shift[rt][i] = st0[rt][i] * ninv;
+  };
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -904,14 +917,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x4 acc[2][RT];
-        rows.template logits2<LS>(acc, kt[cur], 2 * h, col, quad);
+        rows.template logits2<LS, P2>(acc, kt[cur], 2 * h, col, quad, shift);
         if (any_late) {
           const int kp2[2] = {kpos[2 * h], kpos[2 * h + 1]};
           rows.mask2(acc, kp2, rpos_s, w, quad);
         }
         if (!P2) stats_update<RT>(st0, st1, acc, c);
-        else if (mean) key_max2<RT, true>(acc, st0, c, red[cur][w], 2 * h, col, quad);
-        else key_max2<RT, false>(acc, st0, c, red[cur][w], 2 * h, col, quad);
+        else if (mean) key_max2<RT, true>(acc, c, red[cur][w], 2 * h, col, quad);
+        else key_max2<RT, false>(acc, c, red[cur][w], 2 * h, col, quad);
       }
       if (it + 1 < ntl) store_batch(cur ^ 1);
       if (it + 2 < ntl) load_batch(kb_at(it + 2));
@@ -923,6 +936,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   };
 
   if (MODE == kModePass2) {
+    set_shift();
     sweep(std::integral_constant<bool, true>{});
     return;
   }
@@ -993,6 +1007,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
+  set_shift();
   sweep(std::integral_constant<bool, true>{});
   if (MODE < kModeStep) return;
 

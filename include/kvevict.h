@@ -231,7 +231,7 @@ size_t kv_evict_score_select_compact_workspace(const kve_cache* in, const kve_ob
  * result of kv_evict_score(in, o, scores, NULL) followed by
  * kv_evict_select_compact(in, scores, NULL, in->n_rows, budget, ...), with the
  * same meaning of every argument.  For bf16 caches whose max_seg_len fits the
- * on-chip selection (8704 rows at head_dim 128, 4608 at 64) it runs as one
+ * on-chip selection (9216 rows at head_dim 128, 5120 at 64) it runs as one
  * kernel: each segment's work-groups score their chunk, wait for the segment's
  * other chunks, select, and gather their own chunk's kept rows while those are
  * still in cache; otherwise it makes the two calls.  scores ([in->n_rows] fp32)
@@ -284,8 +284,8 @@ size_t kv_evict_score_select_compact_inplace_workspace(const kve_cache* c, const
  * uniform_budget, n_prefix, n_recent, new_len), with the same meaning of every
  * argument (hole filling: the survivors in [K, n), in ascending slot order,
  * move into the evicted slots of [0, K), in ascending slot order).  For bf16
- * caches whose max_seg_len fits the on-chip selection (8704 rows at head_dim
- * 128, 4608 at 64) it runs as one kernel (a segment's work-groups score their
+ * caches whose max_seg_len fits the on-chip selection (9216 rows at head_dim
+ * 128, 5120 at 64) it runs as one kernel (a segment's work-groups score their
  * chunks, usually the whole segment in one; the last of them to finish selects
  * and moves the segment's survivors); otherwise it makes the two calls.  The kept
  * sets may differ from the two-call form's only where scores tie to fp32
@@ -318,9 +318,9 @@ size_t kv_evict_score_budget_select_compact_workspace(const kve_cache* in, const
  * head_entropy ([n_seg] fp32) is required and written; budget_out ([n_seg] int32)
  * is optional and receives the head budgets.  out->max_seg_len must be at least
  * in->max_seg_len (a head may keep every row).  For bf16 caches whose segments fit
- * the on-chip selection (8704 rows at head_dim 128, 4608 at 64) and whose heads'
+ * the on-chip selection (9216 rows at head_dim 128, 5120 at 64) and whose heads'
  * work-groups fit its dispatch bound (about 96 per request-layer, so at most 10
- * heads of up to 8704 rows) it runs as one kernel: each request-layer's heads score their
+ * heads of up to 9216 rows) it runs as one kernel: each request-layer's heads score their
  * chunks, publish their entropies, meet, and every work-group solves the same
  * head budgets with the budget kernel's solver before selecting and gathering
  * its own chunk's kept rows; otherwise it makes the three calls.  The entropies

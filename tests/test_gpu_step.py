@@ -24,14 +24,14 @@ CASES = {
     # single-kernel path
     "qwen3-4b-1l": (get_workload("qwen3-4b-1l"), 1792),
     "llama-ragged": (get_workload("r1-llama-8b").scaled(batch=3, len_lo=700, len_hi=3300, n_layers=1), 640),
-    "long-8k": (get_workload("long-65k").scaled(batch=1, len_lo=8704, len_hi=8704), 2048),
-    "d64-bf16": (get_workload("tiny-f32").scaled(dtype="bf16", batch=3, len_lo=1500, len_hi=4608), 1000),
+    "long-9216": (get_workload("long-65k").scaled(batch=1, len_lo=9216, len_hi=9216), 2048),
+    "d64-bf16": (get_workload("tiny-f32").scaled(dtype="bf16", batch=3, len_lo=1500, len_hi=5120), 1000),
     "qwen-short": (get_workload("qwen3-4b-1l").scaled(batch=2, len_lo=333, len_hi=333), 300),
     "d64-long": (get_workload("tiny-f32").scaled(dtype="bf16", batch=1, len_lo=6000, len_hi=8704), 3000),
     "non-causal": (get_workload("qwen3-4b-1l").scaled(batch=2, len_lo=500, len_hi=900, causal=0), 480),
     # two-call fallback
     "tiny-f32": (get_workload("tiny-f32"), 448),
-    "long-9k": (get_workload("long-65k").scaled(batch=1, len_lo=8705, len_hi=9000), 2048),
+    "long-9217": (get_workload("long-65k").scaled(batch=1, len_lo=9217, len_hi=9500), 2048),
 }
 
 
