@@ -341,9 +341,10 @@ def cpu_model():
 CSRC = os.path.join(ROOT, "decode_kv_cache_evict_amd", "csrc")
 TRAFFIC = {
     "split": (os.path.join(ROOT, "profiles", "select_compact_qwen3-4b-36l_hbm_traffic.txt"),
-              [os.path.join(CSRC, "select.hip"), os.path.join(CSRC, "select_common.h")]),
+              [os.path.join(CSRC, f) for f in ("select.hip", "select_common.h", "common.h", "internal.h")]),
     "fused": (os.path.join(ROOT, "profiles", "score_select_compact_qwen3-4b-36l_hbm_traffic.txt"),
-              [os.path.join(CSRC, "score.hip"), os.path.join(CSRC, "select_common.h")]),
+              [os.path.join(CSRC, f) for f in ("score.hip", "select_common.h", "budget_common.h", "common.h",
+                                                "internal.h")]),
 }
 
 
