@@ -1,4 +1,5 @@
-"""Workload descriptions (shapes, knobs, seeds) for the eviction step.
+"""Workload descriptions (shapes, knobs, seeds) for the eviction step, read
+from workloads/configs/<name>.json.
 
 Sizes follow the five benchmark cases of the eviction-step build:
   tiny-f32      one fp32 layer, 4 query / 2 KV heads, d=64, 512 keys -> 448
@@ -10,7 +11,9 @@ Value structure (clustered pre-RoPE keys and queries, a few "global" queries
 that revisit early clusters) follows the BeaconKV page's observations
 (section on thought-revisiting tokens: global queries cluster, Fig. 4).
 """
-from dataclasses import dataclass, replace
+import json
+import os
+from dataclasses import dataclass, fields, replace
 
 
 @dataclass(frozen=True)
@@ -66,38 +69,24 @@ class Workload:
         return replace(self, **kw)
 
 
-WORKLOADS = {
-    "tiny-f32": Workload(
-        name="tiny-f32", dtype="f32", n_layers=1, batch=1, n_q_heads=4, n_kv_heads=2,
-        head_dim=64, rope_theta=1e4, len_lo=512, len_hi=512, budget=448,
-        n_recent_q=8, n_beacon=8, fps_cap=16, fps_keep=8, n_clusters=8,
-        early_frac=0.0, early_clusters=0, global_frac=0.0, beacon_mode="c01",
-        fps_buf_mode="beacons+recent", seed_base=1000),
-    "qwen3-4b-1l": Workload(
-        name="qwen3-4b-1l", dtype="bf16", n_layers=1, batch=14, n_q_heads=32, n_kv_heads=8,
-        head_dim=128, rope_theta=1e6, len_lo=2048, len_hi=2048, budget=1792,
-        n_recent_q=16, n_beacon=32, fps_cap=32, fps_keep=16, n_clusters=16,
-        early_frac=0.1, early_clusters=4, global_frac=0.05, beacon_mode="past",
-        fps_buf_mode="beacons", seed_base=2000),
-    "qwen3-4b-36l": Workload(
-        name="qwen3-4b-36l", dtype="bf16", n_layers=36, batch=16, n_q_heads=32, n_kv_heads=8,
-        head_dim=128, rope_theta=1e6, len_lo=4096, len_hi=4096, budget=3584,
-        n_recent_q=16, n_beacon=32, fps_cap=32, fps_keep=16, n_clusters=16,
-        early_frac=0.1, early_clusters=4, global_frac=0.05, beacon_mode="past",
-        fps_buf_mode="beacons", triggers=4, append=512, seed_base=3000),
-    "r1-llama-8b": Workload(
-        name="r1-llama-8b", dtype="bf16", n_layers=32, batch=10, n_q_heads=32, n_kv_heads=8,
-        head_dim=128, rope_theta=5e5, len_lo=6144, len_hi=8192, budget=0,
-        n_recent_q=16, n_beacon=32, fps_cap=0, fps_keep=0, n_clusters=16,
-        early_frac=0.1, early_clusters=4, global_frac=0.05, beacon_mode="past",
-        fps_buf_mode="beacons", seed_base=4000),
-    "long-65k": Workload(
-        name="long-65k", dtype="bf16", n_layers=1, batch=4, n_q_heads=32, n_kv_heads=8,
-        head_dim=128, rope_theta=5e5, len_lo=65536, len_hi=65536, budget=8192,
-        n_recent_q=16, n_beacon=32, fps_cap=0, fps_keep=0, n_clusters=16,
-        early_frac=0.1, early_clusters=4, global_frac=0.05, beacon_mode="past",
-        fps_buf_mode="beacons", trace_layers=(10, 21), d_model=4096, seed_base=5000),
-}
+CONFIG_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "configs")
+
+
+def load_workload(path):
+    """A Workload from a JSON file of its fields (every field named; unknown keys are an error)."""
+    with open(path) as f:
+        d = json.load(f)
+    names = {f.name for f in fields(Workload)}
+    missing, extra = names - set(d), set(d) - names
+    if missing or extra:
+        raise ValueError(f"{path}: missing fields {sorted(missing)}, unknown fields {sorted(extra)}")
+    d["trace_layers"] = tuple(d["trace_layers"])
+    return Workload(**d)
+
+
+# the five cases, one JSON file each (shapes, seeds and knobs)
+WORKLOADS = {w.name: w for w in (load_workload(os.path.join(CONFIG_DIR, f)) for f in sorted(os.listdir(CONFIG_DIR))
+                                 if f.endswith(".json"))}
 
 
 def get_workload(name):
