@@ -345,7 +345,7 @@ template <int RT>
 __device__ __forceinline__ void stats_update(float (&mc)[RT][4], float (&l)[RT][4], const f32x4 (&acc)[2][RT],
                                              float c) {
   float lsum[RT][4];
-  bool redo = false;
+  float big = 0.f;                           // the largest sum (one compare instead of one per sum)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -353,9 +353,9 @@ __device__ __forceinline__ void stats_update(float (&mc)[RT][4], float (&l)[RT][
       const float v = l[rt][i] + fast_exp2(fmaf(acc[0][rt][i], c, -mc[rt][i])) +
                       fast_exp2(fmaf(acc[1][rt][i], c, -mc[rt][i]));
       lsum[rt][i] = v;
-      redo |= !(v <= kBig);
+      big = __builtin_fmaxf(big, v);
     }
-  if (__any(redo)) {
+  if (__any(!(big <= kBig))) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1201,17 +1201,17 @@ hipError_t launch_valu(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Keys per MFMA work-group of the two scoring passes: the multiple of 64 in
-// [256, 2048] with the shortest expected launch, counted as rounds of
+// [256, 8192] with the shortest expected launch, counted as rounds of
 // resident work-groups (three per CU) times the keys a work-group scores plus
 // a fixed cost of about 96 keys' worth (query load, statistics); ties go to
 // the length nearest 1024.  This keeps the last round of a launch from
-// running mostly empty (65,536-key segments, 32 of them: 1408 keys, two full
-// rounds, instead of 1024 keys, 2.7 rounds).
+// running mostly empty (65,536-key segments, 32 of them: 2752 keys, one full
+// round, instead of 1024 keys, 2.7 rounds).
 int mfma_chunk(int n_seg, int max_seg_len) {
   constexpr int64_t kResident = 3 * 256, kOverhead = 96;
   int best = kMfmaChunk;
   int64_t best_cost = INT64_MAX;
-  for (int c = 256; c <= 2048; c += 64) {
+  for (int c = 256; c <= 8192; c += 64) {
     const int64_t wgs = int64_t(n_seg) * ((max_seg_len + c - 1) / c);
     const int64_t cost = (wgs + kResident - 1) / kResident * (c + kOverhead);
     if (cost < best_cost || (cost == best_cost && std::abs(c - kMfmaChunk) < std::abs(best - kMfmaChunk))) {
