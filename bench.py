@@ -48,6 +48,10 @@ def parse():
                     help="attention: time kv_decode_attention over the compacted cache; skipkv: time the "
                          "sentence-redundancy score (SkipKV) on sentence-structured hidden states; epikv: "
                          "the attention-free hidden-state score and its select/compact (long-65k)")
+    ap.add_argument("--stamps", action="store_true",
+                    help="after the timed steps, run the trigger once more and report the one-call kernel's mean "
+                         "time per phase (needs the phase-stamping library: "
+                         "KVE_LIB=decode_kv_cache_evict_amd/_lib/libkvevict_stamps.so)")
     ap.add_argument("--call", choices=["split", "fused", "inplace", "inplace-split"], default="fused",
                     help="split: kv_evict_score then kv_evict_select_compact; "
                          "fused: kv_evict_score_select_compact (one kernel per call); "
@@ -285,6 +289,38 @@ class StepRunner:
                 ci += 1
         if side is not main:
             main.wait_stream(side)
+
+
+STAMP_PHASES = ["pass 1", "first segment barrier", "log-sum-exp merge", "pass 2", "second meeting",
+                "threshold", "ranking", "gather"]
+
+
+def phase_stamps(run_once):
+    """Run the trigger once more with the phase-stamping library (KVE_STAMPS
+    build) and summarise its work-group items: mean microseconds per phase
+    (consecutive stamps; the in-place kernel stamps the first four phases),
+    mean item life, and the span from the first item's start to the last
+    item's end."""
+    import numpy as np
+    import torch
+    import decode_kv_cache_evict_amd as kv
+    torch.cuda.synchronize()
+    kv.kve_debug_stamps()                    # clears what earlier runs left
+    run_once()
+    torch.cuda.synchronize()
+    st, tpu = kv.kve_debug_stamps()
+    st = st[st[:, 0] > 0].astype(np.int64)
+    if len(st) == 0:
+        raise RuntimeError("no work-group item recorded a stamp (not a one-call trigger?)")
+    full = st[(st > 0).all(axis=1)]
+    k = 9 if len(full) else 5
+    rec = full if len(full) else st[(st[:, :5] > 0).all(axis=1)]
+    d = np.diff(rec[:, :k], axis=1) / tpu
+    return {"items": int(len(rec)), "of_items": int(len(st)),
+            "mean_us": {name: round(float(x), 2) for name, x in zip(STAMP_PHASES, d.mean(axis=0))},
+            "item_life_us": round(float(((rec[:, k - 1] - rec[:, 0]) / tpu).mean()), 2),
+            "span_us": round(float((rec[:, k - 1].max() - rec[:, 0].min()) / tpu), 1),
+            "clock": f"memory clock, {tpu:g} ticks per microsecond"}
 
 
 def verify_trigger(runner, st, si, out, w, call, ran):
@@ -747,6 +783,8 @@ def config_bench(args, w):
          "global_batch": B, "seq_len": w.len_hi, "parallelism": "single GPU"},
         per, nbytes, dom, dom, dtype=w.dtype)
     res["verified"] = verified
+    if args.stamps:
+        res["phase_us"] = phase_stamps(calls[0][1])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -1015,6 +1053,10 @@ def main():
     res["copy_reference"] = {"what": "torch copy_ of 2 GiB, read + write bytes",
                              "gb_per_s": 2 * src.numel() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9}
     del src, dst
+    if args.stamps:
+        if flush is not None:
+            flush.fill_(7)
+        res["phase_us"] = phase_stamps(lambda: runner.run(0))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -13,6 +13,6 @@ from ._abi import (  # noqa: F401
     kv_evict_score_select_compact_inplace, kv_evict_score_budget_select_compact_workspace,
     kv_evict_score_budget_select_compact, beacon_fps_update,
     epikv_workspace_size, epikv_score, skipkv_workspace_size, skipkv_sentence_scores, kv_decode_attention_workspace, kv_decode_attention, kv_rope_apply,
-    kve_abi_version, kve_set_test_overrides, kve_debug_flags, EXPORTS, LIB_PATH,
+    kve_abi_version, kve_set_test_overrides, kve_debug_flags, kve_debug_stamps, EXPORTS, LIB_PATH,
     KVE_AGG_MAX, KVE_AGG_MEAN, KVE_EPIKV_Z, KVE_EPIKV_MEAN,
 )

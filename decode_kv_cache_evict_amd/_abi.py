@@ -29,7 +29,8 @@ EXPORTS = ["kv_evict_score_workspace", "kv_evict_score", "kv_evict_budgets", "kv
            "kv_evict_score_budget_select_compact", "beacon_fps_update",
            "epikv_workspace_size", "epikv_score", "skipkv_workspace_size", "skipkv_sentence_scores",
            "kv_decode_attention_workspace", "kv_decode_attention",
-           "kv_rope_apply", "kve_set_test_overrides", "kve_debug_flags", "kve_last_error", "kve_abi_version"]
+           "kv_rope_apply", "kve_set_test_overrides", "kve_debug_flags", "kve_debug_stamps", "kve_last_error",
+           "kve_abi_version"]
 
 
 class KveError(RuntimeError):
@@ -91,6 +92,7 @@ def lib():
             "kv_rope_apply": (I32, [P, P, P, I64, I32, D, I32, P]),
             "kve_set_test_overrides": (I32, [I32, I32]),
             "kve_debug_flags": (I32, [ctypes.POINTER(ctypes.c_uint32)]),
+            "kve_debug_stamps": (I32, [P, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
             "kve_last_error": (ctypes.c_char_p, []),
             "kve_abi_version": (I32, []),
         }
@@ -354,6 +356,16 @@ def kve_debug_flags():
     f = ctypes.c_uint32(0)
     _check(lib().kve_debug_flags(ctypes.byref(f)))
     return int(f.value)
+
+
+def kve_debug_stamps(max_items=1 << 16):
+    """Phase stamps of a KVE_STAMPS build since the last call (cleared):
+    (uint64 array [rows, 9], ticks per microsecond); raises KveError on other builds."""
+    import numpy as np
+    buf = np.zeros((max_items, 9), dtype=np.uint64)
+    n, tpu = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().kve_debug_stamps(buf.ctypes.data, int(max_items), ctypes.byref(n), ctypes.byref(tpu)))
+    return buf[:n.value], tpu.value
 
 
 SCORE_IMPLS = {"default": 0, "valu": 1, "fused": 2}

@@ -60,6 +60,16 @@ def build_debug(verbose=False):
     return build(verbose, extra=("-DKVE_DEBUG",), suffix="_debug", lib=DEBUG_LIB)
 
 
+STAMPS_LIB = os.path.join(LIBDIR, "libkvevict_stamps.so")
+
+
+def build_stamps(verbose=False):
+    """libkvevict_stamps.so: every source built with -DKVE_STAMPS, whose one-call
+    trigger kernels record a memory-clock stamp at each phase boundary of every
+    work-group item (read with kve_debug_stamps())."""
+    return build(verbose, extra=("-DKVE_STAMPS",), suffix="_stamps", lib=STAMPS_LIB)
+
+
 SAN_LIB = os.path.join(LIBDIR, "libkvevict_san.so")
 # host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI layer
 # (argument checks, workspace carving, launch set-up); device code is built as usual
@@ -106,5 +116,7 @@ if __name__ == "__main__":
     print(build(verbose=True))
     if "--debug" in sys.argv:
         print(build_debug(verbose=True))
+    if "--stamps" in sys.argv:
+        print(build_stamps(verbose=True))
     if "--sanitized" in sys.argv:
         print(build_sanitized())

@@ -153,6 +153,27 @@ kve_status kve_debug_flags(uint32_t* flags) {
 #endif
 }
 
+kve_status kve_debug_stamps(uint64_t* stamps, int64_t max_items, int64_t* n_rows, double* ticks_per_us) {
+  if (!stamps || !n_rows || !ticks_per_us || max_items < 0)
+    return fail(KVE_EINVAL, "kve_debug_stamps: NULL pointer or negative max_items");
+#ifdef KVE_STAMPS
+  int dev = 0, khz = 0;
+  if (hipDeviceSynchronize() != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    return fail(KVE_EDEVICE, "kve_debug_stamps: device synchronisation or clock query failed");
+  static_assert(sizeof(unsigned long long) == sizeof(uint64_t), "64-bit stamps");
+  const int64_t n = kve::debug_take_stamps(reinterpret_cast<unsigned long long*>(stamps), max_items);
+  if (n < 0) return fail(KVE_EDEVICE, "kve_debug_stamps: stamps could not be copied");
+  *n_rows = n;
+  *ticks_per_us = double(khz) / 1000.0;
+  return KVE_OK;
+#else
+  *n_rows = 0;
+  *ticks_per_us = 0.0;
+  return fail(KVE_EINVAL, "kve_debug_stamps: not a KVE_STAMPS build");
+#endif
+}
+
 int32_t kve_abi_version(void) { return KVE_ABI_VERSION; }
 
 size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o) {

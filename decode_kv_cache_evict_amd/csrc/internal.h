@@ -61,6 +61,12 @@ hipError_t noalloc_scratch(void** ptr);
 // Debug build (KVE_DEBUG) only: read and clear the bounds-check flag word of
 // the score / select kernel files (0 in the regular build, ~0u when the copy fails).
 unsigned int debug_take_score();
+// Phase-stamp build (KVE_STAMPS) only: copy up to n_items rows of
+// kStampPhases memory-clock stamps of the one-call trigger's work-group items
+// into host memory and clear them; returns the rows copied (-1 on a copy
+// failure, 0 in the other builds).
+constexpr int kStampPhases = 9;
+int64_t debug_take_stamps(unsigned long long* host, int64_t n_items);
 unsigned int debug_take_select();
 // The one-kernel trigger with entropy budgets applies when every
 // request-layer's work-groups fit the dispatch bound of its barrier.

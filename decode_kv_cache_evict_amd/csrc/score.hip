@@ -250,6 +250,29 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreArgs a) {
 // costs one fma, one exp and one add per logit.  The causal mask is applied only
 // to tiles holding a key newer than the wave's earliest query position.
 constexpr float kBig = 18446744073709551616.0f;   // 2^64
+
+// ---------------------------------------------------------------- phase stamps
+// Built with -DKVE_STAMPS (libkvevict_stamps.so), the one-call trigger kernels
+// record the memory-clock time (s_memrealtime) at each phase boundary of every
+// work-group item (ticket) below kStampItems; kve_debug_stamps() copies them
+// out.  Phases: 0 item taken, 1 pass 1 done and its row statistics stored,
+// 2 first segment barrier passed, 3 log-sum-exp merged, 4 pass 2 done,
+// 5 second meeting passed (scores, and with entropy budgets the head budgets,
+// known), 6 threshold found, 7 output places ranked, 8 rows gathered.  In the
+// regular build the stamps compile to nothing.
+#ifdef KVE_STAMPS
+constexpr int kStampItems = 1 << 16;
+__device__ unsigned long long kve_stamps[kStampItems][kStampPhases];
+#define KVE_STAMP(item, ph)                                                                      \
+  do {                                                                                             \
+    if (threadIdx.x == 0 && (item) >= 0 && (item) < kStampItems)                                   \
+      kve_stamps[(item)][(ph)] = __builtin_amdgcn_s_memrealtime();                                 \
+  } while (0)
+#else
+#define KVE_STAMP(item, ph) \
+  do {                      \
+  } while (0)
+#endif
 constexpr int kBK = 64;                           // keys per LDS batch
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -571,7 +594,7 @@ __device__ __forceinline__ void segment_threshold(const ScoreArgs& a, int64_t of
 // rejected segment).
 template <int D>
 __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, int64_t off, int n, int k0, int k1,
-                                                   int K, uint32_t* keys, const SegKeys* loaded, int tid) {
+                                                   int K, uint32_t* keys, const SegKeys* loaded, int tid, int item) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
@@ -593,6 +616,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     uint32_t T, kk;
     if (loaded) segment_radix(a, n, K - P - R, keys, *loaded, hist, sh, tid, T, kk);
     else segment_threshold(a, off, n, K - P - R, keys, hist, sh, tid, T, kk);
+    KVE_STAMP(item, 6);
     // kept slots and threshold ties before this chunk
     int eq_b = 0, gt_b = 0;
     for (int j = P + tid; j < min(k0, n - R); j += 256) {
@@ -621,6 +645,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     }
   }
   __syncthreads();
+  KVE_STAMP(item, 7);
   // gather this chunk's kept rows to output rows base .. base + cnt - 1
   const int64_t dst0 = oo + base;
   gather_rows<CPR>([&](int r) { return mine[r]; }, [&](int r) { return dst0 + r; }, cnt, a.k, a.v, a.pos, off,
@@ -796,6 +821,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
   int s, ch;
+  int item = -1;                             // the ticket (one-call kernels), for the phase stamps
   if (MODE >= kModeFused) {
     if (tid == 0) {
       if (MODE == kModeBudget) {               // one queue: a request-layer's heads are consecutive tickets
@@ -806,10 +832,11 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
       }
     }
     __syncthreads();
-    const int item = sh_item;
+    item = sh_item;
     if (item < 0) return;
     s = item / a.n_chunks;
     ch = item % a.n_chunks;
+    KVE_STAMP(item, 0);
   } else {
     xcd_item(a, s, ch);
   }
@@ -966,8 +993,10 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // segment barrier: the stores above are acknowledged before the arrival count
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  KVE_STAMP(item, 1);
   if (tid == 0) sh_item = segment_barrier(ctl + kQueues + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
+  KVE_STAMP(item, 2);
   // Every work-group of the segment has read the segment's length by now (the
   // output length may be the input length array): the segment counts as failed
   // until its last work-group has moved its rows.  Both this store and the
@@ -1003,12 +1032,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     lse_s[r] = lse;
   }
   __syncthreads();
+  KVE_STAMP(item, 3);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
   set_shift();
   sweep(std::integral_constant<bool, true>{});
+  KVE_STAMP(item, 4);
   if (MODE < kModeStep) return;
 
   // Every chunk's scores are stored (acknowledged before the arrival count).
@@ -1048,8 +1079,10 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     } else {
       K = a.budget ? a.budget[s] : a.uniform_budget;
     }
-    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid);
+    KVE_STAMP(item, 5);
+    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid, item);
     if (keep_n < 0) return;
+    KVE_STAMP(item, 8);
     // the last work-group to finish its gather publishes the segment's length
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1384,6 +1417,23 @@ void* g_scratch_ptr[kMaxDevices];
 std::once_flag g_scratch_once[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
 }  // namespace
+
+int64_t debug_take_stamps(unsigned long long* host, int64_t n_items) {
+#ifdef KVE_STAMPS
+  const int64_t n = n_items < kStampItems ? n_items : kStampItems;
+  const size_t bytes = size_t(n) * kStampPhases * sizeof(unsigned long long);
+  if (n <= 0) return 0;
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(kve_stamps), bytes) != hipSuccess) return -1;
+  void* dev = nullptr;
+  if (hipGetSymbolAddress(&dev, HIP_SYMBOL(kve_stamps)) != hipSuccess) return -1;
+  if (hipMemset(dev, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return -1;
+  return n;
+#else
+  (void)host;
+  (void)n_items;
+  return 0;
+#endif
+}
 
 unsigned int debug_take_score() {
 #ifdef KVE_DEBUG

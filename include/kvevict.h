@@ -478,6 +478,24 @@ kve_status kve_set_test_overrides(int32_t score_impl, int32_t spin_limit);
  */
 kve_status kve_debug_flags(uint32_t* flags);
 
+/*
+ * kve_debug_stamps — phase timestamps of a library built with -DKVE_STAMPS
+ * (libkvevict_stamps.so), for measuring where the one-call trigger kernels
+ * spend their time.  That build has every work-group item (ticket t, t below
+ * 65536) of kv_evict_score_select_compact and
+ * kv_evict_score_budget_select_compact record the memory-clock counter at
+ * nine phase boundaries: 0 item taken, 1 pass 1 done, 2 first segment barrier
+ * passed, 3 log-sum-exp merged, 4 pass 2 done, 5 second meeting passed (and
+ * head budgets known), 6 threshold found, 7 output places ranked, 8 rows
+ * gathered; the in-place kernel records phases 0-4.  This call synchronises
+ * the device, copies rows 0 .. max_items-1 (9 values each, 0 where nothing was
+ * recorded since the previous call) into host memory `stamps`, clears them,
+ * and sets *n_rows to the rows copied and *ticks_per_us to the counter's rate.
+ * Errors: EINVAL (a NULL pointer, max_items < 0, or not a KVE_STAMPS build),
+ * EDEVICE (the device could not be read).
+ */
+kve_status kve_debug_stamps(uint64_t* stamps, int64_t max_items, int64_t* n_rows, double* ticks_per_us);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* kve_last_error(void);
 

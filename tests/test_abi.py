@@ -110,3 +110,15 @@ def test_debug_flags_call_outside_a_debug_build():
     f = ctypes.c_uint32(7)
     st, msg = _fail(L.kve_debug_flags, ctypes.byref(f))
     assert st == 1 and "not a KVE_DEBUG build" in msg and f.value == 0
+
+
+def test_stamps_call_outside_a_stamps_build():
+    if os.path.basename(kv.LIB_PATH) == "libkvevict_stamps.so":
+        pytest.skip("run against the phase-stamping library")
+    L = kv.lib()
+    n, tpu = ctypes.c_int64(5), ctypes.c_double(1.0)
+    buf = (ctypes.c_uint64 * 9)()
+    assert _fail(L.kve_debug_stamps, None, 1, ctypes.byref(n), ctypes.byref(tpu))[0] == 1
+    assert _fail(L.kve_debug_stamps, buf, -1, ctypes.byref(n), ctypes.byref(tpu))[0] == 1
+    st, msg = _fail(L.kve_debug_stamps, buf, 1, ctypes.byref(n), ctypes.byref(tpu))
+    assert st == 1 and "not a KVE_STAMPS build" in msg and n.value == 0
