@@ -599,7 +599,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int wtot[4];
-  __shared__ int mine[kMfmaChunk];           // this chunk's kept slots, ascending
+  __shared__ int mine[kMfmaChunk];           // kept slots of the piece being gathered, ascending
   const int64_t oo = a.out_off[s];
   const int P = a.n_prefix, R = a.n_recent;
   const bool out_ok = oo >= 0 && oo + a.out_cap <= a.out_rows;
@@ -607,11 +607,28 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   const int keep_n = K >= n ? n : K;
   if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D))
     return -1;                               // the segment keeps the failure mark stored after the first barrier
-  int base = 0, cnt = 0;                     // output row of this chunk's first kept slot; kept count
+  // The chunk is ranked and gathered in pieces of at most kMfmaChunk slots
+  // (whole segments of up to step_max_seg keys in the entropy-budget kernel),
+  // so a piece's kept slots always fit `mine`.
+  int base = 0;                              // output row of the next kept slot
+  bool first = true;
+  auto gather_piece = [&](int cnt) {         // mine[0, cnt) -> output rows base .. base + cnt - 1
+    __syncthreads();
+    if (first) KVE_STAMP(item, 7);
+    first = false;
+    const int64_t dst0 = oo + base;
+    gather_rows<CPR>([&](int r) { return mine[r]; }, [&](int r) { return dst0 + r; }, cnt, a.k, a.v, a.pos, off,
+                     a.k_out, a.v_out, a.pos_out, a.kept, tid, n, oo, oo + a.out_cap);
+    base += cnt;
+    __syncthreads();                         // the next piece rewrites mine
+  };
   if (K >= n) {
-    for (int j = k0 + tid; j < k1; j += 256) if (KVE_CHECK(j - k0 < kMfmaChunk, 7)) mine[j - k0] = j;
     base = k0;
-    cnt = k1 - k0;
+    for (int p0 = k0; p0 < k1; p0 += kMfmaChunk) {
+      const int p1 = min(k1, p0 + kMfmaChunk);
+      for (int j = p0 + tid; j < p1; j += 256) mine[j - p0] = j;
+      gather_piece(p1 - p0);
+    }
   } else {
     uint32_t T, kk;
     if (loaded) segment_radix(a, n, K - P - R, keys, *loaded, hist, sh, tid, T, kk);
@@ -628,28 +645,27 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     const int prot_b = min(k0, P) + max(0, k0 - (n - R));
     base = prot_b + gt_b + min(eq_b, int(kk));
     int eq_seen = eq_b;
-    for (int j0 = k0; j0 < k1; j0 += 256) {
-      const int j = j0 + tid;
-      const bool in = j < k1;
-      const bool cand = in && j >= P && j < n - R;
-      const uint32_t key = cand ? keys[j] : 0u;
-      const bool eq = cand && key == T;
-      int eq_tot;
-      const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
-      const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
-      int keep_tot;
-      const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
-      if (keep && KVE_CHECK(at < kMfmaChunk, 7)) mine[at] = j;
-      cnt += keep_tot;
-      eq_seen += eq_tot;
+    for (int p0 = k0; p0 < k1; p0 += kMfmaChunk) {
+      const int p1 = min(k1, p0 + kMfmaChunk);
+      int cnt = 0;
+      for (int j0 = p0; j0 < p1; j0 += 256) {
+        const int j = j0 + tid;
+        const bool in = j < p1;
+        const bool cand = in && j >= P && j < n - R;
+        const uint32_t key = cand ? keys[j] : 0u;
+        const bool eq = cand && key == T;
+        int eq_tot;
+        const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
+        const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
+        int keep_tot;
+        const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
+        if (keep && KVE_CHECK(at < kMfmaChunk, 7)) mine[at] = j;
+        cnt += keep_tot;
+        eq_seen += eq_tot;
+      }
+      gather_piece(cnt);
     }
   }
-  __syncthreads();
-  KVE_STAMP(item, 7);
-  // gather this chunk's kept rows to output rows base .. base + cnt - 1
-  const int64_t dst0 = oo + base;
-  gather_rows<CPR>([&](int r) { return mine[r]; }, [&](int r) { return dst0 + r; }, cnt, a.k, a.v, a.pos, off,
-                   a.k_out, a.v_out, a.pos_out, a.kept, tid, n, oo, oo + a.out_cap);
   return keep_n;
 }
 

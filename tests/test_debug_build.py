@@ -16,7 +16,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GPU_FILES = ["tests/test_gpu_parity.py", "tests/test_gpu_inplace.py", "tests/test_gpu_step.py",
-             "tests/test_gpu_budget_step.py", "tests/test_gpu_variants.py", "tests/test_gpu_graph.py"]
+             "tests/test_gpu_budget_step.py", "tests/test_gpu_variants.py", "tests/test_gpu_graph.py",
+             "tests/test_gpu_fullsize.py"]
 
 
 def _debug_lib():
