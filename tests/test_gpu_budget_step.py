@@ -21,6 +21,8 @@ CASES = {
     "llama-ragged": get_workload("r1-llama-8b").scaled(batch=4, len_lo=700, len_hi=3300, n_layers=1),
     # d = 64, fewer heads per request-layer
     "d64": get_workload("tiny-f32").scaled(dtype="bf16", batch=5, len_lo=900, len_hi=2500),
+    # segments of at most 256 keys: one work-group per segment (no first barrier)
+    "short": get_workload("r1-llama-8b").scaled(batch=6, len_lo=100, len_hi=256, n_layers=1),
 }
 FLOOR = 24
 
@@ -148,12 +150,13 @@ def test_entropy_budget_trigger_agrees_with_three_calls(name):
             assert ok, msg
 
 
-def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(kve_overrides):
+@pytest.mark.parametrize("name", ["llama-ragged", "short"])
+def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(name, kve_overrides):
     """A request-layer whose floors exceed its total gets -1 in every head
     (as kv_evict_entropy_budgets); with the meeting poll bound forced to one
     poll from the host, request-layers whose work-groups did not meet report
     -1 and the others are exact; the default bound is whole again."""
-    w, L, D, s_orc = _case("llama-ragged")
+    w, L, D, s_orc = _case(name)
     totals = _totals(w, L, 0.3)
     totals[1] = FLOOR * w.n_kv_heads - 5                      # below the floors
     H = w.n_kv_heads
@@ -181,12 +184,13 @@ def test_entropy_budget_trigger_floors_exceed_total_and_failed_meetings(kve_over
     check(False)
 
 
-def test_entropy_budget_trigger_degenerate_heads():
+@pytest.mark.parametrize("name", ["llama-ragged", "short"])
+def test_entropy_budget_trigger_degenerate_heads(name):
     """A request-layer with an empty head and a head shorter than the
     protected rows: the empty head gets budget 0 and length 0, the short one
     keeps every row, and the other heads share the total as the oracle's
     budgets (computed with the same lengths) say."""
-    w, L, D, s_full = _case("llama-ragged")
+    w, L, D, s_full = _case(name)
     H = w.n_kv_heads
     D2 = dict(D)
     D2["seg_len"] = D["seg_len"].clone()
