@@ -815,6 +815,10 @@ __device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s,
   return kb;
 }
 
+// The work-group item (ticket) of segment s, chunk ch, for the phase stamps
+// (recomputed where it is stamped, so no register holds it in between).
+__device__ __forceinline__ int stamp_item(const ScoreArgs& a, int s, int ch) { return s * a.n_chunks + ch; }
+
 template <int D, int RT, int MODE>
 __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // Padded LDS row (bf16 elements).  A 16-byte fragment read of the MFMA B
@@ -852,7 +856,7 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     if (item < 0) return;
     s = item / a.n_chunks;
     ch = item % a.n_chunks;
-    KVE_STAMP(item, 0);
+    KVE_STAMP(stamp_item(a, s, ch), 0);
   } else {
     xcd_item(a, s, ch);
   }
@@ -1009,10 +1013,10 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // segment barrier: the stores above are acknowledged before the arrival count
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  KVE_STAMP(item, 1);
+  KVE_STAMP(stamp_item(a, s, ch), 1);
   if (tid == 0) sh_item = segment_barrier(ctl + kQueues + s, nch, a.spin_limit) ? 0 : -1;
   __syncthreads();
-  KVE_STAMP(item, 2);
+  KVE_STAMP(stamp_item(a, s, ch), 2);
   // Every work-group of the segment has read the segment's length by now (the
   // output length may be the input length array): the segment counts as failed
   // until its last work-group has moved its rows.  Both this store and the
@@ -1048,14 +1052,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     lse_s[r] = lse;
   }
   __syncthreads();
-  KVE_STAMP(item, 3);
+  KVE_STAMP(stamp_item(a, s, ch), 3);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st0[rt][i] = lse_s[16 * (w * RT + rt) + 4 * quad + i];
   set_shift();
   sweep(std::integral_constant<bool, true>{});
-  KVE_STAMP(item, 4);
+  KVE_STAMP(stamp_item(a, s, ch), 4);
   if (MODE < kModeStep) return;
 
   // Every chunk's scores are stored (acknowledged before the arrival count).
@@ -1095,10 +1099,10 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     } else {
       K = a.budget ? a.budget[s] : a.uniform_budget;
     }
-    KVE_STAMP(item, 5);
-    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid, item);
+    KVE_STAMP(stamp_item(a, s, ch), 5);
+    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid, stamp_item(a, s, ch));
     if (keep_n < 0) return;
-    KVE_STAMP(item, 8);
+    KVE_STAMP(stamp_item(a, s, ch), 8);
     // the last work-group to finish its gather publishes the segment's length
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
