@@ -11,14 +11,10 @@ namespace kve {
 constexpr int kMaxHeads = 64;
 
 __device__ __forceinline__ double wave_min_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmin(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](double x, double y) { return fmin(x, y); });
 }
 __device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](double x, double y) { return fmax(x, y); });
 }
 
 // LDS of one wave's solve.

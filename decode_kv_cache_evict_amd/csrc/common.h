@@ -99,20 +99,101 @@ __device__ __forceinline__ float lanes32_sum(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// dpp<CTRL, ROW_MASK>(v, fill): the value of v in the lane that the DPP
+// (data-parallel primitive) control CTRL names for this lane, read by the
+// VALU with no LDS traffic and no per-lane address register; lanes whose
+// source is outside their row, or whose row ROW_MASK leaves out, get `fill`.
+// The controls used here (rows are 16 lanes):
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]: lane l ^ 1
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]: lane l ^ 2
+constexpr int kDppRor4 = 0x124;      // row_ror:4: lane (l - 4) mod 16 of the row
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane 7 - l inside each group of 8
+constexpr int kDppRor8 = 0x128;      // row_ror:8: lane l ^ 8
+constexpr int kDppShr1 = 0x111;      // row_shr:n (0x110 + n): lane l - n of the row
+constexpr int kDppBcast15 = 0x142;   // row_bcast:15: lane 15 of the previous row
+constexpr int kDppBcast31 = 0x143;   // row_bcast:31: lane 31
+template <int CTRL, int ROW_MASK = 0xF, typename T>
+__device__ __forceinline__ T dpp(T v, T fill = T{}) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             CTRL, ROW_MASK, 0xF, false));
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v), f = __builtin_bit_cast(uint64_t, fill);
+    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(int(uint32_t(f)), int(uint32_t(b)), CTRL, ROW_MASK, 0xF, false));
+    const uint32_t hi =
+        uint32_t(__builtin_amdgcn_update_dpp(int(uint32_t(f >> 32)), int(uint32_t(b >> 32)), CTRL, ROW_MASK, 0xF, false));
+    return __builtin_bit_cast(T, (uint64_t(hi) << 32) | lo);
+  }
+}
+// op(v[l], v[l ^ 16]) (ROW = 16) or op(v[l], v[l ^ 32]) (ROW = 32) with the
+// row-swap instructions; both lanes of a pair combine the same two operands.
+template <int ROW, typename T, typename Op>
+__device__ __forceinline__ T swap_combine(T v, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+  auto swp = [](uint32_t x) {
+    return ROW == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                     : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  };
+  if constexpr (sizeof(T) == 4) {
+    const auto p = swp(__builtin_bit_cast(uint32_t, v));
+    return op(__builtin_bit_cast(T, uint32_t(p[0])), __builtin_bit_cast(T, uint32_t(p[1])));
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const auto lo = swp(uint32_t(b)), hi = swp(uint32_t(b >> 32));
+    return op(__builtin_bit_cast(T, (uint64_t(uint32_t(hi[0])) << 32) | uint32_t(lo[0])),
+              __builtin_bit_cast(T, (uint64_t(uint32_t(hi[1])) << 32) | uint32_t(lo[1])));
+  }
+}
+
+// op over the 64 lanes, the same value in every lane, combined in the order
+// of the xor butterfly: lane l with l ^ 32, then l ^ 16, 8, 4, 2, 1.  After the
+// l ^ 8 step the lanes l and l ^ 8 hold equal values, so row_ror:4 reads the
+// value of lane l ^ 4.  op must be commutative (both lanes of a pair then
+// get the same result).  Every lane of the wave must be active.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = swap_combine<32>(v, op);
+  v = swap_combine<16>(v, op);
+  v = op(v, dpp<kDppRor8>(v));
+  v = op(v, dpp<kDppRor4>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  return op(v, dpp<kDppXor1>(v));
+}
+// op over each row of 16 lanes in the order l ^ 1, 2, 4, 8 (once the l ^ 1
+// and l ^ 2 steps have made every quad uniform, the half-row mirror reads a
+// lane of quad l ^ 4's, with the same value as lane l ^ 4).  op commutative;
+// every lane active.
+template <typename T, typename Op>
+__device__ __forceinline__ T row16_reduce(T v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  return op(v, dpp<kDppRor8>(v));
+}
+// Inclusive prefix sum over the 64 lanes in lane order (integer T): a
+// Hillis-Steele scan inside each row (row_shr 1, 2, 4, 8), then row 0's total
+// into row 1 and row 2's into row 3, then rows 0-1's total into rows 2 and 3.
+// Every lane active.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_sum(T v) {
+  v += dpp<kDppShr1>(v);
+  v += dpp<kDppShr1 + 1>(v);
+  v += dpp<kDppShr1 + 3>(v);
+  v += dpp<kDppShr1 + 7>(v);
+  v += dpp<kDppBcast15, 0xA>(v);
+  v += dpp<kDppBcast31, 0xC>(v);
   return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](double x, double y) { return x + y; });
 }
 
 // Order-preserving map of fp32 values to uint32 (larger float -> larger key;

@@ -320,8 +320,7 @@ struct WaveRows {
         if (rp >= 0) minpos = min(minpos, rp);
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) minpos = min(minpos, __shfl_xor(minpos, o, kWave));
+    minpos = wave_reduce(minpos, [](int x, int y) { return min(x, y); });
   }
 
   // Logits of key tiles q0, q0+1 of one LDS batch (row stride LS): acc[j][rt] holds
@@ -534,11 +533,8 @@ __device__ __forceinline__ SegKeys segment_keys(const ScoreArgs& a, int64_t off,
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-  }
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   if (ENT) {
     S = wave_sum_f64(S);
     Q2 = wave_sum_f64(Q2 * 0.69314718055994530942);   // log2 -> ln
@@ -909,14 +905,19 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
       st1[rt][i] = 0.f;
     }
 
-  // thread's share of a batch: keys key0 + u*KPU (u < CPT), 16-byte chunk `part`
-  const int key0 = tid / CPR, part = tid % CPR;
-  const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
   const int span = k1 - k0;
 
   // One sweep over the chunk: pass 1 updates (st0, st1); pass 2 writes scores.
   auto sweep = [&](auto pass2_tag) {
     constexpr bool P2 = decltype(pass2_tag)::value;
+    // Pass 2 forms its per-thread addresses from an opaque copy of the thread
+    // index: the compiler then computes them after pass 1 instead of keeping
+    // pass 1's copies in registers (spilled) across pass 1's loop.
+    int t = tid;
+    if constexpr (P2) asm volatile("" : "+v"(t));
+    // thread's share of a batch: keys key0 + u*KPU (u < CPT), 16-byte chunk `part`
+    const int key0 = t / CPR, part = t % CPR;
+    const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
     uint4 pre[CPT];
     int prepos = INT_MAX;
     auto load_batch = [&](int kb) {        // kb: batch start relative to k0
@@ -925,19 +926,19 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
         const bool ok = k0 + kb + key0 + u * KPU < k1;
         pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(kb + u * KPU) * D) : make_uint4(0, 0, 0, 0);
       }
-      if (tid < kBK) prepos = (k0 + kb + tid < k1) ? a.pos[off + k0 + kb + tid] : INT_MAX;
+      if (t < kBK) prepos = (k0 + kb + t < k1) ? a.pos[off + k0 + kb + t] : INT_MAX;
     };
     auto store_batch = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) *reinterpret_cast<uint4*>(&kt[buf][(key0 + u * KPU) * LS + part * 8]) = pre[u];
-      if (tid < kBK) kps[buf][tid] = prepos;
+      if (t < kBK) kps[buf][t] = prepos;
     };
     auto finish_keys = [&](int bi, int kb) {  // per-key max (sum) over the 4 waves -> score
-      const int j = k0 + kb + tid;
-      if (tid < kBK && j < k1) {
+      const int j = k0 + kb + t;
+      if (t < kBK && j < k1) {
         const float sc =
-            mean ? (red[bi][0][tid] + red[bi][1][tid] + red[bi][2][tid] + red[bi][3][tid]) * inv_live
-                 : fast_exp2(fmaxf(fmaxf(red[bi][0][tid], red[bi][1][tid]), fmaxf(red[bi][2][tid], red[bi][3][tid])));
+            mean ? (red[bi][0][t] + red[bi][1][t] + red[bi][2][t] + red[bi][3][t]) * inv_live
+                 : fast_exp2(fmaxf(fmaxf(red[bi][0][t], red[bi][1][t]), fmaxf(red[bi][2][t], red[bi][3][t])));
         if (MODE >= kModeStep)   // read back by the segment's other work-groups: coherent store
           __hip_atomic_store(&a.scores[off + j], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -994,14 +995,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float mm = st0[rt][i], ll = st1[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(mm, o, kWave), l2 = __shfl_xor(ll, o, kWave);
-        const float M = fmaxf(mm, m2);
-        ll = ll * fast_exp2(mm - M) + l2 * fast_exp2(m2 - M);
-        mm = M;
-      }
+      // (m, l) pairs merged over the row's 16 lanes; the pair travels as one
+      // 64-bit lane value
+      const float2 ml = row16_reduce(make_float2(st0[rt][i], st1[rt][i]), [](float2 x, float2 y) {
+        const float M = fmaxf(x.x, y.x);
+        return make_float2(M, x.y * fast_exp2(x.x - M) + y.y * fast_exp2(y.x - M));
+      });
+      const float mm = ml.x, ll = ml.y;
       const int r = 16 * (w * RT + rt) + 4 * quad + i;
       if (col == 0 && r < a.rows) {
         if (MODE >= kModeFused) store_stat(&stats_seg[int64_t(ch) * a.rows + r], make_float2(mm, ll));
@@ -1111,34 +1111,38 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   }
 }
 
-// Pass 1 and the single-read kernel carry the row statistics in registers; all
-// three fit 3 waves per SIMD.
+// Pass 1 and the single-read kernel carry the row statistics in registers.
+// Up to 192 observation rows (three 16-row tiles per wave) every form fits
+// 3 waves per SIMD without spilling; four tiles per wave (up to 256 rows) need
+// more registers and run at 2 waves per SIMD.
+template <int RT>
+constexpr int kScoreWaves = RT <= 3 ? 3 : 2;
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_pass1_kernel(ScoreArgs a) {
   score_mfma_body<D, RT, kModePass1>(a, nullptr);
 }
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_pass2_kernel(ScoreArgs a) {
   score_mfma_body<D, RT, kModePass2>(a, nullptr);
 }
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_fused_kernel(ScoreArgs a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_fused_kernel(ScoreArgs a,
                                                                                                     int* ctl) {
   score_mfma_body<D, RT, kModeFused>(a, ctl);
 }
 
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_step_kernel(ScoreArgs a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_step_kernel(ScoreArgs a,
                                                                                                    int* ctl) {
   score_mfma_body<D, RT, kModeStep>(a, ctl);
 }
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_budget_kernel(ScoreArgs a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_budget_kernel(ScoreArgs a,
                                                                                                      int* ctl) {
   score_mfma_body<D, RT, kModeBudget>(a, ctl);
 }
 template <int D, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void score_fill_kernel(ScoreArgs a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kScoreWaves<RT>, 8))) void score_fill_kernel(ScoreArgs a,
                                                                                                    int* ctl) {
   score_mfma_body<D, RT, kModeFill>(a, ctl);
 }

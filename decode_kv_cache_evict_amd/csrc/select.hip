@@ -80,11 +80,8 @@ __global__ __launch_bounds__(kSelBlock) void select_kernel(SelectArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-  }
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   if ((tid & 63) == 0) {
     mm[tid >> 6] = kmin;
     mm[kSelWaves + (tid >> 6)] = kmax;
@@ -214,11 +211,8 @@ __global__ __launch_bounds__(kLongBlock) void select_long_kernel(SelectArgs a) {
     kmin = min(kmin, key);
     kmax = max(kmax, key);
   });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-  }
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   constexpr int NW = kLongBlock / kWave;
   if ((tid & 63) == 0) {
     mm[tid >> 6] = kmin;
@@ -389,11 +383,8 @@ __global__ __launch_bounds__(kLongBlock) void select_split_kernel(SelectArgs a, 
     kmin = min(kmin, key);
     kmax = max(kmax, key);
   });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, kWave)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, kWave)));
-  }
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   constexpr int NW = kLongBlock / kWave;
   if ((tid & 63) == 0) {
     mm[tid >> 6] = kmin;

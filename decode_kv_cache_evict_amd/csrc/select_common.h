@@ -34,12 +34,7 @@ __device__ __forceinline__ int block_flag_scan(bool f, int* wtot, int& total) {
 template <int BLOCK>
 __device__ __forceinline__ int block_scan(int x, int* wtot, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += v;
-  }
+  const int inc = wave_inclusive_sum(x);
   if (lane == 63) wtot[w] = inc;
   __syncthreads();
   int before = 0;
@@ -58,8 +53,7 @@ __device__ __forceinline__ int block_scan(int x, int* wtot, int& total) {
 template <int BLOCK>
 __device__ __forceinline__ int block_sum(int v, int* wtot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = wave_reduce(v, [](int x, int y) { return x + y; });
   if (lane == 0) wtot[w] = v;
   __syncthreads();
   int t = 0;
@@ -189,12 +183,7 @@ __device__ __forceinline__ bool radix_threshold_v(const Visit& visit, int kc, ui
         h[i] = hist[255 - 4 * tid - i];
         loc += h[i];
       }
-      uint32_t incl = loc;                  // inclusive scan over lanes, high digits first
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += v;
-      }
+      const uint32_t incl = wave_inclusive_sum(loc);   // over lanes, high digits first
       const uint32_t excl = incl - loc;
       const uint64_t hit = __ballot(incl >= kk);
       const int first = __ffsll((unsigned long long)hit) - 1;
