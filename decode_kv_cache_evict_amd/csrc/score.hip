@@ -755,16 +755,45 @@ __device__ __forceinline__ int step_select_fill(const ScoreArgs& a, int s, int64
 }
 
 // One-kernel trigger with ReasonAlloc's entropy budgets
-// (kv_evict_score_budget_select_compact): the heads of one request-layer
-// (a.n_kv consecutive segments, consecutive tickets of one queue) publish their
-// score entropies, meet at a per-request-layer arrival counter, and each of
-// their work-groups solves the same head budgets (the budget kernel's wave
-// solver) before selecting with its own head's budget.  With one queue, only
-// the newest request-layer can be waiting for work-groups not yet started, so
-// at most n_kv * chunks - 1 <= 95 work-groups wait (the launch keeps to that, or
-// fits in one round of resident work-groups; a segment takes one or two
-// chunks).
+// (kv_evict_score_budget_select_compact).  Every (segment, chunk) is two
+// tickets of one queue: a scoring ticket (both passes; chunk 0 then publishes
+// the segment's score entropy and counts its head in at the request-layer's
+// arrival counter) and a selection ticket (wait until the request-layer's
+// n_kv heads are in, solve the head budgets with the budget kernel's wave
+// solver, select with the own head's budget, gather the chunk's kept rows).
+// A request-layer's selection tickets come kSelectLag tickets after its
+// scoring tickets (four rounds of resident work-groups), so by the time one
+// is taken its heads have been scored: no work-group sits idle waiting for the
+// slowest head of its request-layer while it holds a slot.  (A lag of one
+// round left selections waiting; the 32-layer, 2560-head launch gains little
+// beyond two.)
+// Progress: a scoring work-group waits only at its segment barrier, for chunks
+// of its own segment (consecutive tickets: only the newest segment can miss
+// one, a segment takes one or two chunks); a selection ticket is only handed
+// out after every scoring ticket of its request-layer, all taken by running
+// work-groups that wait on nothing else.  The waits are bounded all the same.
 constexpr int kNoBudget = INT_MIN;
+constexpr int kSelectLag = 4 * 3 * 256;
+
+// Ticket t of the entropy-budget trigger -> (segment * n_chunks + chunk) and
+// whether it is a selection ticket.  With U = n_kv * n_chunks tickets per
+// request-layer and D request-layers of lag: scoring tickets of request-layers
+// 0..D-1; then pairs (scoring of request-layer D + p, selection of p); then the
+// selection tickets of the last D request-layers.
+__device__ __forceinline__ int budget_ticket(const ScoreArgs& a, int t, bool& select) {
+  const int U = a.n_kv * a.n_chunks, G = a.n_seg / a.n_kv;
+  const int D = min(G, (kSelectLag + U - 1) / U);
+  select = false;
+  if (t < D * U) return t;
+  const int u = t - D * U;
+  if (u < 2 * (G - D) * U) {
+    const int p = u / (2 * U), r = u % (2 * U);
+    select = r >= U;
+    return select ? p * U + (r - U) : (D + p) * U + r;
+  }
+  select = true;
+  return (G - D) * U + (u - 2 * (G - D) * U);
+}
 
 // Thread 0 of chunk 0's work-group: publish the segment's entropy and count
 // the head in.
@@ -774,16 +803,15 @@ __device__ __forceinline__ void group_arrive(const ScoreArgs& a, int* ctl, int s
   atomicAdd(ctl + kQueues + 3 * a.n_seg + s / a.n_kv, 1);
 }
 
-// Every thread of every work-group of segment s: the head's budget, or
-// kNoBudget when the heads did not meet within the poll bound or the floors
-// exceed the request-layer's total (the segment then keeps -1).
-__device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s, int ch, float e, int tid) {
+// Every thread of a selection work-group of segment s: the head's budget, or
+// kNoBudget when the heads did not all arrive within the poll bound or the
+// floors exceed the request-layer's total (the segment then keeps -1).
+__device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s, int ch, int tid) {
   __shared__ HeadBudgetLds L;
   __shared__ int met, kb;                      // two words: kb is written while others may still read met
   const int H = a.n_kv, grp = s / H;
   int* cnt = ctl + kQueues + 3 * a.n_seg + grp;
   if (tid == 0) {
-    if (ch == 0) group_arrive(a, ctl, s, e);
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < H && ++spins < a.spin_limit)
       __builtin_amdgcn_s_sleep(1);
@@ -815,6 +843,34 @@ __device__ __forceinline__ int group_budget(const ScoreArgs& a, int* ctl, int s,
 // (recomputed where it is stamped, so no register holds it in between).
 __device__ __forceinline__ int stamp_item(const ScoreArgs& a, int s, int ch) { return s * a.n_chunks + ch; }
 
+// Selection ticket of the entropy-budget trigger for (segment s, chunk ch):
+// wait for the request-layer's heads, solve the head budgets (chunk 0 writes
+// the head's), then select over the segment's stored scores and gather the
+// chunk's kept rows; the last chunk to finish publishes the length.  A segment
+// with nothing to gather (rejected or empty) only has its budget written; its
+// length was written by its scoring ticket.  keys: step_max_seg(D) words of LDS.
+template <int D>
+__device__ __forceinline__ void budget_select(const ScoreArgs& a, int* ctl, int s, int ch, uint32_t* keys, int tid) {
+  int64_t off;
+  int n;
+  const bool ok = segment_ok(a, s, off, n);
+  const int k0 = ch * a.chunk;
+  const bool gather = ok && k0 < n;
+  if (!gather && ch != 0) return;
+  const int K = group_budget(a, ctl, s, ch, tid);
+  if (!gather || K == kNoBudget) return;
+  KVE_STAMP(stamp_item(a, s, ch), 5);
+  const int k1 = min(n, k0 + a.chunk), nch = (n + a.chunk - 1) / a.chunk;
+  const int keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, nullptr, tid, stamp_item(a, s, ch));
+  if (keep_n < 0) return;
+  KVE_STAMP(stamp_item(a, s, ch), 8);
+  // the last work-group to finish its gather publishes the segment's length
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
+    __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D, int RT, int MODE>
 __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // Padded LDS row (bf16 elements).  A 16-byte fragment read of the MFMA B
@@ -840,9 +896,9 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   int item = -1;                             // the ticket (one-call kernels), for the phase stamps
   if (MODE >= kModeFused) {
     if (tid == 0) {
-      if (MODE == kModeBudget) {               // one queue: a request-layer's heads are consecutive tickets
+      if (MODE == kModeBudget) {               // one queue: scoring and (lagging) selection tickets
         const int t = atomicAdd(&ctl[0], 1);
-        sh_item = t < a.n_seg * a.n_chunks ? t : -1;
+        sh_item = t < 2 * a.n_seg * a.n_chunks ? t : -1;
       } else {
         sh_item = take_ticket(a, ctl);
       }
@@ -850,6 +906,14 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     __syncthreads();
     item = sh_item;
     if (item < 0) return;
+    if (MODE == kModeBudget) {
+      bool select;
+      item = budget_ticket(a, item, select);
+      if (select) {
+        budget_select<D>(a, ctl, item / a.n_chunks, item % a.n_chunks, reinterpret_cast<uint32_t*>(&kt[0][0]), tid);
+        return;
+      }
+    }
     s = item / a.n_chunks;
     ch = item % a.n_chunks;
     KVE_STAMP(stamp_item(a, s, ch), 0);
@@ -862,13 +926,13 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
   // budgets (entropy 0, its cap is its length) and gets its budget written
   if (!segment_ok(a, s, off, n)) {
     if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = -1;
-    if (MODE == kModeBudget && ch == 0) group_budget(a, ctl, s, 0, 0.f, tid);
+    if (MODE == kModeBudget && ch == 0 && tid == 0) group_arrive(a, ctl, s, 0.f);
     return;
   }
   const int k0 = ch * a.chunk;
   if (k0 >= n) {
     if (MODE >= kModeStep && ch == 0 && tid == 0) a.out_len[s] = 0;   // empty segment
-    if (MODE == kModeBudget && ch == 0) group_budget(a, ctl, s, 0, 0.f, tid);
+    if (MODE == kModeBudget && ch == 0 && tid == 0) group_arrive(a, ctl, s, 0.f);
     return;
   }
   const int k1 = min(n, k0 + a.chunk);
@@ -1086,21 +1150,18 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     if (tid == 0) sh_item = segment_barrier(ctl + kQueues + a.n_seg + s, nch, a.spin_limit) ? 0 : -1;
     __syncthreads();
     if (sh_item < 0) return;
-    int K;
-    const SegKeys* loaded = nullptr;
-    SegKeys sk;
     if constexpr (MODE == kModeBudget) {
-      // the segment's scores into LDS and its entropy; the request-layer's
-      // heads meet, then every work-group finds the same head budgets
-      sk = segment_keys<true>(a, off, n, keys, reinterpret_cast<uint32_t*>(&red[0][0][0]), tid);
-      loaded = &sk;
-      K = group_budget(a, ctl, s, ch, sk.entropy, tid);
-      if (K == kNoBudget) return;
-    } else {
-      K = a.budget ? a.budget[s] : a.uniform_budget;
+      // every chunk's scores are stored: chunk 0 publishes the segment's
+      // entropy and counts the head in; the selection has a ticket of its own
+      if (ch == 0) {
+        const SegKeys sk = segment_keys<true>(a, off, n, keys, reinterpret_cast<uint32_t*>(&red[0][0][0]), tid);
+        if (tid == 0) group_arrive(a, ctl, s, sk.entropy);
+      }
+      return;
     }
+    const int K = a.budget ? a.budget[s] : a.uniform_budget;
     KVE_STAMP(stamp_item(a, s, ch), 5);
-    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, loaded, tid, stamp_item(a, s, ch));
+    keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, nullptr, tid, stamp_item(a, s, ch));
     if (keep_n < 0) return;
     KVE_STAMP(stamp_item(a, s, ch), 8);
     // the last work-group to finish its gather publishes the segment's length
@@ -1237,8 +1298,8 @@ hipError_t launch_fused(const ScoreArgs& a, int* ctl, hipStream_t st) {
 template <int D, int RT>
 hipError_t launch_step_t(const ScoreArgs& a, int* ctl, hipStream_t st) {
   const unsigned items = unsigned(int64_t(a.n_seg) * a.n_chunks);
-  if (a.layer_total)
-    hipLaunchKernelGGL((score_budget_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
+  if (a.layer_total)   // a scoring and a selection ticket per item
+    hipLaunchKernelGGL((score_budget_kernel<D, RT>), dim3(2 * items), dim3(256), 0, st, a, ctl);
   else if (a.inplace)
     hipLaunchKernelGGL((score_fill_kernel<D, RT>), dim3(items), dim3(256), 0, st, a, ctl);
   else
