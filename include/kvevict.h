@@ -320,10 +320,11 @@ size_t kv_evict_score_budget_select_compact_workspace(const kve_cache* in, const
  * in->max_seg_len (a head may keep every row).  For bf16 caches whose segments fit
  * the on-chip selection (9216 rows at head_dim 128, 5120 at 64) and whose heads'
  * work-groups fit its dispatch bound (about 96 per request-layer, so at most 10
- * heads of up to 9216 rows) it runs as one kernel: each request-layer's heads score their
- * chunks, publish their entropies, meet, and every work-group solves the same
- * head budgets with the budget kernel's solver before selecting and gathering
- * its own chunk's kept rows; otherwise it makes the three calls.  The entropies
+ * heads of up to 9216 rows) it runs as one kernel: every head's chunks are
+ * scored and its entropy published, and later work-groups of the same launch,
+ * once all of a request-layer's heads are in, solve the same head budgets
+ * with the budget kernel's solver and select and gather each chunk's kept
+ * rows; otherwise it makes the three calls.  The entropies
  * are summed in another order than the stand-alone scoring's (equal to fp32
  * rounding), so budgets can differ from the three-call form's only where
  * largest-remainder fractions tie to that rounding.  A request-layer whose
