@@ -14,6 +14,19 @@ namespace kve {
 
 namespace {
 
+// The lane holding the largest v, the lowest lane among equal values (-0.0
+// equals +0.0), the same in every lane: one 64-bit max reduction over
+// (order key of v, inverted lane index), moved between lanes with DPP and the
+// row swaps.
+__device__ __forceinline__ int wave_argmax_low(float v, int idx) {
+  const uint64_t key = (uint64_t(float_order_key(v)) << 32) | uint64_t(~uint32_t(idx));
+  const uint64_t m = wave_reduce(key, [](uint64_t x, uint64_t y) { return x > y ? x : y; });
+  return __builtin_amdgcn_readfirstlane(int(~uint32_t(m)));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {   // lane: wave-uniform
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fps_kernel(const T* __restrict__ q_in, T* q_out,
                                                    const int32_t* count_in, int32_t* count_out, int n_buf, int cap,
@@ -64,26 +77,16 @@ __global__ __launch_bounds__(256) void fps_kernel(const T* __restrict__ q_in, T*
   };
   const float nrm = sqrtf(dot_with(mine));
   const float inv = 1.f / fmaxf(nrm, 1e-30f);
-  const float inv0 = __shfl(inv, 0, kWave);
+  const float inv0 = lane_value(inv, 0);
   float dist = has_row ? 1.f - dot_with(rows) * inv * inv0 : -__builtin_huge_valf();
   bool taken = lane == 0;
   int my_pick = lane == 0 ? 0 : -1;                // lane i records the i-th pick
   for (int step = 1; step < k_keep; ++step) {
-    float v = (has_row && !taken) ? dist : -__builtin_huge_valf();
-    int idx = lane;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, kWave);
-      const int oi = __shfl_xor(idx, o, kWave);
-      if (ov > v || (ov == v && oi < idx)) {
-        v = ov;
-        idx = oi;
-      }
-    }
+    const int idx = wave_argmax_low((has_row && !taken) ? dist : -__builtin_huge_valf(), lane);
     const int j = idx < cap ? idx : cap - 1;        // uniform across the wave
     if (lane == j) taken = true;
     if (lane == step) my_pick = j;
-    const float invj = __shfl(inv, j, kWave);
+    const float invj = lane_value(inv, j);
     const float dj = 1.f - dot_with(rows + j * VPR) * inv * invj;
     dist = fminf(dist, dj);
   }
@@ -156,26 +159,16 @@ __global__ __launch_bounds__(256) void fps_gram_kernel(const uint16_t* __restric
   const bool has_row = lane < cap;
   const float nrm = has_row ? sqrtf(fmaxf(G[lane * CAP + lane], 0.f)) : 0.f;
   const float inv = 1.f / fmaxf(nrm, 1e-30f);
-  const float inv0 = __shfl(inv, 0, kWave);
+  const float inv0 = lane_value(inv, 0);
   float dist = has_row ? 1.f - G[lane] * inv * inv0 : -__builtin_huge_valf();   // row 0 of G = column 0
   bool taken = lane == 0;
   int my_pick = lane == 0 ? 0 : -1;                 // lane i records the i-th pick
   for (int step = 1; step < k_keep; ++step) {
-    float v = (has_row && !taken) ? dist : -__builtin_huge_valf();
-    int idx = lane;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, kWave);
-      const int oi = __shfl_xor(idx, o, kWave);
-      if (ov > v || (ov == v && oi < idx)) {
-        v = ov;
-        idx = oi;
-      }
-    }
+    const int idx = wave_argmax_low((has_row && !taken) ? dist : -__builtin_huge_valf(), lane);
     const int j = idx < cap ? idx : cap - 1;         // uniform across the wave
     if (lane == j) taken = true;
     if (lane == step) my_pick = j;
-    const float invj = __shfl(inv, j, kWave);
+    const float invj = lane_value(inv, j);
     if (has_row) dist = fminf(dist, 1.f - G[j * CAP + lane] * inv * invj);
   }
   const uint64_t tm = __ballot(taken && has_row);
