@@ -426,7 +426,7 @@ def step_bytes(w, call="fused"):
     # the benchmark definition's accounting of one trigger: K read once for
     # scoring, queries, the scores written and read once, the kept K/V rows
     # and positions read and written once (out of place), the FPS buffers
-    b["survey_step"] = (b["score_k"] + b["score_q"] + b["score_out"] + b["select_scores"] + b["compact_kv"]
+    b["definition_step"] = (b["score_k"] + b["score_q"] + b["score_out"] + b["select_scores"] + b["compact_kv"]
                         + b["compact_pos"] + b["fps"])
     # one-kernel trigger: K, pos and queries read once, kept V rows read, the
     # scores and the output cache (K, V, pos) written
@@ -990,7 +990,7 @@ def main():
     # definition counts them (K read for scoring, the kept K/V rows read and
     # written by the compaction, queries, scores written and read, positions)
     if args.call == "fused":
-        roof_bytes = (nb["survey_step"] - nb["fps"]) * dom_layers / w.n_layers
+        roof_bytes = (nb["definition_step"] - nb["fps"]) * dom_layers / w.n_layers
     else:
         roof_bytes = dom_bytes
     roof = roof_bytes / (sc_ms * 1e-3) / 1e9
@@ -1011,8 +1011,8 @@ def main():
                                f"{w.n_recent_q} recent + {w.n_beacon} beacon queries per q-head, "
                                f"FPS {w.fps_cap}->{w.fps_keep}, {w.triggers} trigger states",
                    "global_batch": w.batch, "seq_len": w.len_hi, "parallelism": "single GPU"},
-        "step_hbm": {"algorithmic_bytes": nb["survey_step"], "gb_per_s": nb["survey_step"] / (ms * 1e-3) / 1e9,
-                     "frac_of_peak": nb["survey_step"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "step_hbm": {"algorithmic_bytes": nb["definition_step"], "gb_per_s": nb["definition_step"] / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": nb["definition_step"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "accounting": "K read for scoring; kept K/V read and written by the compaction; queries, "
                                    "scores written and read, positions, FPS buffers",
                      "one_pass_bytes": nb["total"],

@@ -35,8 +35,8 @@ def test_benchmark_definition_bytes():
     b = bench.step_bytes(w, "fused")
     S, n, keep, row = 36 * 16 * 8, 4096, 3584, 256
     assert b["compact_kv"] == 4 * S * keep * row == 16_911_433_728
-    assert abs(b["survey_step"] - 22.48e9) < 0.01e9
-    assert abs(b["survey_step"] / (0.7 * 8e12) * 1e3 - 4.01) < 0.01
+    assert abs(b["definition_step"] - 22.48e9) < 0.01e9
+    assert abs(b["definition_step"] / (0.7 * 8e12) * 1e3 - 4.01) < 0.01
 
 
 def test_more_than_one_gpu_is_refused():
