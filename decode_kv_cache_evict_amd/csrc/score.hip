@@ -8,6 +8,7 @@
 // The bf16 path contracts on the matrix cores (v_mfma_f32_16x16x32_bf16) with
 // key tiles staged through LDS by coalesced 16-byte loads; a plain VALU path
 // serves fp32 caches.
+#include <algorithm>
 #include <climits>
 #include <cstdlib>
 #include <mutex>
@@ -60,72 +61,82 @@ __device__ __forceinline__ bool segment_ok(const ScoreArgs& a, int s, int64_t& o
 // ------------------------------------------------------------ query rotation
 // Rotate every observation row to its q_pos (double-precision angle and
 // rotation) and round to the storage dtype; rows past n_obs are zeroed.  One
-// thread per (request, observation row, run of V frequencies, group of heads):
-// the angles are shared by all query heads, so their sines and cosines are
-// formed once per group and applied to each of its heads, with 16-byte loads
-// and stores of both halves.  Small batches split the heads over more groups.
-// The same launch clears the n_zero control ints of the scoring kernel that
-// follows (queue tickets and arrival counters): one launch fewer, and no
-// memset node when the call is captured in a graph.
+// work-group per block of R consecutive observation rows of one request (R
+// chosen on the host so a block holds about 256 rotation items): its threads
+// first form the R * D/2 sines and cosines, one each, into LDS (the angles
+// are shared by every query head), then each thread rotates its items, one
+// item being V frequencies of one row of one head (both halves, 16-byte loads
+// and stores), all of its loads issued before the first rotation.  Items run
+// fastest over the frequencies and then the rows, which are contiguous in
+// memory for one head.  Work-groups past the row blocks only clear the
+// n_zero control ints of the scoring kernel that follows (queue tickets and
+// arrival counters): one launch fewer, and no memset node when the call is
+// captured in a graph.
+constexpr int kRotMaxAngles = 512;                // sines and cosines per work-group (LDS)
+constexpr int kRotItems = 4;                      // items per thread in flight
+
 template <typename T>
-__global__ void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
-                                  const int32_t* __restrict__ n_obs, T* __restrict__ qr,
-                                  int64_t n_work, int n_q, int max_obs, int D, InvFreq inv, int hsplit,
-                                  int* __restrict__ zero, int n_zero) {
-  constexpr int V = 16 / int(sizeof(T));          // frequencies per thread
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx < n_zero) zero[idx] = 0;
-  if (idx >= n_work) return;
-  const int half = D / 2;
-  const int runs = half / V;
-  const int hg = int(idx % hsplit);               // this thread's share of the heads
-  const int i0 = int(idx / hsplit % runs) * V;
-  const int64_t bo = idx / hsplit / runs;         // b * max_obs + o
-  const int o = int(bo % max_obs);
-  const int b = int(bo / max_obs);
+__global__ __launch_bounds__(256) void rotate_obs_kernel(const T* __restrict__ q, const int32_t* __restrict__ q_pos,
+                                                         const int32_t* __restrict__ n_obs, T* __restrict__ qr,
+                                                         int n_blocks, int rblk, int n_q, int max_obs, int D,
+                                                         InvFreq inv, int* __restrict__ zero, int n_zero) {
+  constexpr int V = 16 / int(sizeof(T));          // frequencies per item
+  __shared__ double2 cs_s[kRotMaxAngles];         // (cos, sin) of row r, frequency i at r * half + i
+  const int tid = threadIdx.x;
+  for (int64_t z = int64_t(blockIdx.x) * blockDim.x + tid; z < n_zero; z += int64_t(gridDim.x) * blockDim.x)
+    zero[z] = 0;
+  if (int(blockIdx.x) >= n_blocks) return;
+  const int half = D / 2, runs = half / V;
+  const int obl = (max_obs + rblk - 1) / rblk;    // row blocks per request
+  const int b = int(blockIdx.x) / obl, o0 = int(blockIdx.x) % obl * rblk;
+  const int nr = min(rblk, max_obs - o0);
   const int no = n_obs ? n_obs[b] : max_obs;
-  const bool live = o < no;
-  double sn[V], cs[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    sn[v] = 0.0;
-    cs[v] = 1.0;
-    if (live) {
-      const double ang = double(q_pos[bo]) * inv.v[i0 + v];
-      sincos(ang, &sn[v], &cs[v]);
+  for (int e = tid; e < nr * half; e += blockDim.x) {
+    const int r = e / half, i = e % half;
+    double sn = 0.0, cs = 1.0;
+    if (o0 + r < no) {
+      const double ang = double(q_pos[int64_t(b) * max_obs + o0 + r]) * inv.v[i];
+      sincos(ang, &sn, &cs);
     }
+    cs_s[e] = make_double2(cs, sn);
   }
-  const int hpg = (n_q + hsplit - 1) / hsplit;
-  const int h_beg = hg * hpg, h_end = min(n_q, h_beg + hpg);
-  constexpr int HB = 4;                           // heads whose loads are in flight together
-  for (int h0 = h_beg; h0 < h_end; h0 += HB) {
-    uint4 x[HB], y[HB];
+  __syncthreads();
+  const int n_items = nr * n_q * runs;
+  for (int it0 = 0; it0 < n_items; it0 += kRotItems * int(blockDim.x)) {
+    uint4 x[kRotItems], y[kRotItems];
+    int64_t at[kRotItems];
+    bool live[kRotItems];
 #pragma unroll
-    for (int u = 0; u < HB; ++u) {
-      // a head past the group's end repeats its last head (same values, same place)
-      const int64_t row = (int64_t(b) * n_q + min(h0 + u, h_end - 1)) * max_obs + o;
-      x[u] = live ? *reinterpret_cast<const uint4*>(q + row * D + i0) : make_uint4(0, 0, 0, 0);
-      y[u] = live ? *reinterpret_cast<const uint4*>(q + row * D + i0 + half) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < kRotItems; ++u) {
+      if (it0 + u * int(blockDim.x) >= n_items) break;                  // the same for every thread
+      const int it = min(it0 + u * int(blockDim.x) + tid, n_items - 1);   // past the end: repeat the last item
+      const int run = it % runs, r = it / runs % nr, h = it / runs / nr;
+      at[u] = ((int64_t(b) * n_q + h) * max_obs + o0 + r) * D + run * V;
+      live[u] = o0 + r < no;
+      x[u] = live[u] ? *reinterpret_cast<const uint4*>(q + at[u]) : make_uint4(0, 0, 0, 0);
+      y[u] = live[u] ? *reinterpret_cast<const uint4*>(q + at[u] + half) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < HB; ++u) {
-      const int64_t row = (int64_t(b) * n_q + min(h0 + u, h_end - 1)) * max_obs + o;
+    for (int u = 0; u < kRotItems; ++u) {
+      const int it = it0 + u * int(blockDim.x) + tid;
+      if (it >= n_items) break;
+      const int run = it % runs, r = it / runs % nr;
       uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-      if (live) {
+      if (live[u]) {
         const T* xe = reinterpret_cast<const T*>(&x[u]);
         const T* ye = reinterpret_cast<const T*>(&y[u]);
         T* le = reinterpret_cast<T*>(&lo);
         T* he = reinterpret_cast<T*>(&hi);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          const RotPair r =
-              rotate_pair(double(Elem<T>::widen(xe[v])), double(Elem<T>::widen(ye[v])), cs[v], sn[v]);
-          le[v] = Elem<T>::from_f64(r.a);
-          he[v] = Elem<T>::from_f64(r.b);
+          const double2 c = cs_s[r * half + run * V + v];
+          const RotPair p = rotate_pair(double(Elem<T>::widen(xe[v])), double(Elem<T>::widen(ye[v])), c.x, c.y);
+          le[v] = Elem<T>::from_f64(p.a);
+          he[v] = Elem<T>::from_f64(p.b);
         }
       }
-      *reinterpret_cast<uint4*>(qr + row * D + i0) = lo;
-      *reinterpret_cast<uint4*>(qr + row * D + i0 + half) = hi;
+      *reinterpret_cast<uint4*>(qr + at[u]) = lo;
+      *reinterpret_cast<uint4*>(qr + at[u] + half) = hi;
     }
   }
 }
@@ -1408,21 +1419,24 @@ int* prepare(ScoreArgs& a, void* ws, hipStream_t st, hipError_t& e, int n_zero) 
   a.lse = reinterpret_cast<float*>(w);
   w += align_up(size_t(a.n_seg) * a.rows * sizeof(float));
   int* ctl = reinterpret_cast<int*>(w);
-  const int64_t base_work = int64_t(batch) * a.max_obs * (a.head_dim / 2) / (16 / int64_t(elem));
-  int hsplit = 1;                              // head groups of at least 4 heads: about 64K threads in all
-  while (a.n_q >= 8 * hsplit && base_work * hsplit < 65536) hsplit *= 2;
-  const int64_t n_work = base_work * hsplit;
-  const dim3 rg(unsigned((std::max<int64_t>(n_work, n_zero) + 255) / 256));
+  // rows per work-group: about 256 items (V frequencies of one head's row) per block, at most
+  // kRotMaxAngles sines and cosines, at most every row of a request
+  const int items_per_row = a.n_q * (a.head_dim / 2) / (16 / int(elem));
+  int rblk = std::max(1, 256 / std::max(1, items_per_row));
+  rblk = std::min({rblk, kRotMaxAngles / (a.head_dim / 2), std::max(1, a.max_obs)});
+  const int64_t n_blocks = a.max_obs > 0 ? int64_t(batch) * ((a.max_obs + rblk - 1) / rblk) : 0;
+  const int64_t zero_blocks = (int64_t(n_zero) + 255) / 256;
   const InvFreq inv = inv_freq(a.theta, a.head_dim);
-  if (n_work > 0 || n_zero > 0) {
+  if (n_blocks > 0 || n_zero > 0) {
+    const dim3 rg(unsigned(std::max(n_blocks, zero_blocks)));
     if (a.dtype == 0)
       hipLaunchKernelGGL(rotate_obs_kernel<uint16_t>, rg, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
-                         a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim,
-                         inv, hsplit, ctl, n_zero);
+                         a.q_pos, a.n_obs, static_cast<uint16_t*>(a.qr), int(n_blocks), rblk, a.n_q, a.max_obs,
+                         a.head_dim, inv, ctl, n_zero);
     else
       hipLaunchKernelGGL(rotate_obs_kernel<float>, rg, dim3(256), 0, st, static_cast<const float*>(a.q), a.q_pos,
-                         a.n_obs, static_cast<float*>(a.qr), n_work, a.n_q, a.max_obs, a.head_dim, inv, hsplit, ctl,
-                         n_zero);
+                         a.n_obs, static_cast<float*>(a.qr), int(n_blocks), rblk, a.n_q, a.max_obs, a.head_dim, inv,
+                         ctl, n_zero);
   }
   e = hipGetLastError();
   return ctl;
