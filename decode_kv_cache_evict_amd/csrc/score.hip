@@ -614,9 +614,11 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
   const int keep_n = K >= n ? n : K;
   if (!out_ok || !bud_ok || keep_n > a.out_cap || n > step_max_seg(D))
     return -1;                               // the segment keeps the failure mark stored after the first barrier
-  // The chunk is ranked and gathered in pieces of at most kMfmaChunk slots
-  // (whole segments of up to step_max_seg keys in the entropy-budget kernel),
-  // so a piece's kept slots always fit `mine`.
+  // The chunk's kept slots are listed in `mine` (256 slots ranked per round)
+  // and gathered whenever the next round could overflow it, so every gather
+  // but the last moves at least kMfmaChunk - 255 rows however sparse the kept
+  // slots are (whole segments of up to step_max_seg keys with small per-head
+  // budgets in the entropy-budget kernel), which keeps its loads in flight.
   int base = 0;                              // output row of the next kept slot
   bool first = true;
   auto gather_piece = [&](int cnt) {         // mine[0, cnt) -> output rows base .. base + cnt - 1
@@ -652,26 +654,27 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
     const int prot_b = min(k0, P) + max(0, k0 - (n - R));
     base = prot_b + gt_b + min(eq_b, int(kk));
     int eq_seen = eq_b;
-    for (int p0 = k0; p0 < k1; p0 += kMfmaChunk) {
-      const int p1 = min(k1, p0 + kMfmaChunk);
-      int cnt = 0;
-      for (int j0 = p0; j0 < p1; j0 += 256) {
-        const int j = j0 + tid;
-        const bool in = j < p1;
-        const bool cand = in && j >= P && j < n - R;
-        const uint32_t key = cand ? keys[j] : 0u;
-        const bool eq = cand && key == T;
-        int eq_tot;
-        const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
-        const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
-        int keep_tot;
-        const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
-        if (keep && KVE_CHECK(at < kMfmaChunk, 7)) mine[at] = j;
-        cnt += keep_tot;
-        eq_seen += eq_tot;
+    int cnt = 0;                             // kept slots listed in `mine` and not yet gathered
+    for (int j0 = k0; j0 < k1; j0 += 256) {
+      if (cnt > kMfmaChunk - 256) {          // a round lists at most 256 more: gather the list first
+        gather_piece(cnt);
+        cnt = 0;
       }
-      gather_piece(cnt);
+      const int j = j0 + tid;
+      const bool in = j < k1;
+      const bool cand = in && j >= P && j < n - R;
+      const uint32_t key = cand ? keys[j] : 0u;
+      const bool eq = cand && key == T;
+      int eq_tot;
+      const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
+      const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
+      int keep_tot;
+      const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);
+      if (keep && KVE_CHECK(at < kMfmaChunk, 7)) mine[at] = j;
+      cnt += keep_tot;
+      eq_seen += eq_tot;
     }
+    gather_piece(cnt);
   }
   return keep_n;
 }
