@@ -428,7 +428,9 @@ def skipkv_token_scores(pss_max, starts, T):
     scores near 0 and goes first, whole sentences together); tokens after the
     last complete sentence score 1.  READING: the page's combined score (its
     eq. 6, with token importance and a weight lambda) is not printed; this is
-    the sentence term alone, so this score is partly unpinned."""
+    the sentence term alone.  Pinned to this reading (not to the page's
+    unprinted formula) by a hand example through all three steps and by
+    invariants."""
     starts = np.asarray(starts, dtype=np.int64)
     sc = np.ones(int(T))
     for i in range(len(starts) - 1):
