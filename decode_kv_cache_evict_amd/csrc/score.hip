@@ -487,7 +487,11 @@ __device__ __forceinline__ int take_ticket(const ScoreArgs& a, int* ctl) {
   for (int k = 0; k < kQueues; ++k) {
     const int q = int((x + k) & (kQueues - 1));
     const int nq = (q < a.n_seg ? (a.n_seg - q + kQueues - 1) / kQueues : 0) * a.n_chunks;
-    if (nq == 0 || __hip_atomic_load(&ctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nq) continue;
+    if (nq == 0) continue;
+    // the XCD's own queue is taken from at once (one round trip; a count past
+    // nq is harmless); the others are looked at first so that an empty one is
+    // not counted up by every work-group that steals
+    if (k > 0 && __hip_atomic_load(&ctl[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nq) continue;
     const int t = atomicAdd(&ctl[q], 1);
     if (t < nq) return (t / a.n_chunks * kQueues + q) * a.n_chunks + t % a.n_chunks;
   }
@@ -878,9 +882,9 @@ __device__ __forceinline__ void budget_select(const ScoreArgs& a, int* ctl, int 
   const int keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, nullptr, tid, stamp_item(a, s, ch));
   if (keep_n < 0) return;
   KVE_STAMP(stamp_item(a, s, ch), 8);
-  // the last work-group to finish its gather publishes the segment's length
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // the last work-group to count itself out publishes the segment's length
+  // (no wait for the gather's stores: the length is read only after the
+  // kernel, and a work-group that gets here has passed every meeting)
   if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
     __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1178,9 +1182,9 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     keep_n = step_select_compact<D>(a, s, off, n, k0, k1, K, keys, nullptr, tid, stamp_item(a, s, ch));
     if (keep_n < 0) return;
     KVE_STAMP(stamp_item(a, s, ch), 8);
-    // the last work-group to finish its gather publishes the segment's length
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // the last work-group to count itself out publishes the segment's length
+    // (no wait for the gather's stores: the length is read only after the
+    // kernel, and a work-group that gets here has passed both barriers)
     if (tid == 0 && atomicAdd(ctl + kQueues + 2 * a.n_seg + s, 1) == nch - 1)
       __hip_atomic_store(&a.out_len[s], keep_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
