@@ -199,13 +199,19 @@ kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, f
   if (ws_bytes < need || (need > 0 && !ws))
     return fail(KVE_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(KVE_EWORKSPACE, "workspace not 256-byte aligned");
-  const size_t sb = size_t(c->n_rows) * sizeof(float);
-  const size_t qb = size_t(batch) * o->n_q_heads * o->max_obs * c->head_dim * elem_bytes(c->dtype);
-  if (overlap(scores, sb, c->k, rows_bytes(c)) || overlap(scores, sb, o->q, qb) ||
-      overlap(scores, sb, c->pos, size_t(c->n_rows) * 4) || overlap(ws, need, c->k, rows_bytes(c)) ||
-      overlap(ws, need, scores, sb) || overlap(ws, need, o->q, qb) ||
-      overlap(head_entropy, size_t(c->n_seg) * 4, scores, sb))
-    return fail(KVE_EALIAS, "an output of kv_evict_score overlaps an input");
+  const size_t ns = size_t(c->n_seg);
+  const void* ins[] = {c->k, c->pos, c->seg_off, c->seg_len, o->q, o->q_pos, o->n_obs};
+  const size_t insz[] = {rows_bytes(c), size_t(c->n_rows) * 4, ns * 8, ns * 4,
+                         size_t(batch) * o->n_q_heads * o->max_obs * c->head_dim * elem_bytes(c->dtype),
+                         size_t(batch) * o->max_obs * 4, o->n_obs ? size_t(batch) * 4 : 0};
+  const void* outs[] = {scores, head_entropy, ws};
+  const size_t outsz[] = {size_t(c->n_rows) * sizeof(float), head_entropy ? ns * 4 : 0, need};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);
+  }
   if (c->n_seg == 0) return KVE_OK;
   kve::ScoreArgs a = score_args(c, o, rows, scores);
   a.entropy = head_entropy;
@@ -296,13 +302,14 @@ kve_status kv_evict_select_compact(const kve_cache* in, const float* scores, con
   const size_t ipb = size_t(in->n_rows) * 4, opb = size_t(out->n_rows) * 4;
   const size_t kb = size_t(out->n_rows) * 4;
   const size_t sb = size_t(n_scores) * 4;
-  const void* ins[] = {in->k, in->v, in->pos, scores, in->seg_off, in->seg_len, budget, score_off};
+  const void* ins[] = {in->k, in->v, in->pos, scores, in->seg_off, in->seg_len, budget, score_off, out->seg_off};
   const size_t insz[] = {ib, ib, ipb, sb, size_t(in->n_seg) * 8, size_t(in->n_seg) * 4,
-                         budget ? size_t(in->n_seg) * 4 : 0, score_off ? size_t(in->n_seg) * 8 : 0};
+                         budget ? size_t(in->n_seg) * 4 : 0, score_off ? size_t(in->n_seg) * 8 : 0,
+                         size_t(out->n_seg) * 8};
   const void* outs[] = {out->k, out->v, out->pos, out->seg_len, kept, ctl};
   const size_t outsz[] = {ob, ob, opb, size_t(out->n_seg) * 4, kb, ctl ? ctl_b : 0};
   for (int i = 0; i < 6; ++i) {
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 9; ++j)
       if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(KVE_EALIAS, "output %d overlaps input %d", i, j);
     for (int j = i + 1; j < 6; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(KVE_EALIAS, "outputs %d and %d overlap", i, j);

@@ -116,7 +116,8 @@ size_t kv_evict_score_workspace(const kve_cache* c, const kve_obs* o);
  * normalised entropy of each segment's score distribution (ReasonAlloc "Key
  * Concepts": head utility), or NULL.
  * Errors: EINVAL (null pointers), ESHAPE (head_dim, group, rows > 256),
- * EWORKSPACE, EDEVICE.
+ * EWORKSPACE, EALIAS (scores, head_entropy or the workspace overlapping an
+ * input or each other), EDEVICE.
  */
 kve_status kv_evict_score(const kve_cache* c, const kve_obs* o, float* scores, float* head_entropy,
                           void* ws, size_t ws_bytes, void* stream);

@@ -122,3 +122,23 @@ def test_stamps_call_outside_a_stamps_build():
     assert _fail(L.kve_debug_stamps, buf, -1, ctypes.byref(n), ctypes.byref(tpu))[0] == 1
     st, msg = _fail(L.kve_debug_stamps, buf, 1, ctypes.byref(n), ctypes.byref(tpu))
     assert st == 1 and "not a KVE_STAMPS build" in msg and n.value == 0
+
+
+def test_score_outputs_must_not_overlap_inputs_or_each_other():
+    """kv_evict_score rejects, before any launch, scores, head_entropy or a
+    workspace that overlaps an input (keys, positions, segment table, queries,
+    query positions) or another output."""
+    L = kv.lib()
+    c = kv.KveCache(dtype=0, n_seg=8, n_kv_heads=8, head_dim=128, max_seg_len=64, n_rows=512,
+                    k=0x100000, v=0x200000, pos=0x300000, seg_off=0x400000, seg_len=0x500000)
+    o = kv.KveObs(q=0x600000, q_pos=0x700000, n_obs=None, n_q_heads=32, max_obs=48, rope_theta=1e6, causal=1)
+    need = L.kv_evict_score_workspace(ctypes.byref(c), ctypes.byref(o))
+    ws = 0x10000000
+    call = lambda sc, ent, w: L.kv_evict_score(ctypes.byref(c), ctypes.byref(o), sc, ent, w, need, None)  # noqa: E731
+    for sc, ent, w in ((0x500000, None, ws),          # scores over the segment lengths
+                       (0x800000, 0x600100, ws),      # head_entropy inside the queries
+                       (0x800000, None, 0x700000),    # workspace over the query positions
+                       (0x800000, 0x800400, ws),      # head_entropy inside the scores
+                       (0x800000, None, 0x300000)):   # workspace over the key positions
+        st = call(sc, ent, w)
+        assert st == 3, (hex(sc), ent, hex(w), st, L.kve_last_error().decode())
