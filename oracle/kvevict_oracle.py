@@ -98,6 +98,8 @@ def segment_probabilities(k, key_pos, q_rot, q_pos, causal=True):
     a row with no visible key is all 0."""
     k = np.asarray(k, dtype=np.float64)
     q_rot = np.asarray(q_rot, dtype=np.float64)
+    if k.shape[0] == 0:                          # an empty segment: no key to score
+        return np.zeros((q_rot.shape[0], 0))
     d = k.shape[1]
     logits = (q_rot @ k.T) / math.sqrt(d)
     vis = visible_mask(key_pos, q_pos, causal)

@@ -129,3 +129,17 @@ def test_mean_aggregation_hand_example_and_row_sum_invariant():
     # and matches the dense softmax's column means
     brute = _brute(k, kpos, q3, np.array([45, 50, 60, 60, 60]), True).mean(axis=0)
     assert np.allclose(segment_scores(k, kpos, q3, [45, 50, 60, 60, 60], True, "mean"), brute, rtol=1e-12)
+
+
+def test_empty_segment_has_no_scores():
+    """A segment without keys scores nothing, and the layer's other segments
+    score as they would alone: the softmax and the maximum run over no key."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 8))
+    assert segment_scores(np.zeros((0, 8)), np.zeros(0, dtype=np.int64), q, np.full(2, 9)).shape == (0,)
+    k = rng.standard_normal((5, 8))
+    pos = np.arange(5)
+    qo = np.broadcast_to(q, (3, 1, 2, 8)).copy()           # three requests, one head, the same two rows
+    s = layer_scores(np.concatenate([k, k]), np.concatenate([pos, pos]), np.array([0, 5, 5]), np.array([5, 0, 5]),
+                     qo, np.full((3, 2), 9), np.array([2, 2, 2]), 1, 1e4, "f64")
+    assert np.array_equal(s[:5], s[5:]) and np.all(s > 0)

@@ -6,4 +6,5 @@ embedding, no attention, no selection, no sampling): both the CPU oracle and
 the GPU library receive the same tensors from here and do their own work.
 """
 from .specs import Workload, WORKLOADS, get_workload  # noqa: F401
-from .gen import make_layer, make_append, make_traces, request_lengths, initial_recent_obs, make_sentences  # noqa: F401
+from .gen import make_layer, make_append, make_traces, request_lengths, initial_recent_obs, make_sentences, \
+    random_layer  # noqa: F401

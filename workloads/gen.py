@@ -253,3 +253,39 @@ def make_sentences(batch: int, T: int, d_model: int, seed: int = 0, len_lo: int 
         st[b, :len(s)] = torch.tensor(s, dtype=torch.int32)
         st[b, len(s):] = s[-1]
     return torch.stack(hs), st, torch.tensor(n_sent, dtype=torch.int32)
+
+
+def random_layer(seed: int, dtype: str, head_dim: int, n_kv_heads: int, group: int, lengths, max_obs: int, n_obs,
+                 n_recent_q: int, device="cpu"):
+    """Unstructured inputs of one layer for shape sweeps: keys, values and
+    queries standard normal (keys pre-RoPE), request b's keys at positions
+    start_b .. start_b + n_b - 1 (start_b random in [0, 60000)), its first
+    n_recent_q observation rows at the n_recent_q positions before step
+    t_b = start_b + n_b and the rest at t_b; rows at or past n_obs[b] exist in
+    the tensor but are not observation rows.  Same layout as make_layer."""
+    dt = _DT[dtype]
+    g = _g(device, 7_000_003 + seed)
+    B, Hkv, Hq, d = len(lengths), n_kv_heads, n_kv_heads * group, head_dim
+    starts = torch.randint(0, 60000, (B,), generator=g, device=device)
+    k_parts, v_parts, p_parts = [], [], []
+    for b, n in enumerate(lengths):
+        k_parts.append(torch.randn(Hkv * n, d, generator=g, device=device))
+        v_parts.append(torch.randn(Hkv * n, d, generator=g, device=device).to(dt))
+        p_parts.append((int(starts[b]) + torch.arange(n, dtype=torch.int32, device=device)).repeat(Hkv))
+    q_obs = torch.randn(B, Hq, max_obs, d, generator=g, device=device).to(dt)
+    q_pos = torch.empty(B, max_obs, dtype=torch.int32, device=device)
+    for b, n in enumerate(lengths):
+        t = int(starts[b]) + n
+        r = min(n_recent_q, max_obs)
+        q_pos[b, :r] = torch.arange(t - r, t, dtype=torch.int32, device=device)
+        q_pos[b, r:] = t
+    seg_len = torch.tensor([n for n in lengths for _ in range(Hkv)], dtype=torch.int32)
+    seg_off = torch.zeros(B * Hkv, dtype=torch.int64)
+    seg_off[1:] = torch.cumsum(seg_len.to(torch.int64), 0)[:-1]
+    return {
+        "k_pre": torch.cat(k_parts), "v": torch.cat(v_parts), "pos": torch.cat(p_parts),
+        "seg_off": seg_off.to(device), "seg_len": seg_len.to(device),
+        "q_obs": q_obs, "q_pos": q_pos,
+        "n_obs": torch.tensor(list(n_obs), dtype=torch.int32, device=device),
+        "lengths": list(lengths),
+    }
