@@ -18,8 +18,8 @@ import decode_kv_cache_evict_amd as kv
 import oracle
 from tests.gpu_side import device_layer
 from tests.oracle_side import np64
-from tests.parity import assert_scores_close, kept_matches
-from workloads import random_layer
+from tests.parity import assert_scores_close, budgets_match, kept_matches
+from workloads import random_layer, random_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,170 @@ def test_random_shapes_one_call_and_two_calls_match_oracle(seed):
             assert np.array_equal(k_out[oo:oo + m], k_in[o + ks])
             assert np.array_equal(v_out[oo:oo + m], v_in[o + ks])
             assert np.array_equal(p_out[oo:oo + m], pos_in[o + ks])
+
+
+def _inputs(seed):
+    """The random layer of case `seed` on the device, the oracle's scores of it."""
+    c = _config(seed)
+    L = random_layer(seed, c["dtype"], c["d"], c["n_kv"], c["group"], c["lengths"], c["max_obs"], c["n_obs"],
+                     c["n_recent_q"])
+    L["k_pre"] = L["k_pre"] * 2.0
+    D = device_layer(L, _W(c))
+    k_orc = oracle.to_storage(oracle.rope(np64(L["k_pre"]), L["pos"].numpy(), c["theta"]), c["dtype"])
+    s_orc = oracle.layer_scores(k_orc, L["pos"].numpy(), L["seg_off"].numpy(), L["seg_len"].numpy(),
+                                np64(L["q_obs"]), L["q_pos"].numpy(), L["n_obs"].numpy(), c["n_kv"], c["theta"],
+                                c["dtype"], c["causal"], c["aggregate"])
+    cap = max(max(c["lengths"]), 1)
+    obs = kv.make_obs(D["q_obs"], D["q_pos"], D["n_obs"], c["theta"], c["causal"],
+                      kv.KVE_AGG_MEAN if c["aggregate"] == "mean" else kv.KVE_AGG_MAX)
+    return c, L, D, s_orc, cap, obs
+
+
+def _ints(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("seed", range(0, N_CASES, 2))
+def test_random_shapes_inplace_match_oracle(seed):
+    """Hole filling in place, one call and two calls, on the same random shapes:
+    the survivors are the oracle's kept set (tie band), laid out exactly as
+    oracle.hole_fill, moved rows byte-exact, rows past the new length untouched;
+    the new lengths go to a separate array or to the cache's own lengths."""
+    c, L, D, s_orc, cap, obs = _inputs(seed)
+    S = len(L["seg_len"])
+    bud = c["budget"] if isinstance(c["budget"], list) else [c["budget"]] * S
+    budget_t = torch.tensor(bud, dtype=torch.int32, device="cuda") if isinstance(c["budget"], list) else None
+    uniform = 0 if budget_t is not None else c["budget"]
+    k0, v0, p0 = _ints(D["k"]), _ints(D["v"]), D["pos"].cpu().numpy()
+    for one_call in (True, False):
+        alias = bool((seed // 2 + one_call) % 2)
+        C = dict(D, k=D["k"].clone(), v=D["v"].clone(), pos=D["pos"].clone(), seg_len=D["seg_len"].clone())
+        cache = kv.make_cache(C["k"], C["v"], C["pos"], C["seg_off"], C["seg_len"], c["n_kv"], cap)
+        new_len = C["seg_len"] if alias else torch.full_like(C["seg_len"], -9)
+        scores = torch.zeros(max(D["k"].shape[0], 1), dtype=torch.float32, device="cuda")
+        if one_call:
+            kv.kv_evict_score_select_compact_inplace(cache, obs, scores, budget_t, c["P"], c["R"], new_len,
+                                                     uniform_budget=uniform)
+        else:
+            kv.kv_evict_score(cache, obs, scores)
+            kv.kv_evict_select_compact_inplace(cache, scores, budget_t, c["P"], c["R"], new_len,
+                                               uniform_budget=uniform)
+        torch.cuda.synchronize()
+        nl = new_len.cpu().numpy()
+        k1, v1, p1 = _ints(C["k"]), _ints(C["v"]), C["pos"].cpu().numpy()
+        for s in range(S):
+            o, n, K = int(L["seg_off"][s]), int(L["seg_len"][s]), bud[s]
+            if K < n and K < c["P"] + c["R"]:
+                assert nl[s] == -1, (seed, one_call, s, nl[s])
+                continue
+            m = min(K, n)
+            assert nl[s] == m, (seed, one_call, s, nl[s], m, c)
+            if m == 0:
+                continue
+            src = (p1[o:o + m] - p0[o]).astype(np.int64)        # positions rise by one per slot
+            kept = np.sort(src)
+            ok, _, msg = kept_matches(kept, s_orc[o:o + n], n, K, c["P"], c["R"])
+            assert ok, f"case {seed} one_call={one_call} segment {s}: {msg} ({c})"
+            assert np.array_equal(src, oracle.hole_fill(kept, n)), (seed, s, "layout")
+            assert np.array_equal(k1[o:o + m], k0[o + src]) and np.array_equal(v1[o:o + m], v0[o + src])
+            assert np.array_equal(k1[o + m:o + n], k0[o + m:o + n]) and np.array_equal(p1[o + m:o + n], p0[o + m:o + n])
+
+
+@pytest.mark.parametrize("seed", range(1, N_CASES, 2))
+def test_random_shapes_entropy_budgets_match_oracle(seed):
+    """The one-call trigger with entropy-driven head budgets on the random
+    shapes (its three-call fallback where they do not fit one kernel): scores,
+    head entropies, head budgets under the largest-remainder contract, kept
+    sets and gathered rows against the oracle."""
+    c, L, D, s_orc, cap, obs = _inputs(seed)
+    r = np.random.default_rng(5000 + seed)
+    S, H, B = len(L["seg_len"]), c["n_kv"], len(c["lengths"])
+    floor = int(r.choice([0, 16, 64]))
+    inverse = int(r.random() < 0.3)
+    n_all = np.array([int(x) for x in L["seg_len"]], dtype=np.int64)
+    totals = []
+    for b in range(B):
+        n = n_all[b * H:(b + 1) * H]
+        totals.append(max(int(np.minimum(floor, n).sum()), int(r.uniform(0.05, 1.2) * n.sum())))
+    tot = torch.tensor(totals, dtype=torch.int32, device="cuda")
+    scores = torch.zeros(max(D["k"].shape[0], 1), dtype=torch.float32, device="cuda")
+    ent = torch.zeros(S, dtype=torch.float32, device="cuda")
+    bud = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    out = {"k": torch.zeros(S * cap, c["d"], dtype=D["k"].dtype, device="cuda"),
+           "v": torch.zeros(S * cap, c["d"], dtype=D["v"].dtype, device="cuda"),
+           "pos": torch.full((S * cap,), -7, dtype=torch.int32, device="cuda"),
+           "seg_off": torch.arange(S, dtype=torch.int64, device="cuda") * cap,
+           "seg_len": torch.full((S,), -9, dtype=torch.int32, device="cuda"),
+           "kept": torch.full((S * cap,), -5, dtype=torch.int32, device="cuda")}
+    cache = kv.make_cache(D["k"], D["v"], D["pos"], D["seg_off"], D["seg_len"], H, cap)
+    cout = kv.make_cache(out["k"], out["v"], out["pos"], out["seg_off"], out["seg_len"], H, cap)
+    kv.kv_evict_score_budget_select_compact(cache, obs, scores, ent, tot, floor, c["P"], c["R"], cout,
+                                            inverse=inverse, budget_out=bud, kept_idx=out["kept"])
+    torch.cuda.synchronize()
+    assert_scores_close(scores.cpu().numpy()[:D["k"].shape[0]], s_orc, what=f"case {seed} scores {c}")
+    g_ent, g_bud = ent.cpu().numpy(), bud.cpu().numpy()
+    lens, kept = out["seg_len"].cpu().numpy(), out["kept"].cpu().numpy()
+    k_in, v_in, p_in = _ints(D["k"]), _ints(D["v"]), D["pos"].cpu().numpy()
+    k_out, v_out, p_out = _ints(out["k"]), _ints(out["v"]), out["pos"].cpu().numpy()
+    for b in range(B):
+        segs = list(range(b * H, (b + 1) * H))
+        n = n_all[segs]
+        E = np.array([oracle.normalized_entropy(s_orc[int(L["seg_off"][s]):int(L["seg_off"][s]) + n[i]])
+                      for i, s in enumerate(segs)])
+        assert np.all(np.abs(g_ent[segs] - E) <= 2e-3 * np.maximum(np.abs(E), 1e-3)), (seed, g_ent[segs], E)
+        ok, msg = budgets_match(g_bud[segs], g_ent[segs], E, n, totals[b], floor, bool(inverse))
+        assert ok, f"case {seed} request {b}: {msg} ({c}, floor {floor}, total {totals[b]})"
+        for i, s in enumerate(segs):
+            K = int(g_bud[s])
+            o = int(L["seg_off"][s])
+            if K < n[i] and K < c["P"] + c["R"]:
+                assert lens[s] == -1, (seed, s, lens[s], K)
+                continue
+            assert lens[s] == min(K, n[i]), (seed, s, lens[s], K)
+            ks = kept[s * cap:s * cap + lens[s]]
+            ok, _, msg = kept_matches(ks, s_orc[o:o + n[i]], int(n[i]), K, c["P"], c["R"])
+            assert ok, f"case {seed} segment {s}: {msg}"
+            rows = slice(s * cap, s * cap + lens[s])
+            assert np.array_equal(k_out[rows], k_in[o + ks]) and np.array_equal(v_out[rows], v_in[o + ks])
+            assert np.array_equal(p_out[rows], p_in[o + ks])
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_fps_buffers_match_oracle(seed):
+    """Continual FPS on random buffers: bf16 (Gram matrix on the matrix cores)
+    or fp32, head size 64 or 128, capacities 1-64, k_keep 1..cap, full and
+    partly filled buffers, in place or not: every full buffer's picks pass the
+    oracle's farthest-point check and its rows are those picks in ascending
+    order; the others pass through unchanged."""
+    r = np.random.default_rng(7000 + seed)
+    dt = "f32" if r.random() < 0.3 else "bf16"
+    d = int(r.choice([64, 128]))
+    cap_max = 64 if (dt == "bf16" or d == 64) else 32          # fp32: cap * d * 4 bytes per wave in LDS
+    cap = int(r.integers(1, cap_max + 1))
+    keep = int(r.integers(1, cap + 1))
+    n_buf = int(r.integers(1, 50))
+    X = random_rows(seed, (n_buf, cap, d), dt).cuda()
+    cnt = torch.full((n_buf,), cap, dtype=torch.int32)
+    for i in r.choice(n_buf, size=min(n_buf, 3), replace=False):
+        cnt[int(i)] = int(r.integers(0, cap))                    # not full: passes through
+    cnt = cnt.cuda()
+    in_place = bool(r.random() < 0.5)
+    q_in, c_in = X.clone(), cnt.clone()
+    q_out = q_in if in_place else torch.full_like(X, 3)
+    c_out = c_in if in_place else torch.full_like(cnt, -3)
+    picks = torch.full((n_buf, keep), -9, dtype=torch.int32, device="cuda")
+    kv.beacon_fps_update(q_in, q_out, c_in, c_out, keep, picks)
+    torch.cuda.synchronize()
+    Xn, P, Co = np64(X), picks.cpu().numpy(), c_out.cpu().numpy()
+    raw_in = X.view(torch.int16 if dt == "bf16" else torch.int32).cpu().numpy()
+    raw_out = q_out.view(torch.int16 if dt == "bf16" else torch.int32).cpu().numpy()
+    cn = cnt.cpu().numpy()
+    for p in range(n_buf):
+        if cn[p] != cap:
+            assert Co[p] == cn[p] and np.all(P[p] == -1), (seed, p)
+            assert np.array_equal(raw_out[p, :cn[p]], raw_in[p, :cn[p]]), (seed, p)
+            continue
+        assert Co[p] == keep, (seed, p, Co[p])
+        ok, step = oracle.fps_acceptable(Xn[p], P[p], 2e-3)
+        assert ok, f"case {seed} ({dt}, d {d}, cap {cap}, keep {keep}) buffer {p}: step {step}, picks {P[p].tolist()}"
+        assert np.array_equal(raw_out[p, :keep], raw_in[p, np.sort(P[p])]), (seed, p)

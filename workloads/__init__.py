@@ -7,4 +7,4 @@ the GPU library receive the same tensors from here and do their own work.
 """
 from .specs import Workload, WORKLOADS, get_workload  # noqa: F401
 from .gen import make_layer, make_append, make_traces, request_lengths, initial_recent_obs, make_sentences, \
-    random_layer  # noqa: F401
+    random_layer, random_rows  # noqa: F401

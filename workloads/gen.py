@@ -289,3 +289,10 @@ def random_layer(seed: int, dtype: str, head_dim: int, n_kv_heads: int, group: i
         "n_obs": torch.tensor(list(n_obs), dtype=torch.int32, device=device),
         "lengths": list(lengths),
     }
+
+
+def random_rows(seed: int, shape, dtype: str, device="cpu"):
+    """Standard-normal rows of the given shape in the storage dtype (beacon
+    buffers and other unstructured inputs of shape sweeps)."""
+    g = _g(device, 9_000_011 + seed)
+    return torch.randn(*shape, generator=g, device=device).to(_DT[dtype])
