@@ -1,8 +1,8 @@
 """The instrumented builds of the library.  The bounds-checked build
 (libkvevict_debug.so, every source compiled with -DKVE_DEBUG): on the CPU it
 loads and passes the ABI tests; on the GPU the parity suites of the select,
-compact, in-place and one-call trigger kernels run against it in a child
-process, and every test must leave the bounds-check flags at zero
+compact, in-place and one-call trigger kernels, and the random-shape sweeps,
+run against it in a child process, and every test must leave the bounds-check flags at zero
 (tests/conftest.py checks them after each).  The phase-stamping build
 (libkvevict_stamps.so, -DKVE_STAMPS): on the CPU it loads and passes the ABI
 tests; on the GPU the benchmark's --stamps run reports every work-group item
@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GPU_FILES = ["tests/test_gpu_parity.py", "tests/test_gpu_inplace.py", "tests/test_gpu_step.py",
              "tests/test_gpu_budget_step.py", "tests/test_gpu_variants.py", "tests/test_gpu_graph.py",
-             "tests/test_gpu_fullsize.py"]
+             "tests/test_gpu_fullsize.py", "tests/test_gpu_random.py"]
 
 
 def _debug_lib():
