@@ -653,7 +653,7 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
       eq_b += keys[j] == T;
       gt_b += keys[j] > T;
     }
-    eq_b = block_sum<256>(eq_b, wtot);
+    eq_b = kk != 0u ? block_sum<256>(eq_b, wtot) : 0;   // kk == 0: no threshold tie is kept
     gt_b = block_sum<256>(gt_b, wtot);
     const int prot_b = min(k0, P) + max(0, k0 - (n - R));
     base = prot_b + gt_b + min(eq_b, int(kk));
@@ -669,8 +669,8 @@ __device__ __forceinline__ int step_select_compact(const ScoreArgs& a, int s, in
       const bool cand = in && j >= P && j < n - R;
       const uint32_t key = cand ? keys[j] : 0u;
       const bool eq = cand && key == T;
-      int eq_tot;
-      const int eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
+      int eq_tot = 0, eq_rank = 0;
+      if (kk != 0u) eq_rank = eq_seen + block_flag_scan<256>(eq, wtot, eq_tot);
       const bool keep = in && (!cand || key > T || (eq && uint32_t(eq_rank) < kk));
       int keep_tot;
       const int at = cnt + block_flag_scan<256>(keep, wtot, keep_tot);

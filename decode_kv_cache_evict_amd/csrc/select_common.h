@@ -144,7 +144,10 @@ __device__ __forceinline__ void gather_rows(const SrcAt& src_at, const DstAt& ds
 // pass the number of leading bits `known` (0..32) that every candidate shares
 // with `prefix` (e.g. the common prefix of the candidates' minimum and
 // maximum); the digits then start below them.  kc == 0 gives T = 0xFFFFFFFF,
-// kk = 0.  hist: 256 uints of LDS; sh: 2 uints of LDS.  When the candidates
+// kk = 0.  When the digit that holds the kc-th key is kept whole (its count is
+// exactly what is still needed), the passes stop there with T one below the
+// digit's smallest possible key and kk = 0: the same kept set (every key
+// above T), usually one digit pass sooner.  hist: 256 uints of LDS; sh: 2 uints of LDS.  When the candidates
 // are spread over several work-groups, merge(hist) replaces each digit pass's
 // local histogram by the sum over all of them (every work-group then takes the
 // same digits) and returns false if they could not meet, which ends the
@@ -200,8 +203,15 @@ __device__ __forceinline__ bool radix_threshold_v(const Visit& visit, int kc, ui
           }
           cum += h[i];
         }
-        sh[0] = prefix | (uint32_t(digit) << shift);
-        sh[1] = kk - above;
+        const uint32_t pick = prefix | (uint32_t(digit) << shift);
+        if (shift > 0 && pick != 0u && hist[digit] == kk - above) {
+          // every candidate with this digit is kept: T just below them, no ties
+          sh[0] = pick - 1u;
+          sh[1] = 0u;
+        } else {
+          sh[0] = pick;
+          sh[1] = kk - above;
+        }
       }
     }
     __syncthreads();
@@ -210,6 +220,7 @@ __device__ __forceinline__ bool radix_threshold_v(const Visit& visit, int kc, ui
     mask |= wmask << shift;
     hi = shift;
     __syncthreads();
+    if (kk == 0u) break;
   }
   T = prefix;
   kk_out = kk;
