@@ -7,6 +7,8 @@
 // g is a bandwidth-bound stream over the bf16 traces: one wavefront walks a run
 // of consecutive steps of one (layer, request), keeping the previous row in
 // registers so every row is read once.  z works on LDS tiles of g in double.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -63,6 +65,79 @@ __global__ __launch_bounds__(256) void epikv_g_kernel(const uint16_t* __restrict
   }
 }
 
+// g for d_model >= 2048: one work-group per run of `run` steps of one
+// (layer, request).  Thread j holds the 16-byte chunks j + 256 c (c < CPT) of
+// each row.  Rows go in batches of RB = 8 / CPT; the next batch's loads are
+// issued before the current batch's differences, so 32 KB per work-group
+// stay in flight across the reductions and the barrier.  The previous row
+// stays in registers, so every row is read once plus one row per run.  Each
+// row's sum of squared differences is reduced over the lanes, then over the
+// four waves through LDS (two alternating slots: one barrier per batch).
+template <int CPT>
+__global__ __launch_bounds__(256) void epikv_g_rows_kernel(const uint16_t* __restrict__ ha,
+                                                           const uint16_t* __restrict__ hb, int batch, int T, int run,
+                                                           float* __restrict__ g) {
+  constexpr int RB = 8 / CPT;
+  __shared__ float part[2][4][RB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int runs = (T + run - 1) / run;
+  const int lb = int(blockIdx.x) / runs, r = int(blockIdx.x) % runs;   // lb = layer * batch + b
+  const int layer = lb / batch, b = lb % batch;
+  constexpr int64_t row_vec = 256 * CPT;      // uint4 per row
+  const uint4* base = reinterpret_cast<const uint4*>(layer == 0 ? ha : hb) + int64_t(b) * T * row_vec + tid;
+  const int t0 = r * run, t1 = min(T, t0 + run);
+  float* gout = g + int64_t(lb) * T;
+  auto load = [&](int tb, uint4 (&dst)[RB][CPT]) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int t = min(tb + i, t1 - 1);      // past the run's end: the last row again (not written)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) dst[i][c] = base[int64_t(t) * row_vec + c * 256];
+    }
+  };
+  uint4 prev[CPT], cur[RB][CPT], nxt[RB][CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) prev[c] = t0 > 0 ? base[int64_t(t0 - 1) * row_vec + c * 256] : make_uint4(0, 0, 0, 0);
+  load(t0, cur);
+  int slot = 0;
+  for (int tb = t0; tb < t1; tb += RB) {
+    if (tb + RB < t1) load(tb + RB, nxt);
+    float s[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const uint4 pv = i == 0 ? prev[c] : cur[i - 1][c];
+        const uint16_t* x = reinterpret_cast<const uint16_t*>(&cur[i][c]);
+        const uint16_t* y = reinterpret_cast<const uint16_t*>(&pv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = bf16_to_f32(x[e]) - bf16_to_f32(y[e]);
+          acc = fmaf(d, d, acc);
+        }
+      }
+      s[i] = wave_sum(acc);
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < RB; ++i) part[slot][w][i] = s[i];
+    __syncthreads();
+    if (tid < RB && tb + tid < t1) {
+      const int t = tb + tid;
+      const float v = part[slot][0][tid] + part[slot][1][tid] + part[slot][2][tid] + part[slot][3][tid];
+      gout[t] = t > 0 ? sqrtf(v) : 0.f;
+    }
+    slot ^= 1;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) prev[c] = cur[RB - 1][c];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) cur[i][c] = nxt[i][c];
+  }
+}
+
 // z for both layers and their difference over one tile of steps of one request.
 __global__ __launch_bounds__(kZTile) void epikv_z_kernel(const float* __restrict__ g, int batch, int T, int W,
                                                          float eps, int form, float* __restrict__ out) {
@@ -114,18 +189,32 @@ hipError_t launch_epikv(const void* h_a, const void* h_b, int32_t batch, int32_t
                         float eps, int32_t form, float* g_out, float* scores, void* ws, hipStream_t st) {
   if (batch == 0 || T == 0) return hipSuccess;
   float* g = g_out ? g_out : static_cast<float*>(ws);
-  const int runs = (T + kRun - 1) / kRun;
-  const int64_t waves = int64_t(2) * batch * runs;
-  const dim3 grid(unsigned((waves + 3) / 4));
   const uint16_t* a = static_cast<const uint16_t*>(h_a);
   const uint16_t* b = static_cast<const uint16_t*>(h_b);
-  switch (d_model / 512) {
-    case 1: hipLaunchKernelGGL(epikv_g_kernel<1>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
-    case 2: hipLaunchKernelGGL(epikv_g_kernel<2>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
-    case 4: hipLaunchKernelGGL(epikv_g_kernel<4>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
-    case 8: hipLaunchKernelGGL(epikv_g_kernel<8>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
-    case 16: hipLaunchKernelGGL(epikv_g_kernel<16>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
-    default: return hipErrorInvalidValue;
+  if (d_model >= 2048) {
+    // runs sized so that the launch is about one round of resident
+    // work-groups (five per CU at this kernel's register use), in whole batches
+    constexpr int64_t kResident = 5 * 256;
+    const int64_t pairs = int64_t(2) * batch;
+    const int64_t per_pair = std::max<int64_t>(1, kResident / pairs);
+    const int rb = 8 / (d_model / 2048);
+    const int run = int(std::max<int64_t>(rb, (T + per_pair - 1) / per_pair + rb - 1) / rb * rb);
+    const dim3 grid(unsigned(pairs * ((T + run - 1) / run)));
+    switch (d_model / 2048) {
+      case 1: hipLaunchKernelGGL(epikv_g_rows_kernel<1>, grid, dim3(256), 0, st, a, b, batch, T, run, g); break;
+      case 2: hipLaunchKernelGGL(epikv_g_rows_kernel<2>, grid, dim3(256), 0, st, a, b, batch, T, run, g); break;
+      case 4: hipLaunchKernelGGL(epikv_g_rows_kernel<4>, grid, dim3(256), 0, st, a, b, batch, T, run, g); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const int runs = (T + kRun - 1) / kRun;
+    const int64_t waves = int64_t(2) * batch * runs;
+    const dim3 grid(unsigned((waves + 3) / 4));
+    switch (d_model / 512) {
+      case 1: hipLaunchKernelGGL(epikv_g_kernel<1>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
+      case 2: hipLaunchKernelGGL(epikv_g_kernel<2>, grid, dim3(256), 0, st, a, b, batch, T, g); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

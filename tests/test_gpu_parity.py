@@ -371,9 +371,12 @@ def test_fps_capacities_and_head_sizes(cap, k_keep, d):
         assert torch.equal(out[p, :k_keep], buf[p, np.sort(P[p]).tolist()])
 
 
-def test_epikv_matches_oracle():
+@pytest.mark.parametrize("Dm,T", [(512, 1500), (1024, 901), (2048, 777), (4096, 1500), (8192, 333)])
+def test_epikv_matches_oracle(Dm, T):
+    """Per-wave runs below d_model 2048, row-batched work-group runs from 2048
+    on (ragged last batch and run at these T)."""
     w = get_workload("long-65k")
-    B, T, Dm, W = 2, 1500, 512, 256
+    B, W = 2, 256
     h = make_traces(w, T=T, d_model=Dm, batch=B)
     hd = h.cuda()
     scores = torch.zeros(B, T, dtype=torch.float32, device="cuda")
