@@ -138,47 +138,77 @@ __global__ __launch_bounds__(256) void epikv_g_rows_kernel(const uint16_t* __res
   }
 }
 
-// z for both layers and their difference over one tile of steps of one request.
+// z for both layers and their difference over one tile of steps of one
+// request, from prefix sums: each layer's window sums of d and d^2, where d is
+// g less the mean c of the tile's span (which keeps the sums near the size of
+// the window's spread, so that E[d^2] - E[d]^2 loses little to cancellation),
+// are differences of two inclusive prefix sums held in LDS in double.
 __global__ __launch_bounds__(kZTile) void epikv_z_kernel(const float* __restrict__ g, int batch, int T, int W,
                                                          float eps, int form, float* __restrict__ out) {
-  extern __shared__ double zs[];               // [2][kZTile + W - 1]
-  const int b = blockIdx.y;
+  extern __shared__ double zs[];               // [2][kZTile + W - 1]: prefix sums of d and of d^2
+  __shared__ double wtot[2][kZTile / 64];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t0 = blockIdx.x * kZTile;
   const int span = kZTile + W - 1;
-  const int first = t0 - (W - 1);
-  for (int i = threadIdx.x; i < 2 * span; i += kZTile) {
-    const int l = i / span, k = i % span;
-    const int t = first + k;
-    zs[i] = (t >= 1 && t < T) ? double(g[(int64_t(l) * batch + b) * T + t]) : 0.0;
-  }
-  __syncthreads();
-  const int t = t0 + threadIdx.x;
-  if (t >= T) return;
-  if (t == 0) {
-    out[int64_t(b) * T] = 0.f;
-    return;
-  }
-  const int lo = max(1, t - W + 1);
-  const int cnt = t - lo + 1;
-  double z[2];
+  const int first = t0 - (W - 1);              // span entry k is step first + k
+  const int per = (span + kZTile - 1) / kZTile; // consecutive span entries per thread
+  const int j0 = tid * per, j1 = min(span, j0 + per);
+  const int t = t0 + tid;
+  double z[2] = {0.0, 0.0};
   for (int l = 0; l < 2; ++l) {
-    const double* u = zs + l * span + (lo - first);
-    double s = 0.0;
-    for (int k = 0; k < cnt; ++k) s += u[k];
-    const double mu = s / cnt;
-    if (form == 1) {                           // rolling-mean form: g_bar(t)
-      z[l] = mu;
-      continue;
+    const float* gl = g + (int64_t(l) * batch + b) * T;
+    auto val = [&](int k) {                    // steps before 1 or past T enter no window
+      const int tt = first + k;
+      return tt >= 1 && tt < T ? double(gl[tt]) : 0.0;
+    };
+    double loc = 0.0;
+    for (int k = j0; k < j1; ++k) loc += val(k);
+    loc = wave_sum_f64(loc);
+    if (lane == 0) wtot[0][w] = loc;
+    __syncthreads();
+    const int n_valid = max(1, min(first + span, T) - max(first, 1));
+    const double c = (wtot[0][0] + wtot[0][1] + wtot[0][2] + wtot[0][3]) / double(n_valid);
+    __syncthreads();
+    double s1 = 0.0, s2 = 0.0;
+    for (int k = j0; k < j1; ++k) {
+      const double d = val(k) - c;
+      s1 += d;
+      s2 += d * d;
+      zs[k] = s1;
+      zs[span + k] = s2;
     }
-    double v = 0.0;
-    for (int k = 0; k < cnt; ++k) {
-      const double d = u[k] - mu;
-      v += d * d;
+    const double i1 = wave_inclusive_sum(s1), i2 = wave_inclusive_sum(s2);
+    if (lane == 63) {
+      wtot[0][w] = i1;
+      wtot[1][w] = i2;
     }
-    const double sd = sqrt(v / cnt);
-    z[l] = (u[cnt - 1] - mu) / (sd + double(eps));
+    __syncthreads();
+    double o1 = i1 - s1, o2 = i2 - s2;         // the entries before this thread's
+    for (int q = 0; q < w; ++q) {
+      o1 += wtot[0][q];
+      o2 += wtot[1][q];
+    }
+    for (int k = j0; k < j1; ++k) {
+      zs[k] += o1;
+      zs[span + k] += o2;
+    }
+    __syncthreads();
+    if (t >= 1 && t < T) {
+      const int lo = max(1, t - W + 1), cnt = t - lo + 1;
+      const int kh = t - first, kl = lo - first;
+      const double S1 = zs[kh] - (kl > 0 ? zs[kl - 1] : 0.0);
+      const double S2 = zs[span + kh] - (kl > 0 ? zs[span + kl - 1] : 0.0);
+      const double md = S1 / cnt;              // window mean of d
+      if (form == 1) {                         // rolling-mean form: g_bar(t)
+        z[l] = c + md;
+      } else {
+        const double sd = sqrt(fmax(S2 / cnt - md * md, 0.0));
+        z[l] = (double(gl[t]) - c - md) / (sd + double(eps));
+      }
+    }
+    __syncthreads();                           // zs and wtot are rewritten for the other layer
   }
-  out[int64_t(b) * T + t] = float(z[0] - z[1]);
+  if (t < T) out[int64_t(b) * T + t] = t == 0 ? 0.f : float(z[0] - z[1]);
 }
 
 }  // namespace
