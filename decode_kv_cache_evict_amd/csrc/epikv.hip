@@ -4,9 +4,11 @@
 //   z_l(t) = (g_l(t) - mean) / (std + eps) over a causal window,
 //   score(t) = z_a(t) - z_b(t)  (part 3), or, in the rolling-mean form of
 //   part 2 (双带层解剖结构), score(t) = mean_a(t) - mean_b(t) over the same window.
-// g is a bandwidth-bound stream over the bf16 traces: one wavefront walks a run
-// of consecutive steps of one (layer, request), keeping the previous row in
-// registers so every row is read once.  z works on LDS tiles of g in double.
+// g is a bandwidth-bound stream over the bf16 traces: a wavefront (d_model 512
+// or 1024) or a work-group (d_model 2048 and up) walks a run of consecutive
+// steps of one (layer, request), keeping the previous row in registers so
+// every row is read once.  z works on LDS tiles of g in double, from prefix
+// sums.
 #include <algorithm>
 
 #include "common.h"
@@ -16,7 +18,7 @@ namespace kve {
 
 namespace {
 
-constexpr int kRun = 64;          // steps per wavefront in the g pass
+constexpr int kRun = 64;          // steps per wavefront in the per-wave g pass
 constexpr int kZTile = 256;       // steps per work-group in the z pass
 
 // VPL = 16-byte vectors per lane per row (d_model = 512 * VPL).
