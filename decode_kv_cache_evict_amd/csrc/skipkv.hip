@@ -120,7 +120,6 @@ __global__ __launch_bounds__(256) void pss_kernel(SkipArgs a) {
   const int kq = a.d_model / 4;                       // dimensions per wave (a multiple of 16)
   const int kb = w * kq;
   f32x4 c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00;
-#pragma unroll 4
   for (int k = kb; k < kb + kq; k += 16) {
     const int v = (k >> 2) + q;
     const float4 xa0 = pa0[v], xa1 = pa1[v], xb0 = pb0[v], xb1 = pb1[v];
