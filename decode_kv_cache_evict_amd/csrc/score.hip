@@ -1002,13 +1002,18 @@ __device__ __forceinline__ void score_mfma_body(const ScoreArgs& a, int* ctl) {
     const uint16_t* gk = static_cast<const uint16_t*>(a.k) + (off + k0 + key0) * D + part * 8;
     uint4 pre[CPT];
     int prepos = INT_MAX;
+    // the batch's loads go out at the top wave priority, so that a wave
+    // issuing them is not held behind the exp2 and MFMA streams of the other
+    // work-groups on its SIMD (36-layer step about 1.5 % shorter)
     auto load_batch = [&](int kb) {        // kb: batch start relative to k0
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const bool ok = k0 + kb + key0 + u * KPU < k1;
         pre[u] = ok ? *reinterpret_cast<const uint4*>(gk + int64_t(kb + u * KPU) * D) : make_uint4(0, 0, 0, 0);
       }
       if (t < kBK) prepos = (k0 + kb + t < k1) ? a.pos[off + k0 + kb + t] : INT_MAX;
+      __builtin_amdgcn_s_setprio(0);
     };
     auto store_batch = [&](int buf) {
 #pragma unroll
